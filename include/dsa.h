@@ -1,0 +1,220 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DSA stage library, libdsa.so.
+ *
+ * The DSA stage of a hybrid KDA+DSA model, as the pages describe it: a
+ * lightweight indexer scores every causal history position of each query,
+ * weights the per-head scores, keeps the Top-K positions, and a sparse
+ * attention core reads only those positions of the MLA latent KV cache.
+ *
+ * Pages cited (Baidu AI Cloud articles), tagged for brevity:
+ *  [A] "Day0 Inference Adaptation and Performance Optimization for a New
+ *       Architecture Domestic Large Language Model on Ascend"
+ *  [B] "Day0 Inference Optimization for New Architecture LLMs Based on CANN"
+ *  [C] "Optimizing LLM Inference for New Architectures: Day-0 Adaptation,
+ *       Sparse Attention, and Long-Sequence Parallelism"
+ *  [D] "Day0 Inference Adaptation and Performance Optimization for
+ *       New-Architecture LLMs"
+ *  [E] "Inference Optimization for a Novel LLM Architecture: From Operator
+ *       Fusion to Multi-Dimensional Parallelism"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers documented "device" must be HIP device (or managed) memory;
+ *    structs and scalars are read on the host during the call only.
+ *  - Ownership: the caller owns every buffer, workspaces included.  The
+ *    library allocates no memory and keeps no state between calls; calls on
+ *    different streams are independent when each has its own workspace.
+ *  - Asynchrony: all device work is enqueued on `stream` (a hipStream_t, or
+ *    NULL for the null stream); nothing synchronizes the device.
+ *  - Layout: row-major, innermost dimension contiguous.  A query row is a
+ *    query token r = b*n_q + i (sequence b, query i of that sequence).
+ *    Positions are logical per sequence; both paged pools share the one
+ *    block table ([A] §4 "Sparse attention read": the paged layout follows
+ *    the indexer's addressing).  Row r sees the causal history
+ *        L_r = L_b - n_q + i + 1,  L_b = min(seq_lens[b], max_seq_len)
+ *    positions (a query sees itself; queries of one step are causal among
+ *    themselves, as in speculative verification).
+ *  - Errors: every check that needs only host data happens before anything
+ *    is launched and returns a status.  Data that lives on the device is
+ *    handled by rule, never by a fault: a block-table entry outside
+ *    [0, num_blocks) makes that position absent (indexer score -inf,
+ *    skipped by attention); an index outside [0, L_r), such as the -1
+ *    padding, is skipped; a row with nothing to attend outputs zeros and
+ *    lse = -inf.  A failed launch returns DSA_ERR_HIP.  Nothing prints.
+ *  - Supported shapes (anything else returns DSA_ERR_UNSUPPORTED):
+ *      indexer  BF16 or E4M3(+fp32 scale per 128): n_heads 64, head_dim 128
+ *               F32: n_heads <= 16, head_dim <= 128
+ *      attention BF16 q, BF16 or MXFP8 (E4M3 + E8M0 per 32) KV:
+ *               n_heads 128, d_qk 576, d_v 512
+ *               F32 q and KV: n_heads <= 16, d_qk <= 128, d_v <= d_qk
+ *      block_size 64, 1 <= top_k <= 4096, n_q <= 8 unless n_q == L_b
+ *      (prefill: one sequence, one query per position).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_NULL = 1,         /* a required pointer is NULL                        */
+    DSA_ERR_SHAPE = 2,        /* sizes inconsistent or out of range                */
+    DSA_ERR_UNSUPPORTED = 3,  /* valid, but no kernel for this shape/dtype         */
+    DSA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than the size query     */
+    DSA_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed        */
+} dsa_status;
+
+typedef enum {
+    DSA_F32 = 0,
+    DSA_BF16 = 1,
+    DSA_E4M3 = 2              /* OCP FP8 E4M3 ("e4m3fn": bias 7, max 448, no inf)  */
+} dsa_dtype;
+
+typedef enum {
+    DSA_SCALE_NONE = 0,
+    DSA_SCALE_F32 = 1,        /* one fp32 factor per `group` elements              */
+    DSA_SCALE_E8M0 = 2        /* one OCP MX E8M0 byte, 2^(b-127), per `group`      */
+} dsa_scale_kind;
+
+/* A paged cache pool: [num_blocks][block_size][width] elements of `dtype`.
+ * Index-K pool ([B] §2.1: the indexer reads the paged K cache directly) and
+ * MLA latent KV pool ([D] §2.2: KV compressed into a low-rank latent row
+ * per position, shared by all heads).  For quantized pools ([A] §5
+ * "Layered Quantization") `scales` holds [num_blocks][block_size]
+ * [width/group] factors; the element value is value(code) * factor. */
+typedef struct {
+    const void* data;           /* device, see above                               */
+    const void* scales;         /* device, fp32 or E8M0 bytes; NULL when NONE      */
+    dsa_dtype dtype;
+    dsa_scale_kind scale_kind;
+    int32_t group;              /* elements per scale: 128 (F32 kind), 32 (E8M0)   */
+    int32_t width;              /* elements per position: d_I or d_qk              */
+    int64_t num_blocks;         /* blocks in the pool                              */
+} dsa_cache;
+
+/* The batch: sequences, their lengths and the shared block table ([D] §8:
+ * paged KV cache). */
+typedef struct {
+    int32_t batch;              /* sequences                                       */
+    int32_t n_q;                /* query tokens per sequence (rows = batch*n_q)    */
+    const int32_t* seq_lens;    /* device [batch]: L_b, counting this step's n_q   */
+    const int32_t* block_table; /* device [batch][max_blocks]: physical block ids  */
+    int32_t max_blocks;         /* table row length                                */
+    int32_t block_size;         /* tokens per block; must be 64                    */
+    int32_t max_seq_len;        /* host bound >= every L_b; <= max_blocks*64       */
+} dsa_batch;
+
+/* Indexer inputs ([D] §4.1 "Indexer Fusion": q_idx, paged K cache, head
+ * weights; [D] §4.2: the head weights come from the head-weight projection). */
+typedef struct {
+    const void* q;              /* device [rows][n_heads][head_dim] in dtype       */
+    dsa_dtype dtype;            /* F32, BF16 or E4M3; k.dtype must match           */
+    const float* q_scale;       /* device [rows][n_heads*head_dim/128] for E4M3    */
+    int32_t n_heads;            /* H_I                                             */
+    int32_t head_dim;           /* d_I                                             */
+    const float* head_w;        /* device [rows][n_heads] fp32                     */
+    dsa_cache k;                /* index-K pool, width == head_dim                 */
+} dsa_indexer_args;
+
+/* Sparse attention inputs and outputs ([A] §4 "Sparse attention read";
+ * [D] §2.2 "reads only the selected KV entries ... chunked, IO-aware").
+ * K is the whole latent row [latent | rope]; V is its first d_v channels. */
+typedef struct {
+    const void* q;              /* device [rows][n_heads][d_qk] in dtype           */
+    dsa_dtype dtype;            /* F32 or BF16; the output has the same dtype      */
+    int32_t n_heads;            /* H                                               */
+    int32_t d_v;                /* value channels                                  */
+    float sm_scale;             /* logit scale, e.g. 1/sqrt(d_qk)                  */
+    dsa_cache kv;               /* latent pool, width == d_qk                      */
+    void* out;                  /* device [rows][n_heads][d_v] in dtype            */
+    float* lse;                 /* device [rows][n_heads] natural-log LSE, or NULL */
+} dsa_attn_args;
+
+/* Human-readable name of a status code (static storage). */
+const char* dsa_status_string(dsa_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t dsa_version(void);
+
+/*
+ * dsa_indexer_scores -- relevance scoring and head-weighted sum
+ * ([D] §4.1 "Indexer Fusion", steps batched_dot and weighted_sum;
+ *  [A] §2 "Sparse Attention (DSA)": the indexer scores historical positions).
+ *
+ *   scores[r][s] = sum_j head_w[r][j] * max(0, sum_c q[r][j][c] * k[s][c])
+ *
+ * for s < L_r, with k[s] read through the block table and dequantized
+ * (E4M3 code * fp32 scale).  Accumulation is fp32.  Only [0, L_r) of each
+ * row is written.  scores: device fp32 [rows][ld_scores], ld_scores >=
+ * max_seq_len.  Errors: NULL, SHAPE, UNSUPPORTED, HIP.
+ */
+dsa_status dsa_indexer_scores(const dsa_batch* batch, const dsa_indexer_args* idx,
+                              float* scores, int64_t ld_scores, void* stream);
+
+/* Workspace bytes dsa_topk needs for this batch and top_k (may be 0). */
+size_t dsa_topk_workspace_bytes(const dsa_batch* batch, int32_t top_k);
+
+/*
+ * dsa_topk -- Top-K selection per row ([D] §4.1 "topk(scores, top_k)";
+ * [C] §3: the fused indexer outputs only the final Top-K indices).
+ *
+ * For each row, the k_r = min(top_k, L_r) positions of scores[r][0:L_r]
+ * with the largest values.  Ties go to the lowest position; -0.0 equals
+ * +0.0.  indices: device int32 [rows][top_k], positions ascending, the
+ * slots from k_r on set to -1.  Reads only scores[r][0:L_r].  Scores must
+ * not be NaN (the order of NaN is unspecified).  ws may be NULL when the
+ * size query returns 0.  Errors: NULL, SHAPE, WORKSPACE, HIP.
+ */
+dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores,
+                    int32_t top_k, int32_t* indices, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes dsa_sparse_attn needs (split partials across the index list). */
+size_t dsa_sparse_attn_workspace_bytes(const dsa_batch* batch, const dsa_attn_args* attn,
+                                       int32_t top_k);
+
+/*
+ * dsa_sparse_attn -- attention over the selected positions of the latent
+ * cache ([A] §2: SFA reads only those positions; [D] §4.1: gathers the
+ * selected positions from the main KV and runs chunked, parallel sparse
+ * attention; [D] §5.1: the result depends only on the selected set).
+ *
+ * For each row r and head h, over the valid entries s of indices[r][0:top_k]
+ * (0 <= s < L_r; others skipped):
+ *   z_s = sm_scale * q[r][h][:] . kv[s][:],  p = softmax(z),
+ *   out[r][h][:] = sum_s p_s * kv[s][0:d_v],  lse[r][h] = log sum_s exp(z_s).
+ * Accumulation fp32, online softmax over chunks; out is rounded to the q
+ * dtype (nearest-even for BF16).  Duplicate indices count as often as they
+ * appear.  indices: device int32 [rows][top_k].  Errors: NULL, SHAPE,
+ * UNSUPPORTED, WORKSPACE, HIP.
+ */
+dsa_status dsa_sparse_attn(const dsa_batch* batch, const dsa_attn_args* attn,
+                           const int32_t* indices, int32_t top_k,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes dsa_forward needs (scores, indices when not returned, and
+ * the attention partials). */
+size_t dsa_forward_workspace_bytes(const dsa_batch* batch, const dsa_indexer_args* idx,
+                                   const dsa_attn_args* attn, int32_t top_k);
+
+/*
+ * dsa_forward -- the whole stage: scoring -> weighting -> Top-K -> sparse
+ * attention ([A] §4 "Indexer fusion" and its illustrative pipeline
+ * fused_indexer then sfa; [D] §4.1).  The result equals dsa_indexer_scores,
+ * then dsa_topk, then dsa_sparse_attn on the same inputs, bit for bit.
+ * indices_out: device int32 [rows][top_k] receiving the selected positions,
+ * or NULL.  Errors: as the three calls, plus WORKSPACE.
+ */
+dsa_status dsa_forward(const dsa_batch* batch, const dsa_indexer_args* idx,
+                       const dsa_attn_args* attn, int32_t top_k, int32_t* indices_out,
+                       void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

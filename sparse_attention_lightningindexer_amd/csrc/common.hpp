@@ -1,0 +1,100 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of libdsa.
+//
+// Lane layouts of the matrix instructions used here (64-lane wave, l = lane,
+// g = l / 16, j = l % 16), checked on gfx950 hardware:
+//   v_mfma_f32_16x16x32_bf16   A: lane holds A[j][8g + 0..7], B: B[8g + 0..7][j],
+//                              D: lane holds D[4g + 0..3][j]
+//   v_mfma_f32_16x16x32_fp8    same as bf16 with 8 e4m3 bytes per lane (OCP e4m3)
+//   v_mfma_scale_f32_16x16x128_f8f6f4 (fp8 operands, unit scales):
+//                              A: lane holds A[j][32g + 0..31], B: B[32g + 0..31][j]
+//   ds_read_b64_tr_b16         in each 16-lane group, lane j's element e is the
+//                              16-bit word (j % 4) at the address given by lane
+//                              4e + j/4 of that group.
+//   v_permlane16_swap / v_permlane32_swap with both operands x give the pair
+//                              (x[l], x[l ^ 16]) / (x[l], x[l ^ 32]) in some order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+#define DSA_LDS __attribute__((address_space(3)))
+
+constexpr int kWave = 64;
+constexpr int kBlock = 64;  // tokens per cache block
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Sum of x over lanes l, l^16, l^32, l^48 (every lane gets the total).
+__device__ __forceinline__ float sum_over_groups(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Max of x over lanes l, l^16, l^32, l^48.
+__device__ __forceinline__ float max_over_groups(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x128 e4m3 x e4m3 with unit (E8M0 = 127) block scales.
+__device__ __forceinline__ f32x4 mfma_fp8_k128(i32x8 a, i32x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Number of lanes below this one whose bit is set in `mask`.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    uint32_t lo = (uint32_t)mask, hi = (uint32_t)(mask >> 32);
+    return (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) {
+    return __builtin_amdgcn_ballot_w64(p);
+}
+
+// Causal history of row r = b*n_q + i with the clamped sequence length Lb.
+__device__ __forceinline__ int history_len(int Lb, int n_q, int i) {
+    int L = Lb - n_q + i + 1;
+    return L < 0 ? 0 : L;
+}
+
+__device__ __forceinline__ int clamp_len(const int32_t* seq_lens, int b, int max_seq_len) {
+    int L = seq_lens[b];
+    L = L < 0 ? 0 : L;
+    return L > max_seq_len ? max_seq_len : L;
+}
+
+// Physical block of logical block j of sequence b, or -1 when absent.
+__device__ __forceinline__ int64_t phys_block(const int32_t* table, int max_blocks, int b, int j,
+                                              int64_t num_blocks) {
+    if (j < 0 || j >= max_blocks) return -1;
+    int64_t p = table[(int64_t)b * max_blocks + j];
+    return (p < 0 || p >= num_blocks) ? -1 : p;
+}
+
+}  // namespace dsa

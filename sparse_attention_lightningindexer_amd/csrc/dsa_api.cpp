@@ -1,0 +1,241 @@
+// dsa_api.cpp -- the C ABI of libdsa (declared in include/dsa.h).
+//
+// Host-side only: argument validation (every check that needs no device data
+// happens before anything is enqueued), workspace sizing and carving, and
+// dispatch to the gfx950 kernels on the caller's stream.  No allocation, no
+// synchronization, no global state.
+#include <limits.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "dsa.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kMaxTopK = 4096;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+dsa_status check_batch(const dsa_batch* b) {
+    if (b == nullptr) return DSA_ERR_NULL;
+    if (b->batch < 0 || b->n_q < 1 || b->block_size != 64 || b->max_blocks < 1 || b->max_seq_len < 0)
+        return DSA_ERR_SHAPE;
+    if ((int64_t)b->max_seq_len > (int64_t)b->max_blocks * 64) return DSA_ERR_SHAPE;
+    if ((int64_t)b->batch * b->n_q > INT_MAX / 2) return DSA_ERR_SHAPE;
+    if (b->batch > 0 && (b->seq_lens == nullptr || b->block_table == nullptr)) return DSA_ERR_NULL;
+    return DSA_OK;
+}
+
+dsa_status check_pool(const dsa_cache* c, int width) {
+    if (c->data == nullptr) return DSA_ERR_NULL;
+    if (c->num_blocks < 1 || c->width != width) return DSA_ERR_SHAPE;
+    if (c->num_blocks * 64 > (int64_t)INT_MAX) return DSA_ERR_UNSUPPORTED;  // pool rows are int32
+    return DSA_OK;
+}
+
+dsa_status check_indexer(const dsa_batch* b, const dsa_indexer_args* a) {
+    if (a == nullptr) return DSA_ERR_NULL;
+    if (b->batch > 0 && (a->q == nullptr || a->head_w == nullptr)) return DSA_ERR_NULL;
+    dsa_status s = check_pool(&a->k, a->head_dim);
+    if (s != DSA_OK) return s;
+    if (a->k.dtype != a->dtype) return DSA_ERR_UNSUPPORTED;
+    switch (a->dtype) {
+    case DSA_F32:
+        if (a->n_heads < 1 || a->n_heads > 16 || a->head_dim < 1 || a->head_dim > 128) return DSA_ERR_UNSUPPORTED;
+        if (a->k.scale_kind != DSA_SCALE_NONE) return DSA_ERR_UNSUPPORTED;
+        return DSA_OK;
+    case DSA_BF16:
+        if (a->n_heads != 64 || a->head_dim != 128) return DSA_ERR_UNSUPPORTED;
+        if (a->k.scale_kind != DSA_SCALE_NONE) return DSA_ERR_UNSUPPORTED;
+        return DSA_OK;
+    case DSA_E4M3:
+        if (a->n_heads != 64 || a->head_dim != 128) return DSA_ERR_UNSUPPORTED;
+        if (a->k.scale_kind != DSA_SCALE_F32 || a->k.group != 128) return DSA_ERR_UNSUPPORTED;
+        if (a->k.scales == nullptr || (b->batch > 0 && a->q_scale == nullptr)) return DSA_ERR_NULL;
+        return DSA_OK;
+    default:
+        return DSA_ERR_UNSUPPORTED;
+    }
+}
+
+dsa_status check_attn(const dsa_batch* b, const dsa_attn_args* a) {
+    if (a == nullptr) return DSA_ERR_NULL;
+    if (b->batch > 0 && (a->q == nullptr || a->out == nullptr)) return DSA_ERR_NULL;
+    dsa_status s = check_pool(&a->kv, a->kv.width);
+    if (s != DSA_OK) return s;
+    if (a->dtype == DSA_F32) {
+        if (a->n_heads < 1 || a->n_heads > 16 || a->kv.width < 1 || a->kv.width > 128) return DSA_ERR_UNSUPPORTED;
+        if (a->d_v < 1 || a->d_v > a->kv.width) return DSA_ERR_SHAPE;
+        if (a->kv.dtype != DSA_F32 || a->kv.scale_kind != DSA_SCALE_NONE) return DSA_ERR_UNSUPPORTED;
+        return DSA_OK;
+    }
+    if (a->dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
+    if (a->n_heads != 128 || a->kv.width != 576 || a->d_v != 512) return DSA_ERR_UNSUPPORTED;
+    if (a->kv.dtype == DSA_BF16 && a->kv.scale_kind == DSA_SCALE_NONE) return DSA_OK;
+    if (a->kv.dtype == DSA_E4M3 && a->kv.scale_kind == DSA_SCALE_E8M0 && a->kv.group == 32)
+        return a->kv.scales == nullptr ? DSA_ERR_NULL : DSA_OK;
+    return DSA_ERR_UNSUPPORTED;
+}
+
+dsa::IndexerLaunch indexer_launch(const dsa_batch* b, const dsa_indexer_args* a, float* scores, int64_t ld) {
+    dsa::IndexerLaunch L{};
+    L.dtype = a->dtype == DSA_F32 ? 0 : (a->dtype == DSA_BF16 ? 1 : 2);
+    L.q = a->q;
+    L.q_scale = a->q_scale;
+    L.w = a->head_w;
+    L.kpool = a->k.data;
+    L.kscale = (const float*)a->k.scales;
+    L.seq_lens = b->seq_lens;
+    L.table = b->block_table;
+    L.max_blocks = b->max_blocks;
+    L.num_blocks = a->k.num_blocks;
+    L.batch = b->batch;
+    L.n_q = b->n_q;
+    L.max_seq_len = b->max_seq_len;
+    L.H = a->n_heads;
+    L.D = a->head_dim;
+    L.scores = scores;
+    L.ld = ld;
+    return L;
+}
+
+dsa::AttnLaunch attn_launch(const dsa_batch* b, const dsa_attn_args* a, const int32_t* indices, int top_k,
+                            float* ws) {
+    dsa::AttnLaunch L{};
+    L.q_dtype = a->dtype == DSA_F32 ? 0 : 1;
+    L.kv_kind = a->kv.dtype == DSA_F32 ? 0 : (a->kv.dtype == DSA_BF16 ? 1 : 2);
+    L.q = a->q;
+    L.kv = a->kv.data;
+    L.kvscale = (const uint8_t*)a->kv.scales;
+    L.seq_lens = b->seq_lens;
+    L.table = b->block_table;
+    L.max_blocks = b->max_blocks;
+    L.num_blocks = a->kv.num_blocks;
+    L.batch = b->batch;
+    L.n_q = b->n_q;
+    L.max_seq_len = b->max_seq_len;
+    L.H = a->n_heads;
+    L.Dqk = a->kv.width;
+    L.Dv = a->d_v;
+    L.top_k = top_k;
+    L.sm_scale = a->sm_scale;
+    L.indices = indices;
+    L.out = a->out;
+    L.lse = a->lse;
+    L.ws = ws;
+    L.splits = a->dtype == DSA_F32 ? 1 : dsa::attn_splits(b->batch * b->n_q, top_k, a->kv.width);
+    return L;
+}
+
+size_t attn_ws(const dsa_batch* b, const dsa_attn_args* a, int top_k) {
+    if (a->dtype == DSA_F32) return 0;
+    return dsa::attn_ws_bytes(b->batch * b->n_q, top_k, a->kv.width, a->n_heads, a->d_v);
+}
+
+int64_t forward_ld(const dsa_batch* b) { return ((int64_t)b->max_seq_len + 63) / 64 * 64; }
+
+dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status s) {
+    switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: sizes inconsistent or out of range";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: no kernel for this shape or dtype";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: a HIP call or kernel launch failed";
+    default: return "unknown dsa_status";
+    }
+}
+
+int32_t dsa_version(void) { return 100; }
+
+dsa_status dsa_indexer_scores(const dsa_batch* batch, const dsa_indexer_args* idx, float* scores,
+                              int64_t ld_scores, void* stream) {
+    dsa_status s = check_batch(batch);
+    if (s != DSA_OK) return s;
+    if ((s = check_indexer(batch, idx)) != DSA_OK) return s;
+    if (batch->batch > 0 && scores == nullptr) return DSA_ERR_NULL;
+    if (ld_scores < batch->max_seq_len) return DSA_ERR_SHAPE;
+    return hip_status(dsa::launch_indexer(indexer_launch(batch, idx, scores, ld_scores), (hipStream_t)stream));
+}
+
+size_t dsa_topk_workspace_bytes(const dsa_batch* batch, int32_t top_k) {
+    (void)batch;
+    (void)top_k;
+    return 0;
+}
+
+dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores, int32_t top_k,
+                    int32_t* indices, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    dsa_status s = check_batch(batch);
+    if (s != DSA_OK) return s;
+    if (top_k < 1 || top_k > kMaxTopK) return DSA_ERR_SHAPE;
+    if (batch->batch > 0 && (scores == nullptr || indices == nullptr)) return DSA_ERR_NULL;
+    if (ld_scores < batch->max_seq_len) return DSA_ERR_SHAPE;
+    dsa::TopkLaunch L{scores, ld_scores, batch->seq_lens, batch->batch, batch->n_q, batch->max_seq_len, top_k,
+                      indices};
+    return hip_status(dsa::launch_topk(L, (hipStream_t)stream));
+}
+
+size_t dsa_sparse_attn_workspace_bytes(const dsa_batch* batch, const dsa_attn_args* attn, int32_t top_k) {
+    if (check_batch(batch) != DSA_OK || attn == nullptr || top_k < 1 || top_k > kMaxTopK) return 0;
+    return attn_ws(batch, attn, top_k);
+}
+
+dsa_status dsa_sparse_attn(const dsa_batch* batch, const dsa_attn_args* attn, const int32_t* indices,
+                           int32_t top_k, void* ws, size_t ws_bytes, void* stream) {
+    dsa_status s = check_batch(batch);
+    if (s != DSA_OK) return s;
+    if ((s = check_attn(batch, attn)) != DSA_OK) return s;
+    if (top_k < 1 || top_k > kMaxTopK) return DSA_ERR_SHAPE;
+    if (batch->batch > 0 && indices == nullptr) return DSA_ERR_NULL;
+    const size_t need = attn_ws(batch, attn, top_k);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+    return hip_status(
+        dsa::launch_sparse_attn(attn_launch(batch, attn, indices, top_k, (float*)ws), (hipStream_t)stream));
+}
+
+size_t dsa_forward_workspace_bytes(const dsa_batch* batch, const dsa_indexer_args* idx, const dsa_attn_args* attn,
+                                   int32_t top_k) {
+    if (check_batch(batch) != DSA_OK || idx == nullptr || attn == nullptr || top_k < 1 || top_k > kMaxTopK) return 0;
+    const size_t rows = (size_t)batch->batch * batch->n_q;
+    return align_up(sizeof(float) * rows * (size_t)forward_ld(batch)) + align_up(sizeof(int32_t) * rows * top_k) +
+           align_up(attn_ws(batch, attn, top_k));
+}
+
+dsa_status dsa_forward(const dsa_batch* batch, const dsa_indexer_args* idx, const dsa_attn_args* attn,
+                       int32_t top_k, int32_t* indices_out, void* ws, size_t ws_bytes, void* stream) {
+    dsa_status s = check_batch(batch);
+    if (s != DSA_OK) return s;
+    if ((s = check_indexer(batch, idx)) != DSA_OK) return s;
+    if ((s = check_attn(batch, attn)) != DSA_OK) return s;
+    if (top_k < 1 || top_k > kMaxTopK) return DSA_ERR_SHAPE;
+    const size_t need = dsa_forward_workspace_bytes(batch, idx, attn, top_k);
+    if (ws == nullptr || ws_bytes < need) return DSA_ERR_WORKSPACE;
+    const size_t rows = (size_t)batch->batch * batch->n_q;
+    const int64_t ld = forward_ld(batch);
+    char* p = (char*)ws;
+    float* scores = (float*)p;
+    p += align_up(sizeof(float) * rows * (size_t)ld);
+    int32_t* idx_ws = (int32_t*)p;
+    p += align_up(sizeof(int32_t) * rows * top_k);
+    float* attn_ws_p = (float*)p;
+    int32_t* indices = indices_out != nullptr ? indices_out : idx_ws;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = dsa::launch_indexer(indexer_launch(batch, idx, scores, ld), st);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+    dsa::TopkLaunch T{scores, ld, batch->seq_lens, batch->batch, batch->n_q, batch->max_seq_len, top_k, indices};
+    if ((e = dsa::launch_topk(T, st)) != hipSuccess) return DSA_ERR_HIP;
+    return hip_status(dsa::launch_sparse_attn(attn_launch(batch, attn, indices, top_k, attn_ws_p), st));
+}
+
+}  // extern "C"

@@ -1,0 +1,331 @@
+// indexer.hip -- Lightning Indexer scoring for gfx950.
+//
+//   I[r][s] = sum_j w[r][j] * max(0, q[r][j][:] . k[s][:]),  s < L_r
+//
+// Relevance scoring and the per-head weighted aggregation of the indexer
+// ("Day0 Inference Adaptation and Performance Optimization for
+// New-Architecture LLMs", §4.1 Indexer Fusion; the ReLU is the per-head
+// nonlinearity), reading the paged index-K cache directly through the block
+// table ("Day0 Inference Optimization for New Architecture LLMs Based on
+// CANN", §2.1).  The quantized path keeps one fp32 scale per 128 elements of
+// q and k; scales are positive, so they are taken out of the ReLU:
+//   I = s_k[s] * sum_j (w_j * s_q[j]) * max(0, q8_j . k8_s).
+//
+// The contraction q.K^T runs on MFMA with heads as M, positions as N and the
+// index dimension as K; the ReLU-weighted sum over the 64 heads is a
+// register epilogue plus two cross-lane swaps.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dsa {
+
+// --------------------------------------------------------------- fp32 path
+// Small fp32 shapes: one thread per (row, position); q and w of the row in LDS.
+__global__ __launch_bounds__(64) void indexer_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ w, const float* __restrict__ kpool,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
+    int64_t num_blocks, int n_q, int max_seq_len, int H, int D, float* __restrict__ scores,
+    int64_t ld) {
+    extern __shared__ float sh[];  // [H*D] q, then [H] w
+    const int r = blockIdx.y, b = r / n_q, i = r % n_q;
+    const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, i);
+    if ((int)blockIdx.x * 64 >= L) return;  // block-uniform
+    for (int t = threadIdx.x; t < H * D; t += 64) sh[t] = q[(int64_t)r * H * D + t];
+    for (int t = threadIdx.x; t < H; t += 64) sh[H * D + t] = w[(int64_t)r * H + t];
+    __syncthreads();
+    const int s = blockIdx.x * 64 + threadIdx.x;
+    if (s >= L) return;
+    const int64_t p = phys_block(table, max_blocks, b, s / kBlock, num_blocks);
+    if (p < 0) {
+        scores[(int64_t)r * ld + s] = -INFINITY;
+        return;
+    }
+    const float* k = kpool + (p * kBlock + s % kBlock) * D;
+    float acc = 0.f;
+    for (int j = 0; j < H; ++j) {
+        float d = 0.f;
+        for (int c = 0; c < D; ++c) d = fmaf(sh[j * D + c], k[c], d);
+        acc = fmaf(sh[H * D + j], fmaxf(d, 0.f), acc);
+    }
+    scores[(int64_t)r * ld + s] = acc;
+}
+
+// ------------------------------------------------------------- MFMA paths
+// Element traits: per-lane operand fragment of one MFMA and the k-steps that
+// cover the 128-wide index vector.
+struct IdxBf16 {
+    using frag = bf16x8;
+    static constexpr int KSTEPS = 4;      // 4 x K=32
+    static constexpr int FB = 16;         // fragment bytes per lane
+    static constexpr int ROW = 256;       // bytes per 128-wide vector
+    static constexpr bool SCALED = false;
+};
+struct IdxFp8 {
+    using frag = i32x8;
+    static constexpr int KSTEPS = 1;      // 1 x K=128
+    static constexpr int FB = 32;
+    static constexpr int ROW = 128;
+    static constexpr bool SCALED = true;
+};
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) { return mfma_bf16(a, b, c); }
+__device__ __forceinline__ f32x4 mma(i32x8 a, i32x8 b, f32x4 c) { return mfma_fp8_k128(a, b, c); }
+
+constexpr int kIdxHeads = 64;  // 4 M-tiles of 16 heads
+
+// Lane's fragment of vector `vec` (ROW bytes each) for k-step ks: FB bytes at
+// ks*4*FB + g*FB -- i.e. elements [K*ks + (K/4)*g, +K/4) of the vector.
+template <class T>
+__device__ __forceinline__ typename T::frag load_frag(const uint8_t* vec, int ks, int g) {
+    return *reinterpret_cast<const typename T::frag*>(vec + ks * 4 * T::FB + g * T::FB);
+}
+
+template <class T>
+__device__ __forceinline__ void load_row_query(const uint8_t* q, const float* q_scale, const float* w,
+                                               int64_t row, bool valid, int g, int j,
+                                               typename T::frag (&qa)[4][T::KSTEPS], float (&wr)[4][4]) {
+    for (int mt = 0; mt < 4; ++mt) {
+        const uint8_t* v = q + ((row * kIdxHeads) + 16 * mt + j) * (int64_t)T::ROW;
+        for (int ks = 0; ks < T::KSTEPS; ++ks) {
+            if (valid) qa[mt][ks] = load_frag<T>(v, ks, g);
+            else qa[mt][ks] = typename T::frag{};
+        }
+        for (int i = 0; i < 4; ++i) {
+            const int h = 16 * mt + 4 * g + i;
+            float x = valid ? w[row * kIdxHeads + h] : 0.f;
+            if constexpr (T::SCALED) x *= valid ? q_scale[row * kIdxHeads + h] : 0.f;
+            wr[mt][i] = x;
+        }
+    }
+}
+
+// ReLU-weighted sum over the 64 heads of one 16-position N-tile: lane holds
+// D[head 16*mt + 4g + i][pos j]; returns the full sum for position j.
+__device__ __forceinline__ float head_weighted_relu_sum(const f32x4 (&acc)[4], const float (&wr)[4][4]) {
+    float v = 0.f;
+    for (int mt = 0; mt < 4; ++mt)
+        for (int i = 0; i < 4; ++i) v = fmaf(wr[mt][i], fmaxf(acc[mt][i], 0.f), v);
+    return sum_over_groups(v);
+}
+
+// Decode: a sequence's n_q <= NQ rows share every K tile.  Each wave walks
+// `tiles_per_wave` consecutive 64-position tiles of one sequence, loading the
+// K fragments straight from HBM into registers (no reuse across waves).
+// grid (ceil(tiles / (4*tiles_per_wave)), batch), block 256.
+template <class T, int NQ>
+__global__ __launch_bounds__(256) void indexer_decode_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ kpool, const float* __restrict__ kscale,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
+    int64_t num_blocks, int n_q, int max_seq_len, float* __restrict__ scores, int64_t ld,
+    int tiles_per_wave) {
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, j = lane & 15;
+    const int Lb = clamp_len(seq_lens, b, max_seq_len);
+    const int tile0 = (blockIdx.x * 4 + wave) * tiles_per_wave;
+    if (tile0 * kBlock >= Lb) return;  // wave-uniform; no block barrier below
+
+    typename T::frag qa[NQ][4][T::KSTEPS];
+    float wr[NQ][4][4];
+    int Lr[NQ];
+    for (int qi = 0; qi < NQ; ++qi) {
+        const bool valid = qi < n_q;
+        const int64_t row = (int64_t)b * n_q + qi;
+        Lr[qi] = valid ? history_len(Lb, n_q, qi) : 0;
+        load_row_query<T>(q, q_scale, w, row, valid, g, j, qa[qi], wr[qi]);
+    }
+
+    for (int t = tile0; t < tile0 + tiles_per_wave; ++t) {
+        const int s0 = t * kBlock;
+        if (s0 >= Lb) break;
+        const int64_t p = phys_block(table, max_blocks, b, t, num_blocks);
+        if (p < 0) {
+            for (int qi = 0; qi < NQ; ++qi)
+                if (s0 + lane < Lr[qi]) scores[((int64_t)b * n_q + qi) * ld + s0 + lane] = -INFINITY;
+            continue;
+        }
+        typename T::frag kf[4][T::KSTEPS];
+        float ksc[4];
+        for (int nt = 0; nt < 4; ++nt) {
+            const uint8_t* v = kpool + (p * kBlock + 16 * nt + j) * (int64_t)T::ROW;
+            for (int ks = 0; ks < T::KSTEPS; ++ks) kf[nt][ks] = load_frag<T>(v, ks, g);
+            if constexpr (T::SCALED) ksc[nt] = kscale[p * kBlock + 16 * nt + j];
+        }
+        for (int qi = 0; qi < NQ; ++qi) {
+            if (s0 >= Lr[qi]) continue;
+            const int64_t row = (int64_t)b * n_q + qi;
+            for (int nt = 0; nt < 4; ++nt) {
+                f32x4 acc[4];
+                for (int mt = 0; mt < 4; ++mt) {
+                    acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int ks = 0; ks < T::KSTEPS; ++ks) acc[mt] = mma(qa[qi][mt][ks], kf[nt][ks], acc[mt]);
+                }
+                float v = head_weighted_relu_sum(acc, wr[qi]);
+                if constexpr (T::SCALED) v *= ksc[nt];
+                const int s = s0 + 16 * nt + j;
+                if (g == 0 && s < Lr[qi]) scores[row * ld + s] = v;
+            }
+        }
+    }
+}
+
+// Prefill (many query rows per sequence): 8 waves x 2 rows = 16 rows per row
+// block; the block's K tiles are staged in LDS (gathered directly into LDS,
+// double-buffered) and shared by all 16 rows.  Causal load skew is balanced
+// by pairing row block x with row block NB-1-x in one workgroup, the
+// head-tail pairing the pages use across devices ("Day0 Inference Adaptation
+// and Performance Optimization for New-Architecture LLMs", §6.2 Zigzag
+// Layout), applied here across the GPU's compute units.
+// grid (ceil(NB/2), batch), block 512.
+template <class T>
+__global__ __launch_bounds__(512) void indexer_prefill_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ kpool, const float* __restrict__ kscale,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
+    int64_t num_blocks, int n_q, int max_seq_len, float* __restrict__ scores, int64_t ld) {
+    constexpr int UNITS = T::ROW / 16;          // 16-byte units per K row
+    constexpr int TILE_BYTES = kBlock * T::ROW;
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[2][TILE_BYTES];
+    __shared__ int tile_ok[2];
+
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, j = lane & 15;
+    const int Lb = clamp_len(seq_lens, b, max_seq_len);
+    const int NB = (n_q + 15) / 16;
+    const int rbs[2] = {(int)blockIdx.x, NB - 1 - (int)blockIdx.x};
+    const int npass = (rbs[1] > rbs[0]) ? 2 : 1;
+
+    for (int pass = 0; pass < npass; ++pass) {
+        const int rb = rbs[pass];
+        typename T::frag qa[2][4][T::KSTEPS];
+        float wr[2][4][4];
+        int Lr[2];
+        for (int qi = 0; qi < 2; ++qi) {
+            const int i = rb * 16 + wave * 2 + qi;
+            const bool valid = i < n_q;
+            Lr[qi] = valid ? history_len(Lb, n_q, i) : 0;
+            load_row_query<T>(q, q_scale, w, (int64_t)b * n_q + i, valid, g, j, qa[qi], wr[qi]);
+        }
+        const int last = (rb * 16 + 15 < n_q - 1) ? rb * 16 + 15 : n_q - 1;
+        const int Lmax = history_len(Lb, n_q, last);
+        const int ntiles = (Lmax + kBlock - 1) / kBlock;
+
+        // Gather tile t into LDS buffer `buf`: unit U of the tile (row U/UNITS,
+        // column U%UNITS) receives global column (U%UNITS) ^ (row % UNITS), an
+        // XOR swizzle that keeps the column reads below bank-conflict free.
+        auto stage = [&](int t, int buf) {
+            int64_t p = phys_block(table, max_blocks, b, t, num_blocks);
+            if (threadIdx.x == 0) tile_ok[buf] = p >= 0;
+            if (p < 0) p = 0;
+            const uint8_t* base = kpool + p * TILE_BYTES;
+            for (int k = wave; k < TILE_BYTES / (16 * kWave); k += 8) {
+                const int U = k * kWave + lane;
+                const int row = U / UNITS, col = (U % UNITS) ^ (row % UNITS);
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(base + row * T::ROW + col * 16),
+                    (DSA_LDS void*)(&ktile[buf][k * kWave * 16]), 16, 0, 0);
+            }
+        };
+        if (ntiles > 0) stage(0, 0);
+        for (int t = 0; t < ntiles; ++t) {
+            const int buf = t & 1;
+            __builtin_amdgcn_s_waitcnt(0x0f70 & ~0x3f00);  // vmcnt(0)
+            __syncthreads();
+            if (t + 1 < ntiles) stage(t + 1, buf ^ 1);
+            const int s0 = t * kBlock;
+            const bool ok = tile_ok[buf] != 0;
+            float ksc[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (T::SCALED) {
+                if (ok) {
+                    const int64_t p = phys_block(table, max_blocks, b, t, num_blocks);
+                    for (int nt = 0; nt < 4; ++nt) ksc[nt] = kscale[p * kBlock + 16 * nt + j];
+                }
+            }
+            if (s0 < Lr[0] || s0 < Lr[1]) {
+                for (int nt = 0; nt < 4; ++nt) {
+                    typename T::frag kf[T::KSTEPS];
+                    const int prow = 16 * nt + j;
+                    const uint8_t* rowp = &ktile[buf][prow * T::ROW];
+                    for (int ks = 0; ks < T::KSTEPS; ++ks) {
+                        if constexpr (T::FB == 16) {
+                            const int u = (4 * ks + g) ^ (prow % UNITS);
+                            kf[ks] = *reinterpret_cast<const bf16x8*>(rowp + u * 16);
+                        } else {
+                            const int u0 = (2 * g) ^ (prow % UNITS), u1 = (2 * g + 1) ^ (prow % UNITS);
+                            const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + u0 * 16);
+                            const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + u1 * 16);
+                            kf[ks] = typename T::frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        }
+                    }
+                    for (int qi = 0; qi < 2; ++qi) {
+                        if (s0 >= Lr[qi]) continue;
+                        f32x4 acc[4];
+                        for (int mt = 0; mt < 4; ++mt) {
+                            acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                            for (int ks = 0; ks < T::KSTEPS; ++ks) acc[mt] = mma(qa[qi][mt][ks], kf[ks], acc[mt]);
+                        }
+                        float v = head_weighted_relu_sum(acc, wr[qi]);
+                        if constexpr (T::SCALED) v *= ksc[nt];
+                        if (!ok) v = -INFINITY;
+                        const int s = s0 + prow;
+                        const int64_t row = (int64_t)b * n_q + rb * 16 + wave * 2 + qi;
+                        if (g == 0 && s < Lr[qi]) scores[row * ld + s] = v;
+                    }
+                }
+            }
+        }
+        __syncthreads();  // LDS buffers are reused by the next pass
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
+    const int rows = a.batch * a.n_q;
+    if (rows == 0 || a.max_seq_len == 0) return hipSuccess;
+    if (a.dtype == 0) {  // f32
+        dim3 grid((a.max_seq_len + 63) / 64, rows);
+        size_t sh = sizeof(float) * (size_t)(a.H * a.D + a.H);
+        hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(64), sh, st, (const float*)a.q, a.w,
+                           (const float*)a.kpool, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
+                           a.n_q, a.max_seq_len, a.H, a.D, a.scores, a.ld);
+        return hipGetLastError();
+    }
+    const bool fp8 = a.dtype == 2;
+    if (a.n_q <= 8) {
+        const int tiles = (a.max_seq_len + kBlock - 1) / kBlock;
+        const int tpw = tiles >= 4096 ? 4 : 2;   // tiles per wave
+        dim3 grid((tiles + 4 * tpw - 1) / (4 * tpw), a.batch);
+#define DSA_DEC(T, NQ)                                                                          \
+    hipLaunchKernelGGL((indexer_decode_kernel<T, NQ>), grid, dim3(256), 0, st,                  \
+                       (const uint8_t*)a.q, a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale,  \
+                       a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len,  \
+                       a.scores, a.ld, tpw)
+        if (fp8) {
+            if (a.n_q == 1) DSA_DEC(IdxFp8, 1); else if (a.n_q == 2) DSA_DEC(IdxFp8, 2);
+            else if (a.n_q <= 4) DSA_DEC(IdxFp8, 4); else DSA_DEC(IdxFp8, 8);
+        } else {
+            if (a.n_q == 1) DSA_DEC(IdxBf16, 1); else if (a.n_q == 2) DSA_DEC(IdxBf16, 2);
+            else if (a.n_q <= 4) DSA_DEC(IdxBf16, 4); else DSA_DEC(IdxBf16, 8);
+        }
+#undef DSA_DEC
+        return hipGetLastError();
+    }
+    const int NB = (a.n_q + 15) / 16;
+    dim3 grid((NB + 1) / 2, a.batch);
+    if (fp8)
+        hipLaunchKernelGGL((indexer_prefill_kernel<IdxFp8>), grid, dim3(512), 0, st,
+                           (const uint8_t*)a.q, a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale,
+                           a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len,
+                           a.scores, a.ld);
+    else
+        hipLaunchKernelGGL((indexer_prefill_kernel<IdxBf16>), grid, dim3(512), 0, st,
+                           (const uint8_t*)a.q, a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale,
+                           a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len,
+                           a.scores, a.ld);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

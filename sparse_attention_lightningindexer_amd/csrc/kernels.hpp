@@ -1,0 +1,64 @@
+// kernels.hpp -- host-side launch descriptors of the gfx950 kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kTopkCacheMax = 16384;      // rows up to this length keep their keys in LDS
+constexpr int kAttnMaxSplits = 32;        // split partials merged per row
+constexpr int kAttnMaxSplitSlots = 4096;  // index slots one attention workgroup compacts
+
+struct IndexerLaunch {
+    int dtype;                 // 0 f32, 1 bf16, 2 e4m3
+    const void* q;
+    const float* q_scale;
+    const float* w;
+    const void* kpool;
+    const float* kscale;
+    const int32_t* seq_lens;
+    const int32_t* table;
+    int max_blocks;
+    int64_t num_blocks;
+    int batch, n_q, max_seq_len, H, D;
+    float* scores;
+    int64_t ld;
+};
+
+struct TopkLaunch {
+    const float* scores;
+    int64_t ld;
+    const int32_t* seq_lens;
+    int batch, n_q, max_seq_len, top_k;
+    int32_t* indices;
+};
+
+struct AttnLaunch {
+    int q_dtype;               // 0 f32, 1 bf16
+    int kv_kind;               // 0 f32, 1 bf16, 2 MXFP8 (e4m3 + e8m0 per 32)
+    const void* q;
+    const void* kv;
+    const uint8_t* kvscale;
+    const int32_t* seq_lens;
+    const int32_t* table;
+    int max_blocks;
+    int64_t num_blocks;
+    int batch, n_q, max_seq_len, H, Dqk, Dv, top_k;
+    float sm_scale;
+    const int32_t* indices;
+    void* out;
+    float* lse;
+    float* ws;                 // split partials, attn_ws_bytes
+    int splits;
+};
+
+hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st);
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t st);
+hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st);
+
+int attn_splits(int rows, int top_k, int Dqk);
+size_t attn_ws_bytes(int rows, int top_k, int Dqk, int H, int Dv);
+
+}  // namespace dsa

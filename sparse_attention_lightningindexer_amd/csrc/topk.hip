@@ -1,0 +1,141 @@
+// topk.hip -- exact per-row Top-K selection for gfx950.
+//
+// Keeps the k_r = min(top_k, L_r) highest-scoring history positions of each
+// row ("Day0 Inference Adaptation and Performance Optimization for
+// New-Architecture LLMs", §4.1, the topk(scores, top_k) step; only the set
+// matters downstream, §5.1).  Ties go to the lowest position and the output
+// is ascending, padded with -1.
+//
+// Method: scores map to order-preserving 32-bit keys (-0.0 folded into
+// +0.0); an MSB-first radix select with 8-bit digits and LDS histograms
+// finds the k-th largest key T and how many keys equal to T are needed;
+// one ordered pass then keeps every key > T and the first needed keys == T,
+// using wave ballots for the in-order ranks.  One workgroup per row; rows are
+// visited longest-first when the grid is larger than the GPU.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dsa {
+
+__device__ __forceinline__ uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0u) u = 0u;  // -0.0 == +0.0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int NT, bool CACHE>
+__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores, int64_t ld,
+                                                  const int32_t* __restrict__ seq_lens, int n_q,
+                                                  int max_seq_len, int rows, int top_k,
+                                                  int32_t* __restrict__ indices) {
+    constexpr int NW = NT / kWave;
+    extern __shared__ uint32_t keys[];  // [max_seq_len] when CACHE
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t cut_digit, cut_above;
+    __shared__ int wave_cnt[2][NW];
+
+    const int r = rows - 1 - (int)blockIdx.x;
+    const int b = r / n_q, i = r % n_q;
+    const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, i);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int32_t* out = indices + (int64_t)r * top_k;
+    const float* row = scores + (int64_t)r * ld;
+
+    if (L <= top_k) {  // keep the whole history
+        for (int t = tid; t < top_k; t += NT) out[t] = t < L ? t : -1;
+        return;
+    }
+
+    auto key_at = [&](int s) -> uint32_t {
+        if constexpr (CACHE) return keys[s];
+        else return score_key(row[s]);
+    };
+
+    uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)top_k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int t = tid; t < 256; t += NT) hist[t] = 0u;
+        __syncthreads();
+        for (int s = tid; s < L; s += NT) {
+            uint32_t k;
+            if (CACHE && shift == 24) {
+                k = score_key(row[s]);
+                keys[s] = k;
+            } else {
+                k = key_at(s);
+            }
+            if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // suffix counts S(d) = #keys with digit >= d; the cut digit D has
+            // S(D) >= krem > S(D+1).
+            const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+            const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+            const uint32_t tot = h0 + h1 + h2 + h3;
+            uint32_t T = tot;
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t o = __shfl_down(T, off, 64);
+                if (lane + off < 64) T += o;
+            }
+            const uint32_t above = T - tot;
+            const uint32_t S3 = above + h3, S2 = S3 + h2, S1 = S2 + h1, S0 = S1 + h0;
+            if (S3 >= krem && above < krem) { cut_digit = 4 * lane + 3; cut_above = above; }
+            if (S2 >= krem && S3 < krem) { cut_digit = 4 * lane + 2; cut_above = S3; }
+            if (S1 >= krem && S2 < krem) { cut_digit = 4 * lane + 1; cut_above = S2; }
+            if (S0 >= krem && S1 < krem) { cut_digit = 4 * lane; cut_above = S1; }
+        }
+        __syncthreads();
+        prefix |= cut_digit << shift;
+        mask |= 255u << shift;
+        krem -= cut_above;
+    }
+    // prefix is the k-th largest key; krem keys equal to it are taken, lowest first.
+    const uint32_t T = prefix;
+    int n_sel = 0, n_eq = 0, par = 0;
+    for (int base = 0; base < L && n_sel < top_k; base += NT, par ^= 1) {
+        const int s = base + tid;
+        const uint32_t k = s < L ? key_at(s) : 0u;
+        const bool gt = s < L && k > T, eq = s < L && k == T;
+        const uint64_t meq = ballot(eq);
+        if (lane == 0) wave_cnt[par][wave] = __popcll(meq);
+        __syncthreads();
+        int eq_before = 0, eq_tot = 0;
+        for (int w = 0; w < NW; ++w) {
+            const int c = wave_cnt[par][w];
+            eq_before += w < wave ? c : 0;
+            eq_tot += c;
+        }
+        const int eq_rank = n_eq + eq_before + lanes_below(meq);
+        const bool sel = gt || (eq && eq_rank < (int)krem);
+        const uint64_t msel = ballot(sel);
+        __syncthreads();  // all reads of wave_cnt[par] done
+        if (lane == 0) wave_cnt[par][wave] = __popcll(msel);
+        __syncthreads();
+        int sel_before = 0, sel_tot = 0;
+        for (int w = 0; w < NW; ++w) {
+            const int c = wave_cnt[par][w];
+            sel_before += w < wave ? c : 0;
+            sel_tot += c;
+        }
+        const int slot = n_sel + sel_before + lanes_below(msel);
+        if (sel && slot < top_k) out[slot] = s;
+        n_sel += sel_tot;
+        n_eq += eq_tot;
+    }
+}
+
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
+    const int rows = a.batch * a.n_q;
+    if (rows == 0) return hipSuccess;
+    const bool cache = a.max_seq_len <= kTopkCacheMax;
+    const size_t sh = cache ? sizeof(uint32_t) * (size_t)a.max_seq_len : 0;
+    if (cache)
+        hipLaunchKernelGGL((topk_kernel<512, true>), dim3(rows), dim3(512), sh, st, a.scores, a.ld,
+                           a.seq_lens, a.n_q, a.max_seq_len, rows, a.top_k, a.indices);
+    else
+        hipLaunchKernelGGL((topk_kernel<1024, false>), dim3(rows), dim3(1024), 0, st, a.scores, a.ld,
+                           a.seq_lens, a.n_q, a.max_seq_len, rows, a.top_k, a.indices);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,112 @@
+"""The C ABI on the host (CPU only): loading, exported symbols, validation, sizes.
+
+No call here reaches a kernel launch: each one either is a pure host query or
+fails validation first, which the ABI promises happens before anything is
+enqueued.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sparse_attention_lightningindexer_amd import binding as B
+from sparse_attention_lightningindexer_amd.inputs import make_workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = B.lib()
+    decl = _declared()
+    assert set(decl) == set(B.EXPORTS), decl
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = B.lib()
+    for s in range(6):
+        assert lib.dsa_status_string(s).decode().startswith(["DSA_OK", "DSA_ERR_NULL", "DSA_ERR_SHAPE",
+                                                             "DSA_ERR_UNSUPPORTED", "DSA_ERR_WORKSPACE",
+                                                             "DSA_ERR_HIP"][s])
+    assert lib.dsa_version() >= 100
+
+
+def _fake_structs(wl):
+    """ABI structs over fake (never dereferenced) device addresses."""
+    fake = 0x10000
+    batch = B.dsa_batch(wl.batch, wl.n_q, fake, fake, wl.max_blocks, 64, wl.max_seq_len)
+    kc = B.dsa_cache(fake, None, B._DT[wl.idx_dtype], 0, 0, wl.d_I, wl.num_blocks)
+    idx = B.dsa_indexer_args(fake, B._DT[wl.idx_dtype], None, wl.H_I, wl.d_I, fake, kc)
+    kvc = B.dsa_cache(fake, None, B._DT[wl.kv_dtype], 0, 0, wl.d_qk, wl.num_blocks)
+    attn = B.dsa_attn_args(fake, B._DT[wl.q_dtype], wl.H, wl.d_v, wl.sm_scale, kvc, fake, None)
+    return batch, idx, attn
+
+
+def test_validation_errors_are_returned_before_any_launch():
+    lib = B.lib()
+    wl = make_workload(2, batch=2, lens=[100, 50])
+    batch, idx, attn = _fake_structs(wl)
+    ref = C.byref
+    assert lib.dsa_indexer_scores(None, ref(idx), 0x10000, 128, None) == B.DSA_ERR_NULL
+    assert lib.dsa_indexer_scores(ref(batch), ref(idx), None, 128, None) == B.DSA_ERR_NULL
+    assert lib.dsa_indexer_scores(ref(batch), ref(idx), 0x10000, 10, None) == B.DSA_ERR_SHAPE  # ld < max_seq_len
+    bad = B.dsa_batch.from_buffer_copy(batch)
+    bad.block_size = 32
+    assert lib.dsa_indexer_scores(ref(bad), ref(idx), 0x10000, 128, None) == B.DSA_ERR_SHAPE
+    bad = B.dsa_batch.from_buffer_copy(batch)
+    bad.max_seq_len = bad.max_blocks * 64 + 1
+    assert lib.dsa_topk(ref(bad), 0x10000, 10**6, 16, 0x10000, None, 0, None) == B.DSA_ERR_SHAPE
+    i2 = B.dsa_indexer_args.from_buffer_copy(idx)
+    i2.n_heads = 32
+    assert lib.dsa_indexer_scores(ref(batch), ref(i2), 0x10000, 128, None) == B.DSA_ERR_UNSUPPORTED
+    i2 = B.dsa_indexer_args.from_buffer_copy(idx)
+    i2.dtype = B.DSA_E4M3   # k pool still bf16
+    assert lib.dsa_indexer_scores(ref(batch), ref(i2), 0x10000, 128, None) == B.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk(ref(batch), 0x10000, 128, 0, 0x10000, None, 0, None) == B.DSA_ERR_SHAPE
+    assert lib.dsa_topk(ref(batch), 0x10000, 128, 4097, 0x10000, None, 0, None) == B.DSA_ERR_SHAPE
+    assert lib.dsa_topk(ref(batch), None, 128, 16, 0x10000, None, 0, None) == B.DSA_ERR_NULL
+    a2 = B.dsa_attn_args.from_buffer_copy(attn)
+    a2.d_v = 256
+    assert lib.dsa_sparse_attn(ref(batch), ref(a2), 0x10000, 16, None, 0, None) == B.DSA_ERR_UNSUPPORTED
+    # 2 rows -> split partials are needed, so a missing workspace is refused
+    need = lib.dsa_sparse_attn_workspace_bytes(ref(batch), ref(attn), 2048)
+    assert need > 0
+    assert lib.dsa_sparse_attn(ref(batch), ref(attn), 0x10000, 2048, None, 0, None) == B.DSA_ERR_WORKSPACE
+    assert lib.dsa_sparse_attn(ref(batch), ref(attn), 0x10000, 2048, 0x10000, need - 1, None) == B.DSA_ERR_WORKSPACE
+    assert lib.dsa_sparse_attn(ref(batch), ref(attn), None, 2048, 0x10000, need, None) == B.DSA_ERR_NULL
+    fneed = lib.dsa_forward_workspace_bytes(ref(batch), ref(idx), ref(attn), 2048)
+    assert lib.dsa_forward(ref(batch), ref(idx), ref(attn), 2048, None, 0x10000, fneed - 1, None) == B.DSA_ERR_WORKSPACE
+    kv_mx = B.dsa_attn_args.from_buffer_copy(attn)
+    kv_mx.kv.dtype = B.DSA_E4M3
+    kv_mx.kv.scale_kind = B.DSA_SCALE_E8M0
+    kv_mx.kv.group = 32
+    assert lib.dsa_sparse_attn(ref(batch), ref(kv_mx), 0x10000, 16, 0x10000, need, None) == B.DSA_ERR_NULL
+
+
+def test_workspace_sizes_follow_the_split_rule():
+    lib = B.lib()
+    for cfg, kw in ((2, {}), (4, dict(lens=[5000] * 8)), (5, dict(batch=64, lens=100))):
+        wl = make_workload(cfg, **kw) if cfg != 5 else make_workload(2, batch=64, lens=100)
+        batch, idx, attn = _fake_structs(wl)
+        rows = wl.rows
+        n = lib.dsa_sparse_attn_workspace_bytes(C.byref(batch), C.byref(attn), 2048)
+        splits = n // (4 * rows * 128 * 513)
+        assert n == 4 * rows * splits * 128 * 513
+        assert 1 < splits <= 64 and rows * splits >= 256
+        f = lib.dsa_forward_workspace_bytes(C.byref(batch), C.byref(idx), C.byref(attn), 2048)
+        ld = (wl.max_seq_len + 63) // 64 * 64
+        assert f >= 4 * rows * ld + 4 * rows * 2048 + n
+    # enough rows: no splits, no partials
+    wl = make_workload(2, batch=300, lens=70)
+    batch, idx, attn = _fake_structs(wl)
+    assert lib.dsa_sparse_attn_workspace_bytes(C.byref(batch), C.byref(attn), 2048) == 0
+    assert lib.dsa_topk_workspace_bytes(C.byref(batch), 2048) == 0
