@@ -1,0 +1,241 @@
+"""Benchmark of the DSA stage (indexer scoring -> Top-K -> sparse MLA attention) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skewed|fp8|tiny]
+
+A step is one dsa_forward over one batch of synthetic inputs already resident
+in HBM; several independent input sets rotate so that each step's cache rows
+come from HBM rather than the 256 MB Infinity Cache.  Prints one JSON line:
+whole-step throughput (query tokens/s), the roofline of the dominant kernel
+(timed with HIP events on the launch stream), and the CPU oracle timed on the
+host's cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA tokens/s (LI+TopK+SFA), decode B32@8k & prefill 32k; % HBM/MFMA peak"
+WORKLOADS = {"tiny": 1, "decode": 2, "prefill": 3, "skewed": 4, "fp8": 5}
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def algorithmic(wl):
+    """Bytes and flops the method must move/compute per step, per stage (see the design notes).
+
+    The scores intermediate is not counted; gathers count one latent row per
+    selected (row, position); the attention counts QK^T over d_qk and PV over d_v.
+    """
+    import numpy as np
+    L = wl.row_lens().astype(np.int64)
+    k = np.minimum(L, wl.top_k)
+    rows = wl.rows
+    esz = {"f32": 4, "bf16": 2, "e4m3": 1, "mxfp8": 1}
+    # indexer: each sequence's K_I rows once (shared by its n_q queries), q_I, w, scales
+    seq_hist = wl.seq_lens.astype(np.int64)
+    k_row = wl.d_I * esz[wl.idx_dtype] + (4 if wl.idx_dtype == "e4m3" else 0)
+    q_row = wl.H_I * wl.d_I * esz[wl.idx_dtype] + wl.H_I * 4 * (2 if wl.idx_dtype == "e4m3" else 1)
+    idx_bytes = int(seq_hist.sum() * k_row + rows * q_row)
+    idx_flops = int(2 * L.sum() * wl.H_I * wl.d_I)
+    # Top-K: the k_r indices written (scores are the unfused intermediate)
+    topk_bytes = int(rows * wl.top_k * 4)
+    # attention: gathered latent rows, q, out, indices
+    kv_row = wl.d_qk * esz[wl.kv_dtype] + (wl.d_qk // 32 if wl.kv_dtype == "mxfp8" else 0)
+    qb = wl.H * wl.d_qk * esz[wl.q_dtype]
+    ob = wl.H * wl.d_v * (4 if wl.out_dtype == "f32" else 2)
+    attn_bytes = int(k.sum() * kv_row + rows * (qb + ob + wl.top_k * 4))
+    attn_flops = int(2 * k.sum() * wl.H * (wl.d_qk + wl.d_v))
+    return {"indexer": (idx_bytes, idx_flops), "topk": (topk_bytes, 0), "attention": (attn_bytes, attn_flops)}
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "indexer": ["sparse_attention_lightningindexer_amd/csrc/indexer.hip",
+                "sparse_attention_lightningindexer_amd/csrc/common.hpp"],
+    "topk": ["sparse_attention_lightningindexer_amd/csrc/topk.hip",
+             "sparse_attention_lightningindexer_amd/csrc/common.hpp"],
+    "attention": ["sparse_attention_lightningindexer_amd/csrc/sfa.hip",
+                  "sparse_attention_lightningindexer_amd/csrc/common.hpp"],
+}
+
+
+def measured_traffic(stage: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json.txt")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.loads(open(path).read())
+    except ValueError:
+        return None
+    if rec.get("source_hash") != source_hash(KERNEL_SOURCES[stage]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle as it stands, on the host's cores, over a bounded sample of rows."""
+    import numpy as np
+    from oracle import oracle as O
+    rows_all = np.arange(wl.rows, dtype=np.int32)
+    if wl.rows > 64:  # prefill: rows spread evenly over the causal range
+        sample = np.linspace(0, wl.rows - 1, 16).astype(np.int32)
+        what = f"16 of {wl.rows} query rows, evenly spaced over positions (whole stage per row)"
+    else:
+        sample = rows_all
+        what = f"all {wl.rows} query rows of one step (whole stage)"
+    done, t0 = 0, time.perf_counter()
+    reps = 0
+    while True:
+        O.forward(wl, rows=sample)
+        done += len(sample)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s or wl.rows > 64:
+            break
+    dt = time.perf_counter() - t0
+    rate = done / dt
+    if wl.rows > 64:  # scale: the sampled rows' mean cost stands for all rows
+        what += f"; {dt:.1f} s"
+    else:
+        what += f" x {reps}; {dt:.1f} s"
+    return {"value": rate, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle", "sample": what}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=list(WORKLOADS))
+    ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the stage shards by sequence with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from sparse_attention_lightningindexer_amd import binding as B
+    from sparse_attention_lightningindexer_amd.inputs import make_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()  # fail loudly when the HIP library is missing
+    cfg = WORKLOADS[args.workload]
+    nsets = 1 if cfg == 3 else args.sets  # prefill: one set already exceeds the caches many times over
+    print(f"[bench] generating {nsets} input set(s) of workload {args.workload}", file=sys.stderr, flush=True)
+    sets = []
+    for s in range(nsets):
+        wl = make_workload(cfg, rotation=s)
+        dev = B.DeviceInputs(wl)
+        ws = torch.empty(max(1, B.dsa_forward_workspace_bytes(dev)), dtype=torch.uint8, device="cuda")
+        idx = torch.empty((wl.rows, wl.top_k), dtype=torch.int32, device="cuda")
+        sets.append((wl, dev, ws, idx))
+        if s == 0:
+            wl0 = wl
+    del wl
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        _, dev, ws, idx = sets[i % nsets]
+        B.dsa_forward(dev, indices_out=idx, ws=ws, stream=stream)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps of the whole stage
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = gpu_ms / args.steps
+    rows = wl0.rows
+    value = rows * args.steps / (gpu_ms / 1e3)
+    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)",
+          file=sys.stderr, flush=True)
+
+    # per-stage durations: the same kernels through the three unfused calls,
+    # HIP events recorded on the launch stream between them
+    acc = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * args.steps)]
+    scores = [torch.empty((s[0].rows, max(1, s[0].max_seq_len)), dtype=torch.float32, device="cuda")
+              for s in sets]
+    attn_ws = [torch.empty(max(1, B.dsa_sparse_attn_workspace_bytes(s[1])), dtype=torch.uint8, device="cuda")
+               for s in sets]
+    for i in range(args.steps):
+        _, dev, _, idx = sets[i % nsets]
+        sc = scores[i % nsets]
+        ev[4 * i].record(stream)
+        B.dsa_indexer_scores(dev, sc, stream=stream)
+        ev[4 * i + 1].record(stream)
+        B.dsa_topk(dev, sc, indices=idx, stream=stream)
+        ev[4 * i + 2].record(stream)
+        B.dsa_sparse_attn(dev, idx, ws=attn_ws[i % nsets], stream=stream)
+        ev[4 * i + 3].record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        acc["indexer"] += ev[4 * i].elapsed_time(ev[4 * i + 1])
+        acc["topk"] += ev[4 * i + 1].elapsed_time(ev[4 * i + 2])
+        acc["attention"] += ev[4 * i + 2].elapsed_time(ev[4 * i + 3])
+    stage_us = {k: v / args.steps * 1e3 for k, v in acc.items()}
+    algo = algorithmic(wl0)
+    dom = max(stage_us, key=stage_us.get)
+    nbytes, nflops = algo[dom]
+    dur_s = stage_us[dom] * 1e-6
+    if cfg == 3 and dom != "topk":
+        ach = nflops / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / BF16_PEAK_TFLOPS}
+    else:
+        ach = nbytes / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS}
+    roof["traffic"] = measured_traffic(dom, args.workload)
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = nflops
+    roof["avg_us"] = stage_us[dom]
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "fp8e4m3+bf16"}[wl0.idx_dtype],
+        "data": "synthetic",
+        "config": {"workload": wl0.cfg["name"], "batch": wl0.batch, "n_q": wl0.n_q,
+                   "context": int(wl0.max_seq_len), "top_k": wl0.top_k, "index_heads": wl0.H_I,
+                   "index_dim": wl0.d_I, "heads": wl0.H, "d_qk": wl0.d_qk, "d_v": wl0.d_v,
+                   "paging": wl0.cfg["paging"], "input_sets": nsets},
+        "roofline": roof,
+        "stages_us": stage_us,
+    }
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl0, args.cpu_budget)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -300,45 +300,53 @@ __global__ __launch_bounds__(512, 1) void sfa_mla_kernel(
 }
 
 // Merge split partials: out = sum_s exp(lse_s - LSE) * O_s, LSE = log sum_s exp(lse_s).
-// grid rows, block 256: thread t -> head t/2, channels 256*(t%2) .. +256.
+// grid (rows, H/4), block 256: wave w -> head 4*blockIdx.y + w, lane -> 8 channels,
+// so every load instruction of a wave reads 2 KB of contiguous partials.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void sfa_combine_kernel(const float* __restrict__ ws_o,
                                                           const float* __restrict__ ws_lse, int splits,
                                                           int H, int Dv, void* __restrict__ out,
                                                           float* __restrict__ lse) {
     const int row = blockIdx.x;
-    for (int t = threadIdx.x; t < H * 2; t += 256) {
-        const int h = t >> 1, half = t & 1;
-        float M = -INFINITY;
-        for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_lse[((int64_t)row * splits + s) * H + h]);
-        float W = 0.f;
-        float wgt[kAttnMaxSplits];
+    const int h = 4 * blockIdx.y + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (h >= H) return;
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_lse[((int64_t)row * splits + s) * H + h]);
+    float W = 0.f;
+    for (int s = 0; s < splits; ++s) {
+        const float ls = ws_lse[((int64_t)row * splits + s) * H + h];
+        W += (M == -INFINITY || ls == -INFINITY) ? 0.f : expf(ls - M);
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    for (int d = 8 * lane; d < Dv; d += 8 * 64) {
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < splits; ++s) {
             const float ls = ws_lse[((int64_t)row * splits + s) * H + h];
-            wgt[s] = (M == -INFINITY || ls == -INFINITY) ? 0.f : expf(ls - M);
-            W += wgt[s];
-        }
-        const float inv = W > 0.f ? 1.f / W : 0.f;
-        const int d0 = half * (Dv / 2);
-        for (int d = d0; d < d0 + Dv / 2; d += 4) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < splits; ++s) {
-                if (wgt[s] == 0.f) continue;
-                const f32x4 v = *reinterpret_cast<const f32x4*>(ws_o + (((int64_t)row * splits + s) * H + h) * Dv + d);
-                for (int i = 0; i < 4; ++i) acc[i] = fmaf(wgt[s], v[i], acc[i]);
-            }
-            if constexpr (OUT_BF16) {
-                uint16_t* o = (uint16_t*)out + ((int64_t)row * H + h) * Dv + d;
-                const uint32_t lo = f32_to_bf16_bits(acc[0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[1] * inv) << 16);
-                const uint32_t hi = f32_to_bf16_bits(acc[2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[3] * inv) << 16);
-                *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
-            } else {
-                float* o = (float*)out + ((int64_t)row * H + h) * Dv + d;
-                *reinterpret_cast<f32x4*>(o) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+            if (M == -INFINITY || ls == -INFINITY) continue;
+            const float wgt = expf(ls - M);
+            const float* src = ws_o + (((int64_t)row * splits + s) * H + h) * Dv + d;
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+            for (int i = 0; i < 4; ++i) {
+                a0[i] = fmaf(wgt, v0[i], a0[i]);
+                a1[i] = fmaf(wgt, v1[i], a1[i]);
             }
         }
-        if (lse != nullptr && half == 0) lse[(int64_t)row * H + h] = W > 0.f ? M + logf(W) : -INFINITY;
+        if constexpr (OUT_BF16) {
+            uint16_t* o = (uint16_t*)out + ((int64_t)row * H + h) * Dv + d;
+            uint32_t w4[4];
+            for (int i = 0; i < 2; ++i) {
+                w4[i] = f32_to_bf16_bits(a0[2 * i] * inv) | ((uint32_t)f32_to_bf16_bits(a0[2 * i + 1] * inv) << 16);
+                w4[2 + i] = f32_to_bf16_bits(a1[2 * i] * inv) | ((uint32_t)f32_to_bf16_bits(a1[2 * i + 1] * inv) << 16);
+            }
+            *reinterpret_cast<uint4*>(o) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        } else {
+            float* o = (float*)out + ((int64_t)row * H + h) * Dv + d;
+            *reinterpret_cast<f32x4*>(o) = f32x4{a0[0] * inv, a0[1] * inv, a0[2] * inv, a0[3] * inv};
+            *reinterpret_cast<f32x4*>(o + 4) = f32x4{a1[0] * inv, a1[1] * inv, a1[2] * inv, a1[3] * inv};
+        }
     }
+    if (lse != nullptr && lane == 0) lse[(int64_t)row * H + h] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
 // fp32 attention for small shapes: one wave per (head, row); logits of the
@@ -441,8 +449,8 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st) {
                            (uint16_t*)a.out, a.lse, a.ws, ws_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
-    hipLaunchKernelGGL((sfa_combine_kernel<true>), dim3(rows), dim3(256), 0, st, a.ws, ws_lse, splits, kH, kDv,
-                       a.out, a.lse);
+    hipLaunchKernelGGL((sfa_combine_kernel<true>), dim3(rows, kH / 4), dim3(256), 0, st, a.ws, ws_lse, splits, kH,
+                       kDv, a.out, a.lse);
     return hipGetLastError();
 }
 
