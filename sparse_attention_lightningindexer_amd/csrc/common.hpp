@@ -77,6 +77,59 @@ __device__ __forceinline__ uint64_t ballot(bool p) {
     return __builtin_amdgcn_ballot_w64(p);
 }
 
+// ---- asynchronous gathers into LDS, outside the compiler's wait-count tracking
+//
+// global_load_lds writes each lane's bytes to LDS at M0 + lane * size.  Issued
+// through the builtin, the compiler cannot tell which LDS buffer such a load
+// targets and waits for it (vmcnt(0)) before any later LDS read or barrier,
+// which serializes a multi-stage gather pipeline.  Issued here, the loads are
+// invisible to its bookkeeping: the caller waits on them with wait_vmcnt(n)
+// (n = this wave's vector-memory operations issued after the ones needed; they
+// complete in order) and then sync_lds().  Extra outstanding loads only make
+// the compiler's own waits stricter, never incorrect.  `lds` must be uniform.
+__device__ __forceinline__ void lds_gather16(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_gather4(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wave-uniform n in [0, 31]
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+#define DSA_W(N) case N: wait_vmcnt<N>(); break;
+    DSA_W(0) DSA_W(1) DSA_W(2) DSA_W(3) DSA_W(4) DSA_W(5) DSA_W(6) DSA_W(7)
+    DSA_W(8) DSA_W(9) DSA_W(10) DSA_W(11) DSA_W(12) DSA_W(13) DSA_W(14) DSA_W(15)
+    DSA_W(16) DSA_W(17) DSA_W(18) DSA_W(19) DSA_W(20) DSA_W(21) DSA_W(22) DSA_W(23)
+    DSA_W(24) DSA_W(25) DSA_W(26) DSA_W(27) DSA_W(28) DSA_W(29) DSA_W(30)
+#undef DSA_W
+    default: wait_vmcnt<31>(); break;
+    }
+}
+// Workgroup barrier for LDS data only (no wait on outstanding global loads).
+__device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// The value of x, hidden from the optimizer so that address arithmetic derived
+// from it is recomputed where it is used instead of being hoisted out of a loop
+// (and kept live, or spilled) for the whole kernel.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// Scheduling fence: no instruction is moved across it, so a block of LDS
+// reads written before it is issued as a block (their latencies overlap)
+// instead of being interleaved one by one with the MFMAs that consume them.
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// LDS byte address of a __shared__ object (generic pointer cast to the LDS address space).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const DSA_LDS void*)p;
+}
+
 // Causal history of row r = b*n_q + i with the clamped sequence length Lb.
 __device__ __forceinline__ int history_len(int Lb, int n_q, int i) {
     int L = Lb - n_q + i + 1;

@@ -171,31 +171,57 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
 }
 
 // Prefill (many query rows per sequence): 8 waves x 2 rows = 16 rows per row
-// block; the block's K tiles are staged in LDS (gathered directly into LDS,
-// double-buffered) and shared by all 16 rows.  Causal load skew is balanced
-// by pairing row block x with row block NB-1-x in one workgroup, the
-// head-tail pairing the pages use across devices ("Day0 Inference Adaptation
-// and Performance Optimization for New-Architecture LLMs", §6.2 Zigzag
-// Layout), applied here across the GPU's compute units.
-// grid (ceil(NB/2), batch), block 512.
+// block; the block's K tiles are gathered straight into a 4-deep LDS ring and
+// shared by all 16 rows.  Causal load skew is balanced by pairing row block x
+// with row block NB-1-x in one workgroup, the head-tail pairing the pages use
+// across devices ("Day0 Inference Adaptation and Performance Optimization for
+// New-Architecture LLMs", §6.2 Zigzag Layout), applied here across the GPU's
+// compute units.  grid (ceil(NB/2), batch), block 512.
+constexpr int kIdxRing = 4;
+
 template <class T>
 __global__ __launch_bounds__(512) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kpool, const float* __restrict__ kscale,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
     int64_t num_blocks, int n_q, int max_seq_len, float* __restrict__ scores, int64_t ld) {
-    constexpr int UNITS = T::ROW / 16;          // 16-byte units per K row
+    constexpr int UNITS = T::ROW / 16;              // 16-byte units per K row
     constexpr int TILE_BYTES = kBlock * T::ROW;
-    __shared__ __attribute__((aligned(16))) uint8_t ktile[2][TILE_BYTES];
-    __shared__ int tile_ok[2];
+    constexpr int TILE_K = TILE_BYTES / (16 * kWave);  // wave-instructions per tile (16 or 8)
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[kIdxRing][TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) float kst[kIdxRing][kBlock];  // fp8 scales of the tile
+    __shared__ int tile_ok[kIdxRing];
 
     const int b = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, j = lane & 15;
     const int Lb = clamp_len(seq_lens, b, max_seq_len);
     const int NB = (n_q + 15) / 16;
     const int rbs[2] = {(int)blockIdx.x, NB - 1 - (int)blockIdx.x};
     const int npass = (rbs[1] > rbs[0]) ? 2 : 1;
+    // gathers issued per tile by this wave: K units (+ the scale line, wave 0, fp8)
+    const int per_tile = (TILE_K - wave + 7) / 8 + ((T::SCALED && wave == 0) ? 1 : 0);
+
+    // Gather tile t into ring slot `buf`: unit U of the tile (row U/UNITS, column
+    // U%UNITS) receives global column (U%UNITS) ^ (row % UNITS), an XOR swizzle
+    // that keeps the column reads below bank-conflict free.  Absent blocks read
+    // block 0 and are flagged; their scores are -inf.
+    auto stage = [&](int t, int buf) {
+        int64_t p = phys_block(table, max_blocks, b, __builtin_amdgcn_readfirstlane(t), num_blocks);
+        if (threadIdx.x == 0) tile_ok[buf] = p >= 0;
+        if (p < 0) p = 0;
+        const uint8_t* base = kpool + p * TILE_BYTES;
+        const uint32_t dst = lds_addr(&ktile[buf][0]);
+        for (int k = wave; k < TILE_K; k += 8) {
+            const int U = k * kWave + lane;
+            const int row = U / UNITS, col = (U % UNITS) ^ (row % UNITS);
+            lds_gather16(base + row * T::ROW + col * 16, dst + k * kWave * 16);
+        }
+        if constexpr (T::SCALED) {
+            if (wave == 0) lds_gather4(kscale + p * kBlock + lane, lds_addr(&kst[buf][0]));
+        }
+    };
 
     for (int pass = 0; pass < npass; ++pass) {
         const int rb = rbs[pass];
@@ -211,38 +237,18 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
         const int last = (rb * 16 + 15 < n_q - 1) ? rb * 16 + 15 : n_q - 1;
         const int Lmax = history_len(Lb, n_q, last);
         const int ntiles = (Lmax + kBlock - 1) / kBlock;
+        // retire the query loads before the ring starts (known to the compiler, so
+        // it places no wait for them inside the tile loop)
+        __builtin_amdgcn_s_waitcnt(0x0f70);
 
-        // Gather tile t into LDS buffer `buf`: unit U of the tile (row U/UNITS,
-        // column U%UNITS) receives global column (U%UNITS) ^ (row % UNITS), an
-        // XOR swizzle that keeps the column reads below bank-conflict free.
-        auto stage = [&](int t, int buf) {
-            int64_t p = phys_block(table, max_blocks, b, t, num_blocks);
-            if (threadIdx.x == 0) tile_ok[buf] = p >= 0;
-            if (p < 0) p = 0;
-            const uint8_t* base = kpool + p * TILE_BYTES;
-            for (int k = wave; k < TILE_BYTES / (16 * kWave); k += 8) {
-                const int U = k * kWave + lane;
-                const int row = U / UNITS, col = (U % UNITS) ^ (row % UNITS);
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)(base + row * T::ROW + col * 16),
-                    (DSA_LDS void*)(&ktile[buf][k * kWave * 16]), 16, 0, 0);
-            }
-        };
-        if (ntiles > 0) stage(0, 0);
+        for (int t = 0; t < kIdxRing - 1 && t < ntiles; ++t) stage(t, t);
         for (int t = 0; t < ntiles; ++t) {
-            const int buf = t & 1;
-            __builtin_amdgcn_s_waitcnt(0x0f70 & ~0x3f00);  // vmcnt(0)
-            __syncthreads();
-            if (t + 1 < ntiles) stage(t + 1, buf ^ 1);
+            const int buf = t % kIdxRing;
+            wait_vmcnt(per_tile * min(kIdxRing - 2, ntiles - 1 - t));  // tile t has landed
+            sync_lds();  // ... for every wave; slot (t-1) % 4 is free
+            if (t + kIdxRing - 1 < ntiles) stage(t + kIdxRing - 1, (t + kIdxRing - 1) % kIdxRing);
             const int s0 = t * kBlock;
             const bool ok = tile_ok[buf] != 0;
-            float ksc[4] = {1.f, 1.f, 1.f, 1.f};
-            if constexpr (T::SCALED) {
-                if (ok) {
-                    const int64_t p = phys_block(table, max_blocks, b, t, num_blocks);
-                    for (int nt = 0; nt < 4; ++nt) ksc[nt] = kscale[p * kBlock + 16 * nt + j];
-                }
-            }
             if (s0 < Lr[0] || s0 < Lr[1]) {
                 for (int nt = 0; nt < 4; ++nt) {
                     typename T::frag kf[T::KSTEPS];
@@ -259,6 +265,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
                             kf[ks] = typename T::frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                         }
                     }
+                    const float ksc = T::SCALED ? kst[buf][prow] : 1.f;
                     for (int qi = 0; qi < 2; ++qi) {
                         if (s0 >= Lr[qi]) continue;
                         f32x4 acc[4];
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
                             for (int ks = 0; ks < T::KSTEPS; ++ks) acc[mt] = mma(qa[qi][mt][ks], kf[ks], acc[mt]);
                         }
                         float v = head_weighted_relu_sum(acc, wr[qi]);
-                        if constexpr (T::SCALED) v *= ksc[nt];
+                        if constexpr (T::SCALED) v *= ksc;
                         if (!ok) v = -INFINITY;
                         const int s = s0 + prow;
                         const int64_t row = (int64_t)b * n_q + rb * 16 + wave * 2 + qi;
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
                 }
             }
         }
-        __syncthreads();  // LDS buffers are reused by the next pass
+        sync_lds();  // ring slots are reused by the next pass
     }
 }
 

@@ -9,7 +9,7 @@ namespace dsa {
 
 constexpr int kTopkCacheMax = 16384;      // rows up to this length keep their keys in LDS
 constexpr int kAttnMaxSplits = 32;        // split partials merged per row
-constexpr int kAttnMaxSplitSlots = 4096;  // index slots one attention workgroup compacts
+constexpr int kAttnMaxSplitSlots = 2048;  // index slots one attention workgroup compacts
 
 struct IndexerLaunch {
     int dtype;                 // 0 f32, 1 bf16, 2 e4m3

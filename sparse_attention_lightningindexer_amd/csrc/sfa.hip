@@ -64,40 +64,90 @@ __device__ __forceinline__ void dequant_unit(i32x4 codes, float scale, i32x4& lo
     hi = i32x4{(int)packed[4], (int)packed[5], (int)packed[6], (int)packed[7]};
 }
 
+// Work decomposition: one workgroup per (row, half of the heads, split of the
+// index list).  The two head halves write disjoint outputs (no merge); only
+// position splits produce partials, merged by LSE afterwards.  The workgroups
+// of one row are consecutive on one XCD, so the two halves' gathers of the
+// same latent rows meet in that XCD's L2.
+//
+// Workgroup: 4 waves, one per SIMD (the whole register file each), 64 heads.
+// Per chunk of 32 positions:
+//   QK   wave w owns heads 32(w&1) .. +31 of the half and positions 16(w>>1)
+//        .. +15 of the chunk: S^T = K . Q^T with Q^T resident in registers,
+//        each K fragment read from LDS feeding two MFMAs; the two waves of a
+//        head pair exchange their partial row maxima through LDS, then each
+//        writes its bf16 probabilities P[head][pos] and keeps a partial
+//        denominator (summed at the end);
+//   PV   wave w owns value channels 128w .. 128w+127 for the half's 64 heads:
+//        O^T[d][h] += V^T . P^T, each V^T fragment (transposing LDS read)
+//        feeding 4 MFMAs and each P^T fragment 8.
+// LDS (one workgroup per CU): 3 x 36 KiB gather ring (bf16 cache), or 3 x
+// 18.75 KiB fp8 staging + 2 bf16 tiles (MXFP8 cache); + P 5 KiB + slot list 8 KiB.
+constexpr int kWaves = 4, kThreads = kWaves * kWave;
+constexpr int kHalf = kH / 2;                   // heads per workgroup
+constexpr int kDvPerWave = kDv / kWaves;        // 128 value channels = 8 D-tiles
+constexpr int kRing = 3;                        // chunks resident in LDS (bf16 cache)
+constexpr int kMxRing = 3;                      // fp8 staging slots (MXFP8 cache)
+constexpr int kMxCodeB = kCh * kDqk;            // fp8 codes of a chunk (18432 B)
+constexpr int kMxScaleW = 24;                   // bytes of an aligned window holding a row's 18 scales
+constexpr int kMxStageB = kMxCodeB + kCh * kMxScaleW;
+constexpr int kGatherK = kTileB / (16 * kWave);          // 36 wave-instructions per bf16 chunk
+constexpr int kMxCodeK = kMxCodeB / (16 * kWave);        // 18 per fp8 chunk
+constexpr int kMxScaleK = kCh * kMxScaleW / (4 * kWave); // 3 (dword lanes), waves 1..3
+constexpr int kPRow = kCh * 2 + 16;             // bytes per head row of P (64 + 16 pad)
+
 template <bool MX>
-__global__ __launch_bounds__(512, 1) void sfa_mla_kernel(
+__global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kvscale,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
     int64_t num_blocks, int n_q, int max_seq_len, int rows, const int32_t* __restrict__ indices,
     int top_k, int per_split, int splits, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[2][kTileB];
-    __shared__ __attribute__((aligned(16))) uint8_t stage[MX ? kCh * kDqk : 16];  // fp8 codes of the next chunk
+    __shared__ __attribute__((aligned(16))) uint8_t tile[MX ? 2 : kRing][kTileB];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[MX ? kMxRing : 1][MX ? kMxStageB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][kHalf * kPRow];  // P[head][pos] bf16, by chunk parity
+    __shared__ float alpha_s[2][kHalf];  // rescale factor per head, by chunk parity
+    __shared__ float pmax_s[2][kHalf]; // chunk maximum per head over each position half
+    __shared__ float lpart_s[2][kHalf]; // final partial denominators per position half
+    __shared__ int rescale_chunk[2];  // the chunk (by parity) whose factors are not all 1
     __shared__ int32_t prow[kAttnMaxSplitSlots];
-    __shared__ int wave_cnt[8];
+    __shared__ int wave_cnt[kWaves];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, j = lane & 15;
 
-    // work item: with splits, the splits of one row share an XCD (ids equal mod 8)
-    int row, split;
-    if (splits == 1) {
-        row = rows - 1 - (int)blockIdx.x;  // longest histories first in prefill
-        split = 0;
-    } else {
-        const int x = blockIdx.x & 7, jj = blockIdx.x >> 3;
-        row = (jj / splits) * 8 + x;
-        split = jj % splits;
-    }
-    if (row >= rows) return;  // padding of the XCD-aware grid (block-uniform)
+    // work item (row, half, split); ids equal mod 8 share an XCD, and a row's
+    // 2*splits workgroups are consecutive on it.  Rows run longest-first.
+    const int per_row = 2 * splits;
+    const int x = blockIdx.x & 7, jj = blockIdx.x >> 3;
+    const int rows_pad = (rows + 7) & ~7;
+    const int row = rows_pad - 1 - ((jj / per_row) * 8 + x);
+    const int half = (jj % per_row) & 1, split = (jj % per_row) >> 1;
+    if (row < 0 || row >= rows) return;  // padding of the grid (block-uniform)
+    const int hb = half * kHalf;         // first head of this workgroup
     const int b = row / n_q, qi = row % n_q;
     const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, qi);
     const int slot0 = split * per_split;
     const int slot1 = min(top_k, slot0 + per_split);
 
+    // QK role of this wave: head pair hq (32 heads) x position half ph.  Q^T
+    // fragments: qf[ht][ks] holds q[hb + 32hq + 16ht + j][32ks + 8g .. +8].
+    // Loaded first so that they retire, with the index loads below, before the
+    // gather ring starts (a wait for them inside the loop would drain it).
+    const int hq = wave & 1, ph = wave >> 1;
+    const int hl0 = 32 * hq;             // first head of the pair, within the half
+    bf16x8 qf[2][kDqk / 32];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+        const uint16_t* qrow = q + ((int64_t)row * kH + hb + hl0 + 16 * ht + j) * kDqk + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < kDqk / 32; ++ks) qf[ht][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    }
+
     // 0. ordered compaction of the valid index slots into pool-row numbers
     int n_valid = 0;
-    for (int base = slot0; base < slot1; base += 512) {
+    for (int base = slot0; base < slot1; base += kThreads) {
         const int t = base + tid;
         const int s = t < slot1 ? indices[(int64_t)row * top_k + t] : -1;
         int pr = -1;
@@ -109,7 +159,7 @@ __global__ __launch_bounds__(512, 1) void sfa_mla_kernel(
         if (lane == 0) wave_cnt[wave] = __popcll(m);
         __syncthreads();
         int before = 0, tot = 0;
-        for (int w = 0; w < 8; ++w) {
+        for (int w = 0; w < kWaves; ++w) {
             before += w < wave ? wave_cnt[w] : 0;
             tot += wave_cnt[w];
         }
@@ -118,184 +168,293 @@ __global__ __launch_bounds__(512, 1) void sfa_mla_kernel(
         __syncthreads();
     }
     const int nchunks = (n_valid + kCh - 1) / kCh;
+    if (tid < 2) rescale_chunk[tid] = -1;  // visible after the first barrier of the ring
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): q and index loads retired (known to the compiler)
 
-    // Q^T fragments of this wave's 16 heads: lane holds q[h0 + j][32ks + 8g .. +8]
-    const int h0 = 16 * wave;
-    bf16x8 qf[kDqk / 32];
-    {
-        const uint16_t* qrow = q + ((int64_t)row * kH + h0 + j) * kDqk + 8 * g;
-        for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-    }
+    // O^T accumulators: o[dt][ht] holds O^T[128w + 16dt + 4g + i][head hb + 16ht + j]
+    f32x4 o[kDvPerWave / 16][kHalf / 16];
+#pragma unroll
+    for (int dt = 0; dt < kDvPerWave / 16; ++dt)
+#pragma unroll
+        for (int ht = 0; ht < kHalf / 16; ++ht) o[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // softmax state of heads hl0 + 16ht + j (the same m in both waves of the
+    // pair; l over this wave's position half only)
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-    f32x4 o[kDv / 16];
-    for (int t = 0; t < kDv / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-
-    // 1. chunk gather.  bf16: 36 wave-instructions of 64 x 16 B straight into LDS.
-    //    MXFP8: the codes (18 wave-instructions) go straight into a staging area,
-    //    the E8M0 scales of the thread's three units into registers; after the
-    //    chunk's compute they are dequantized into the bf16 tile.
-    constexpr int kMxUnits = kCh * (kDqk / 16);   // 1152 code units per chunk
-    constexpr int kMxPer = (kMxUnits + 511) / 512; // 3 per thread
     auto chunk_row = [&](int c, int r_) -> int {  // pool row of chunk row r_ (tail rows repeat a valid one)
         const int t = c * kCh + r_;
         return prow[t < n_valid ? t : c * kCh];
     };
-    auto issue_gather = [&](int c, int buf) {
-        if constexpr (!MX) {
-            for (int k = wave; k < kTileB / (16 * kWave); k += 8) {
-                const int U = k * kWave + lane;
-                const int r_ = U / kUnits, col = (U % kUnits) ^ (r_ & 7);
-                const uint8_t* src = kv + (int64_t)chunk_row(c, r_) * kRowB + col * 16;
-                __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)(&tile[buf][k * kWave * 16]),
-                                                 16, 0, 0);
+    // Gathers issued per chunk by this wave (wave-instructions k = wave + 4i).
+    constexpr int kBfPer = kGatherK / kWaves;                                                       // 9
+    const int nk_mx = (kMxCodeK - wave + kWaves - 1) / kWaves + (wave >= kWaves - kMxScaleK ? 1 : 0); // 5 or 6
+    const int per_chunk = MX ? nk_mx : kBfPer;
+
+    // 1. bf16 cache: the chunk's 32 latent rows straight into a ring tile.
+    //    Unit U (row U/72, column U%72) of the tile holds global column
+    //    (U%72) ^ (row & 7): the XOR swizzle keeps the operand reads conflict free.
+    auto issue_bf16 = [&](int c, int buf) {
+        int pr[kBfPer];
+#pragma unroll
+        for (int i = 0; i < kBfPer; ++i) pr[i] = chunk_row(c, ((wave + kWaves * i) * kWave + lane) / kUnits);
+        const uint32_t base = lds_addr(&tile[buf][0]);
+#pragma unroll
+        for (int i = 0; i < kBfPer; ++i) {
+            const int k = wave + kWaves * i;
+            const int U = k * kWave + lane;
+            const int r_ = U / kUnits, col = (U % kUnits) ^ (r_ & 7);
+            lds_gather16(kv + (int64_t)pr[i] * kRowB + col * 16, base + k * kWave * 16);
+        }
+    };
+    // 1'. MXFP8 cache: codes [32][576] and, per row, the 4-byte-aligned 24-byte
+    //     window of the scale pool that holds its 18 E8M0 scales.
+    const int64_t scale_bytes = num_blocks * kBlock * (kDqk / 32);
+    auto scale_window = [&](int pr) -> int64_t {
+        const int64_t w = ((int64_t)pr * (kDqk / 32)) & ~(int64_t)3;
+        return w + kMxScaleW <= scale_bytes ? w : scale_bytes - kMxScaleW;
+    };
+    auto issue_mx = [&](int c, int sb) {
+        const uint32_t base = lds_addr(&stage[sb][0]);
+        int pr[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int k = wave + kWaves * i;
+            if (k < kMxCodeK) pr[i] = chunk_row(c, (k * kWave + lane) / (kDqk / 16));
+        }
+        const int sk = wave - (kWaves - kMxScaleK);
+        int spr = 0;
+        if (sk >= 0) spr = chunk_row(c, (sk * kWave + lane) / (kMxScaleW / 4));
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int k = wave + kWaves * i;
+            if (k < kMxCodeK) {
+                const int cu = (k * kWave + lane) % (kDqk / 16);
+                lds_gather16(kv + (int64_t)pr[i] * kDqk + cu * 16, base + k * kWave * 16);
+            }
+        }
+        if (sk >= 0) {
+            const int dw = (sk * kWave + lane) % (kMxScaleW / 4);
+            lds_gather4(kvscale + scale_window(spr) + 4 * dw, base + kMxCodeB + sk * kWave * 4);
+        }
+    };
+    // staged fp8 chunk -> dequantized bf16 tile (all threads)
+    auto convert_mx = [&](int c, int sb, int tb) {
+#pragma unroll 1
+        for (int u = 0; u < (kMxCodeB / 16 + kThreads - 1) / kThreads; ++u) {
+            const int U = tid + kThreads * u;
+            if (U < kMxCodeB / 16) {
+                const int r_ = U / (kDqk / 16), cu = U % (kDqk / 16);
+                const int pr = chunk_row(c, r_);
+                const int off = (int)((int64_t)pr * (kDqk / 32) - scale_window(pr));
+                const float sc = e8m0_to_f32(stage[sb][kMxCodeB + r_ * kMxScaleW + off + cu / 2]);
+                i32x4 lo, hi;
+                dequant_unit(*reinterpret_cast<const i32x4*>(&stage[sb][U * 16]), sc, lo, hi);
+                *reinterpret_cast<i32x4*>(&tile[tb][lds_unit(r_, 2 * cu)]) = lo;
+                *reinterpret_cast<i32x4*>(&tile[tb][lds_unit(r_, 2 * cu + 1)]) = hi;
+            }
+        }
+    };
+
+    // 2. QK of this wave's 32 heads x 16 positions, then the softmax of the
+    //    chunk with the partner wave (same heads, other position half).
+    //    Lane holds S[head hl0 + 16ht + j][pos 16ph + 4g + i] in s[ht][i].
+    auto qk = [&](const uint8_t* T) -> auto {
+        // The 18 K fragments of the wave's 16 rows are read in two batches of 9,
+        // each batch issued ahead of its MFMAs so that LDS latencies overlap.
+        // Unit 4ks + g of row r sits at ((4(ks&1) + g) ^ (r&7)) + 8(ks>>1).
+        constexpr int KB = kDqk / 64;  // 9
+        const int r_ = 16 * ph + j;
+        const uint8_t* base0 = T + r_ * kRowB + ((g ^ (r_ & 7)) << 4);
+        const uint8_t* base1 = T + r_ * kRowB + (((4 + g) ^ (r_ & 7)) << 4);
+        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int bh = 0; bh < 2; ++bh) {
+            bf16x8 ka[KB];
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                const int ks = bh * KB + kk;
+                ka[kk] = *reinterpret_cast<const bf16x8*>(((ks & 1) ? base1 : base0) + 128 * (ks >> 1));
+            }
+            issue_fence();
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht) s[ht] = mfma_bf16(ka[kk], qf[ht][bh * KB + kk], s[ht]);
+        }
+        struct S2 { f32x4 v[2]; };
+        return S2{{s[0], s[1]}};
+    };
+    auto softmax = [&](const f32x4 (&s)[2], int c) {
+        float t[2][4];
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+            float cmax = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = c * kCh + 16 * ph + 4 * g + i < n_valid;
+                t[ht][i] = ok ? s[ht][i] * scale_log2 : -INFINITY;
+                cmax = fmaxf(cmax, t[ht][i]);
+            }
+            cmax = max_over_groups(cmax);
+            if (g == 0) pmax_s[ph][hl0 + 16 * ht + j] = cmax;
+        }
+        sync_lds();  // partial maxima of both position halves are in LDS
+        bool rescale = false;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+            const int hl = hl0 + 16 * ht + j;
+            const float cmax = fmaxf(pmax_s[0][hl], pmax_s[1][hl]);
+            float alpha = 1.f;
+            if (cmax > m_run[ht] + kRescale || (m_run[ht] == -INFINITY && cmax > -INFINITY)) {
+                alpha = m_run[ht] == -INFINITY ? 0.f : exp2f(m_run[ht] - cmax);
+                m_run[ht] = cmax;
+            }
+            rescale |= alpha != 1.f;
+            float psum = 0.f;
+            uint32_t w2[2];
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                const float p0 = t[ht][i] == -INFINITY ? 0.f : exp2f(t[ht][i] - m_run[ht]);
+                const float p1 = t[ht][i + 1] == -INFINITY ? 0.f : exp2f(t[ht][i + 1] - m_run[ht]);
+                w2[i / 2] = f32_to_bf16_bits(p0) | ((uint32_t)f32_to_bf16_bits(p1) << 16);  // P operand
+                psum += p0 + p1;                                                          // fp32 denominator
+            }
+            *reinterpret_cast<uint2*>(pbuf[c & 1] + hl * kPRow + 2 * (16 * ph + 4 * g)) = make_uint2(w2[0], w2[1]);
+            l_run[ht] = l_run[ht] * alpha + sum_over_groups(psum);
+            if (ph == 0 && g == 0) alpha_s[c & 1][hl] = alpha;
+        }
+        if (ph == 0 && ballot(rescale) != 0ull && lane == 0) rescale_chunk[c & 1] = c;  // every writer stores c
+    };
+
+    // 3. PV on this wave's 128 value channels for the half's 64 heads.  V^T
+    //    fragment: lane j of group g addresses row 8g + 4h + j/4, channels
+    //    d0 + 4(j%4) (two transposing reads give positions 8g .. 8g+7 in
+    //    order); P^T fragment: lane reads P[head 16ht + j][pos 8g .. 8g+7].
+    auto pv = [&](const uint8_t* T, int c) {
+        if (rescale_chunk[c & 1] == c) {  // workgroup-uniform
+#pragma unroll
+            for (int ht = 0; ht < kHalf / 16; ++ht) {
+                const float al = alpha_s[c & 1][16 * ht + j];
+#pragma unroll
+                for (int dt = 0; dt < kDvPerWave / 16; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[dt][ht][i] *= al;
+            }
+        }
+        bf16x8 pf[kHalf / 16];
+#pragma unroll
+        for (int ht = 0; ht < kHalf / 16; ++ht)
+            pf[ht] = *reinterpret_cast<const bf16x8*>(pbuf[c & 1] + (16 * ht + j) * kPRow + 16 * g);
+        const int e_ = j >> 2, q4 = j & 3;
+        const int r0 = 8 * g + e_, r1 = 8 * g + 4 + e_;
+#pragma unroll
+        for (int bh = 0; bh < 2; ++bh) {
+            bf16x8 vf[kDvPerWave / 32];
+#pragma unroll
+            for (int dd = 0; dd < kDvPerWave / 32; ++dd) {
+                const int dt = bh * (kDvPerWave / 32) + dd;
+                const int ch = wave * kDvPerWave + 16 * dt + 4 * q4;   // channel this lane addresses
+                const int unit = ch >> 3, byte = (ch & 7) * 2;
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (DSA_LDS v4i16*)(T + r0 * kRowB + ((unit ^ (r0 & 7)) << 4) + byte));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (DSA_LDS v4i16*)(T + r1 * kRowB + ((unit ^ (r1 & 7)) << 4) + byte));
+                const v4i16 both[2] = {lo, hi};
+                vf[dd] = *reinterpret_cast<const bf16x8*>(both);
+            }
+            issue_fence();
+#pragma unroll
+            for (int dd = 0; dd < kDvPerWave / 32; ++dd)
+#pragma unroll
+                for (int ht = 0; ht < kHalf / 16; ++ht)
+                    o[bh * (kDvPerWave / 32) + dd][ht] = mfma_bf16(vf[dd], pf[ht], o[bh * (kDvPerWave / 32) + dd][ht]);
+        }
+    };
+
+    // The gather ring: chunk c lives in ring slot c % R; at the top of
+    // iteration c this wave has issued the chunks up to c + R - 2 (bf16) or
+    // c + R - 1 (MXFP8, where the extra slot is the bf16 tile being filled).
+    if constexpr (!MX) {
+        // Software pipeline: iteration c runs QK(c), then PV(c-1), then the
+        // softmax of chunk c, so that the softmax's dependent VALU chain runs
+        // while the matrix core executes PV(c-1).  Slots: c-1 (PV), c (QK),
+        // c+1 (in flight).
+        if (nchunks > 0) issue_bf16(0, 0);
+        for (int c = 0; c < nchunks; ++c) {
+            wait_vmcnt(0);  // chunk c has landed
+            sync_lds();     // ... for every wave; softmax(c-1) wrote P and alpha; slot (c+1) % R is free
+            if (c + 1 < nchunks) issue_bf16(c + 1, (c + 1) % kRing);
+            const auto sc = qk(tile[c % kRing]);
+            if (c > 0) pv(tile[(c - 1) % kRing], c - 1);
+            softmax(sc.v, c);
+        }
+        if (nchunks > 0) {
+            sync_lds();
+            pv(tile[(nchunks - 1) % kRing], nchunks - 1);
+        }
+    } else {
+        for (int c = 0; c < kMxRing && c < nchunks; ++c) issue_mx(c, c);
+        if (nchunks > 0) {
+            wait_vmcnt(per_chunk * min(kMxRing - 1, nchunks - 1));
+            sync_lds();
+            convert_mx(0, 0, 0);
+        }
+        for (int c = 0; c < nchunks; ++c) {
+            const uint8_t* T = tile[c & 1];
+            if (c + 1 < nchunks) wait_vmcnt(per_chunk * min(kMxRing - 2, nchunks - 2 - c));  // chunk c+1 staged
+            sync_lds();  // tile c%2 converted; tile (c+1)%2, stage c%R and P are free
+            if (c + kMxRing < nchunks) issue_mx(c + kMxRing, c % kMxRing);
+            if (c + 1 < nchunks) convert_mx(c + 1, (c + 1) % kMxRing, (c + 1) & 1);
+            const auto sc = qk(T);
+            softmax(sc.v, c);
+            sync_lds();
+            pv(T, c);
+        }
+    }
+
+    // 4. results.  The denominators of the two position halves are summed.
+    if (g == 0) {
+        lpart_s[ph][hl0 + j] = l_run[0];
+        lpart_s[ph][hl0 + 16 + j] = l_run[1];
+        if (ph == 0) {
+            pmax_s[0][hl0 + j] = m_run[0];
+            pmax_s[0][hl0 + 16 + j] = m_run[1];
+        }
+    }
+    __syncthreads();
+    const int64_t part = (int64_t)row * splits + split;
+#pragma unroll
+    for (int ht = 0; ht < kHalf / 16; ++ht) {
+        const int h = hb + 16 * ht + j;
+        const float lsum = lpart_s[0][16 * ht + j] + lpart_s[1][16 * ht + j];
+        const float inv_l = lsum > 0.f ? 1.f / lsum : 0.f;
+        const int d0 = wave * kDvPerWave + 4 * g;
+        if (splits == 1) {
+            uint16_t* orow = out + ((int64_t)row * kH + h) * kDv + d0;
+#pragma unroll
+            for (int dt = 0; dt < kDvPerWave / 16; ++dt) {
+                const f32x4 v = o[dt][ht];
+                const uint32_t lo = f32_to_bf16_bits(v[0] * inv_l) | ((uint32_t)f32_to_bf16_bits(v[1] * inv_l) << 16);
+                const uint32_t hi = f32_to_bf16_bits(v[2] * inv_l) | ((uint32_t)f32_to_bf16_bits(v[3] * inv_l) << 16);
+                *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(lo, hi);
             }
         } else {
-            for (int k = wave; k < kMxUnits / kWave; k += 8) {
-                const int U = k * kWave + lane;
-                const int r_ = U / (kDqk / 16), cu = U % (kDqk / 16);
-                const uint8_t* src = kv + (int64_t)chunk_row(c, r_) * kDqk + cu * 16;
-                __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)(&stage[k * kWave * 16]), 16, 0, 0);
-            }
-        }
-    };
-    auto finish_gather = [&](int c, int buf) {  // MXFP8 only: staging -> dequantized bf16 tile
-        if constexpr (MX) {
-            float sc[kMxPer];
-            for (int u = 0; u < kMxPer; ++u) {
-                const int U = tid + 512 * u;
-                const int r_ = U / (kDqk / 16), cu = U % (kDqk / 16);
-                sc[u] = U < kMxUnits ? e8m0_to_f32(kvscale[(int64_t)chunk_row(c, r_) * (kDqk / 32) + cu / 2]) : 0.f;
-            }
-            __builtin_amdgcn_s_waitcnt(0x0f70);
-            __syncthreads();  // staging complete
-#pragma unroll 1
-            for (int u = 0; u < kMxPer; ++u) {
-                const int U = tid + 512 * u;
-                if (U < kMxUnits) {
-                    const int r_ = U / (kDqk / 16), cu = U % (kDqk / 16);
-                    i32x4 lo, hi;
-                    dequant_unit(*reinterpret_cast<const i32x4*>(&stage[U * 16]), sc[u], lo, hi);
-                    *reinterpret_cast<i32x4*>(&tile[buf][lds_unit(r_, 2 * cu)]) = lo;
-                    *reinterpret_cast<i32x4*>(&tile[buf][lds_unit(r_, 2 * cu + 1)]) = hi;
-                }
-            }
-        }
-    };
-
-    if (nchunks > 0) {
-        issue_gather(0, 0);
-        finish_gather(0, 0);
-    }
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // this wave's gathers into `buf` have landed
-        __syncthreads();
-        if (c + 1 < nchunks) issue_gather(c + 1, buf ^ 1);
-        const uint8_t* T = tile[buf];
-
-        // 2. S^T = K . Q^T : lane holds S[head j][pos 16mt + 4g + i].  Unit
-        //    4ks + g of row r sits at ((4(ks&1) + g) ^ (r&7)) + 8(ks>>1): two lane
-        //    offsets per M-tile plus a compile-time displacement.
-        f32x4 s[2];
-        for (int mt = 0; mt < 2; ++mt) {
-            s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int r_ = 16 * mt + j;
-            const uint8_t* base0 = T + r_ * kRowB + ((g ^ (r_ & 7)) << 4);
-            const uint8_t* base1 = T + r_ * kRowB + (((4 + g) ^ (r_ & 7)) << 4);
+            float* orow = ws_o + (part * kH + h) * kDv + d0;
 #pragma unroll
-            for (int ks = 0; ks < kDqk / 32; ++ks) {
-                const uint8_t* p_ = ((ks & 1) ? base1 : base0) + 128 * (ks >> 1);
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(p_);
-                s[mt] = mfma_bf16(a, qf[ks], s[mt]);
+            for (int dt = 0; dt < kDvPerWave / 16; ++dt) {
+                const f32x4 v = o[dt][ht];
+                *reinterpret_cast<f32x4*>(orow + 16 * dt) = f32x4{v[0] * inv_l, v[1] * inv_l, v[2] * inv_l, v[3] * inv_l};
             }
         }
-
-        // 3. online softmax for head h0 + j over this chunk's 32 positions
-        float t[8];
-        float cmax = -INFINITY;
-        for (int mt = 0; mt < 2; ++mt)
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = c * kCh + 16 * mt + 4 * g + i < n_valid;
-                const float v = ok ? s[mt][i] * scale_log2 : -INFINITY;
-                t[4 * mt + i] = v;
-                cmax = fmaxf(cmax, v);
-            }
-        cmax = max_over_groups(cmax);
-        float alpha = 1.f;
-        if (cmax > m_run + kRescale || (m_run == -INFINITY && cmax > -INFINITY)) {
-            alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - cmax);
-            m_run = cmax;
-        }
-        uint16_t pb[8];
-        float psum = 0.f;
-        for (int e = 0; e < 8; ++e) {
-            const float p = t[e] == -INFINITY ? 0.f : exp2f(t[e] - m_run);
-            pb[e] = f32_to_bf16_bits(p);   // P operand of the PV product
-            psum += p;                     // the denominator (and lse) keep fp32 p
-        }
-        l_run = l_run * alpha + sum_over_groups(psum);
-        if (ballot(alpha != 1.f) != 0ull) {
-            for (int d = 0; d < kDv / 16; ++d)
-                for (int i = 0; i < 4; ++i) o[d][i] *= alpha;
-        }
-        bf16x8 pf;
-        {
-            uint32_t w4[4] = {pb[0] | ((uint32_t)pb[1] << 16), pb[2] | ((uint32_t)pb[3] << 16),
-                              pb[4] | ((uint32_t)pb[5] << 16), pb[6] | ((uint32_t)pb[7] << 16)};
-            pf = *reinterpret_cast<const bf16x8*>(w4);
-        }
-
-        // 4. O^T += V^T . P^T; V^T fragment via two transposing LDS reads:
-        //    lane j of group g addresses row 16h + 4g + j/4, channels 16d + 4(j%4),
-        //    i.e. unit 2d + (j%4)/2: four lane offsets (d mod 4) per row plus a
-        //    compile-time displacement of 128 bytes per 4 d.
-        {
-            const int e_ = j >> 2, q4 = j & 3;
-            const int r0 = 4 * g + e_, r1 = 16 + 4 * g + e_;
-            const int byte = (q4 & 1) * 8;
-            const uint8_t* b0[4];
-            const uint8_t* b1[4];
-            for (int dd = 0; dd < 4; ++dd) {
-                const int u = 2 * dd + (q4 >> 1);
-                b0[dd] = T + r0 * kRowB + ((u ^ (r0 & 7)) << 4) + byte;
-                b1[dd] = T + r1 * kRowB + ((u ^ (r1 & 7)) << 4) + byte;
-            }
-#pragma unroll
-            for (int d = 0; d < kDv / 16; ++d) {
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (DSA_LDS v4i16*)(b0[d & 3] + 128 * (d >> 2)));
-                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (DSA_LDS v4i16*)(b1[d & 3] + 128 * (d >> 2)));
-                const v4i16 both[2] = {lo, hi};
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(both);
-                o[d] = mfma_bf16(a, pf, o[d]);
-            }
-        }
-        // buf^1 was last read in chunk c-1, before this iteration's barrier; the
-        // staging area is refilled only after the next barrier
-        if (MX && c + 1 < nchunks) finish_gather(c + 1, buf ^ 1);
     }
-
-    // 5. results: lane holds O^T[16d + 4g + i][head h0 + j]
-    const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
-    const float row_lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-    const int h = h0 + j;
-    if (splits == 1) {
-        uint16_t* orow = out + ((int64_t)row * kH + h) * kDv + 4 * g;
-        for (int d = 0; d < kDv / 16; ++d) {
-            const uint32_t lo = f32_to_bf16_bits(o[d][0] * inv_l) | ((uint32_t)f32_to_bf16_bits(o[d][1] * inv_l) << 16);
-            const uint32_t hi = f32_to_bf16_bits(o[d][2] * inv_l) | ((uint32_t)f32_to_bf16_bits(o[d][3] * inv_l) << 16);
-            *reinterpret_cast<uint2*>(orow + 16 * d) = make_uint2(lo, hi);
+    if (tid < kHalf) {
+        const float lsum = lpart_s[0][tid] + lpart_s[1][tid];
+        const float hl_lse = lsum > 0.f ? (pmax_s[0][tid] + log2f(lsum)) * kLn2 : -INFINITY;
+        if (splits == 1) {
+            if (lse != nullptr) lse[(int64_t)row * kH + hb + tid] = hl_lse;
+        } else {
+            ws_lse[part * kH + hb + tid] = hl_lse;
         }
-        if (lse != nullptr && g == 0) lse[(int64_t)row * kH + h] = row_lse;
-    } else {
-        const int64_t part = (int64_t)row * splits + split;
-        float* orow = ws_o + (part * kH + h) * kDv + 4 * g;
-        for (int d = 0; d < kDv / 16; ++d)
-            *reinterpret_cast<f32x4*>(orow + 16 * d) =
-                f32x4{o[d][0] * inv_l, o[d][1] * inv_l, o[d][2] * inv_l, o[d][3] * inv_l};
-        if (g == 0) ws_lse[part * kH + h] = row_lse;
     }
 }
 
@@ -408,7 +567,8 @@ __global__ __launch_bounds__(64) void sfa_f32_kernel(
 int attn_splits(int rows, int top_k, int Dqk) {
     if (Dqk != kDqk) return 1;
     const int nchunks = (top_k + kCh - 1) / kCh;
-    int s = rows >= 256 ? 1 : (256 + rows - 1) / rows;
+    // two head halves per row already; split the index list until ~256 workgroups
+    int s = rows >= 128 ? 1 : (128 + rows - 1) / rows;
     s = s > nchunks ? nchunks : s;
     s = s > kAttnMaxSplits ? kAttnMaxSplits : s;
     // each split must fit its compacted slot list in LDS
@@ -434,16 +594,16 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st) {
     }
     const int splits = a.splits;
     const int per = splits == 1 ? a.top_k : attn_per_split(a.top_k, splits);
-    const int grid = splits == 1 ? rows : ((rows + 7) / 8) * 8 * splits;
+    const int grid = ((rows + 7) / 8) * 8 * 2 * splits;   // (row, head half, split)
     const float scale_log2 = a.sm_scale * kLog2e;
     float* ws_lse = splits == 1 ? nullptr : a.ws + (size_t)rows * splits * kH * kDv;
     if (a.kv_kind == 2)
-        hipLaunchKernelGGL((sfa_mla_kernel<true>), dim3(grid), dim3(512), 0, st, (const uint16_t*)a.q,
+        hipLaunchKernelGGL((sfa_mla_kernel<true>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,
                            (const uint8_t*)a.kv, a.kvscale, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
                            a.n_q, a.max_seq_len, rows, a.indices, a.top_k, per, splits, scale_log2,
                            (uint16_t*)a.out, a.lse, a.ws, ws_lse);
     else
-        hipLaunchKernelGGL((sfa_mla_kernel<false>), dim3(grid), dim3(512), 0, st, (const uint16_t*)a.q,
+        hipLaunchKernelGGL((sfa_mla_kernel<false>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,
                            (const uint8_t*)a.kv, a.kvscale, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
                            a.n_q, a.max_seq_len, rows, a.indices, a.top_k, per, splits, scale_log2,
                            (uint16_t*)a.out, a.lse, a.ws, ws_lse);

@@ -52,17 +52,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     };
 
     uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)top_k;
+    if constexpr (CACHE) {
+        // stage the row's keys in LDS; the unrolled loop issues its loads back to back
+#pragma unroll 8
+        for (int s = tid; s < L; s += NT) keys[s] = score_key(row[s]);
+    }
     for (int shift = 24; shift >= 0; shift -= 8) {
         for (int t = tid; t < 256; t += NT) hist[t] = 0u;
         __syncthreads();
+#pragma unroll 8
         for (int s = tid; s < L; s += NT) {
-            uint32_t k;
-            if (CACHE && shift == 24) {
-                k = score_key(row[s]);
-                keys[s] = k;
-            } else {
-                k = key_at(s);
-            }
+            const uint32_t k = key_at(s);
             if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
         }
         __syncthreads();
