@@ -62,6 +62,10 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
+# kernels of each stage, by name, as rocprofv3 reports them
+STAGE_KERNELS = {"indexer": ("indexer_",), "topk": ("topk_kernel",), "attention": ("sfa_",)}
+COPY_KERNEL = "neg_kernel"  # the plain copy used to calibrate the byte counters
+
 KERNEL_SOURCES = {
     "indexer": ["sparse_attention_lightningindexer_amd/csrc/indexer.hip",
                 "sparse_attention_lightningindexer_amd/csrc/common.hpp"],
@@ -85,6 +89,52 @@ def measured_traffic(stage: str, workload: str):
     if rec.get("source_hash") != source_hash(KERNEL_SOURCES[stage]):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_means(csv_dir: str, counter: str):
+    """Per-kernel mean of one counter over its dispatches in a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {csv_dir}")
+    per = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for rec in csv.DictReader(fh):
+                if rec["Counter_Name"] != counter:
+                    continue
+                d = per.setdefault(rec["Kernel_Name"], {})
+                d[rec["Dispatch_Id"]] = d.get(rec["Dispatch_Id"], 0.0) + float(rec["Counter_Value"])
+    return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
+
+
+def traffic_summary(stage: str, workload: str, fetch_dir: str, write_dir: str, copy_mib: int, cmd: str):
+    """HBM bytes per launch of a stage from FETCH_SIZE / WRITE_SIZE passes (KiB per
+    dispatch), each scaled by what the same counter reads for a plain copy of
+    copy_mib MiB (read copy_mib, write copy_mib) in the same run."""
+    fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mib * 2 ** 20
+
+    def one(table, what):
+        cal = [v for k, v in table.items() if COPY_KERNEL in k]
+        if not cal:
+            raise SystemExit(f"the calibration copy ({COPY_KERNEL}) is missing from the {what} run")
+        factor = copy_bytes / (cal[0][0] * 1024.0)
+        ks = {k: v for k, v in table.items() if any(t in k for t in STAGE_KERNELS[stage])}
+        if not ks:
+            raise SystemExit(f"no {stage} kernels in the {what} run")
+        raw = sum(v[0] for v in ks.values()) * 1024.0
+        return factor, raw, {k[:120]: {"kib_per_dispatch": v[0], "dispatches": v[1]} for k, v in ks.items()}
+
+    ff, fraw, fk = one(fetch, "FETCH_SIZE")
+    wf, wraw, wk = one(write, "WRITE_SIZE")
+    rec = {"stage": stage, "workload": workload, "source_hash": source_hash(KERNEL_SOURCES[stage]),
+           "hbm_bytes_per_launch": fraw * ff + wraw * wf,
+           "read_bytes_per_launch": fraw * ff, "write_bytes_per_launch": wraw * wf,
+           "fetch_factor": ff, "write_factor": wf, "copy_mib": copy_mib,
+           "fetch_kernels": fk, "write_kernels": wk, "command": cmd}
+    return rec
 
 
 def cpu_baseline(wl, budget_s: float):
@@ -124,7 +174,21 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="after the run, copy MIB MiB three times (byte-counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: summarize two rocprofv3 --pmc csv runs (FETCH_SIZE, WRITE_SIZE) "
+                         "of this script into profiles/traffic_<stage>_<workload>.json.txt")
+    ap.add_argument("--stage", default="attention", choices=list(STAGE_KERNELS))
+    ap.add_argument("--command", default="", help="with --traffic-from: the command the runs came from")
     args = ap.parse_args()
+    if args.traffic_from:
+        rec = traffic_summary(args.stage, args.workload, *args.traffic_from, args.copy_calib, args.command)
+        path = os.path.join(ROOT, "profiles", f"traffic_{args.stage}_{args.workload}.json.txt")
+        with open(path, "w") as fh:
+            fh.write(json.dumps(rec, indent=1) + "\n")
+        print(json.dumps({k: rec[k] for k in ("hbm_bytes_per_launch", "fetch_factor", "write_factor")}))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
               "(the stage shards by sequence with no exchange; see the design notes)", file=sys.stderr)
@@ -214,7 +278,8 @@ def main():
         ach = nbytes / dur_s / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS}
     roof["traffic"] = measured_traffic(dom, args.workload)
-    roof["kernel"] = dom
+    roof["kernel"] = {"indexer": "indexer scoring (indexer_*_kernel)", "topk": "top-k (topk_kernel)",
+                      "attention": "sparse attention (sfa_mla_kernel, plus sfa_combine_kernel when split)"}[dom]
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = nflops
     roof["avg_us"] = stage_us[dom]
@@ -231,6 +296,13 @@ def main():
         "roofline": roof,
         "stages_us": stage_us,
     }
+    if args.copy_calib:
+        src = torch.randn(args.copy_calib * 2 ** 18, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl0, args.cpu_budget)

@@ -101,12 +101,13 @@ def test_workspace_sizes_follow_the_split_rule():
         n = lib.dsa_sparse_attn_workspace_bytes(C.byref(batch), C.byref(attn), 2048)
         splits = n // (4 * rows * 128 * 513)
         assert n == 4 * rows * splits * 128 * 513
-        assert 1 < splits <= 64 and rows * splits >= 256
+        # two head halves per row, then the index list is split until ~256 workgroups
+        assert 1 < splits <= 32 and 2 * rows * splits >= 256
         f = lib.dsa_forward_workspace_bytes(C.byref(batch), C.byref(idx), C.byref(attn), 2048)
         ld = (wl.max_seq_len + 63) // 64 * 64
         assert f >= 4 * rows * ld + 4 * rows * 2048 + n
     # enough rows: no splits, no partials
-    wl = make_workload(2, batch=300, lens=70)
+    wl = make_workload(2, batch=128, lens=70)
     batch, idx, attn = _fake_structs(wl)
     assert lib.dsa_sparse_attn_workspace_bytes(C.byref(batch), C.byref(attn), 2048) == 0
     assert lib.dsa_topk_workspace_bytes(C.byref(batch), 2048) == 0
