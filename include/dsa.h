@@ -122,14 +122,14 @@ typedef struct {
 } dsa_indexer_args;
 
 /* Sparse attention inputs and outputs ([A] §4 "Sparse attention read";
- * [D] §2.2 "reads only the selected KV entries ... chunked, IO-aware").
+ * [D] §2.2: the sparse core reads only the selected cache entries, in chunks).
  * K is the whole latent row [latent | rope]; V is its first d_v channels. */
 typedef struct {
     const void* q;              /* device [rows][n_heads][d_qk] in dtype           */
     dsa_dtype dtype;            /* F32 or BF16; the output has the same dtype      */
     int32_t n_heads;            /* H                                               */
     int32_t d_v;                /* value channels                                  */
-    float sm_scale;             /* logit scale, e.g. 1/sqrt(d_qk)                  */
+    float sm_scale;             /* logit scale, finite and > 0, e.g. 1/sqrt(d_qk)  */
     dsa_cache kv;               /* latent pool, width == d_qk                      */
     void* out;                  /* device [rows][n_heads][d_v] in dtype            */
     float* lse;                 /* device [rows][n_heads] natural-log LSE, or NULL */
@@ -143,7 +143,7 @@ int32_t dsa_version(void);
 
 /*
  * dsa_indexer_scores -- relevance scoring and head-weighted sum
- * ([D] §4.1 "Indexer Fusion", steps batched_dot and weighted_sum;
+ * ([D] §4.1 "Indexer Fusion": per-head scoring, then the weighted sum;
  *  [A] §2 "Sparse Attention (DSA)": the indexer scores historical positions).
  *
  *   scores[r][s] = sum_j head_w[r][j] * max(0, sum_c q[r][j][c] * k[s][c])
@@ -160,7 +160,7 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch, const dsa_indexer_args* id
 size_t dsa_topk_workspace_bytes(const dsa_batch* batch, int32_t top_k);
 
 /*
- * dsa_topk -- Top-K selection per row ([D] §4.1 "topk(scores, top_k)";
+ * dsa_topk -- Top-K selection per row ([D] §4.1, its top-k step;
  * [C] §3: the fused indexer outputs only the final Top-K indices).
  *
  * For each row, the k_r = min(top_k, L_r) positions of scores[r][0:L_r]

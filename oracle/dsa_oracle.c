@@ -28,7 +28,7 @@
  *     weighted aggregation; the ReLU is the stated nonlinearity);
  *  3. Top-K: the k_r = min(top_k, L_r) positions with the largest I, ties to
  *     the lowest position, emitted in ascending order, padded with -1
- *     ([D] §4.1 "topk(scores, top_k)"; only the set matters, [D] §5.1);
+ *     ([D] §4.1, its top-k step; only the set matters, [D] §5.1);
  *  4. sparse attention over the selected positions of the MLA latent cache:
  *     z_s = sm_scale * q[r,h,:].kv[s,:], two-pass softmax, out = sum p_s *
  *     kv[s, :d_v], lse = m + log sum exp(z - m)  ([A] §2, [D] §2.2: the

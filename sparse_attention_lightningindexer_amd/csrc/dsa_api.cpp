@@ -65,6 +65,7 @@ dsa_status check_attn(const dsa_batch* b, const dsa_attn_args* a) {
     if (b->batch > 0 && (a->q == nullptr || a->out == nullptr)) return DSA_ERR_NULL;
     dsa_status s = check_pool(&a->kv, a->kv.width);
     if (s != DSA_OK) return s;
+    if (!(a->sm_scale > 0.f) || a->sm_scale > 3.0e38f) return DSA_ERR_SHAPE;  // finite and positive
     if (a->dtype == DSA_F32) {
         if (a->n_heads < 1 || a->n_heads > 16 || a->kv.width < 1 || a->kv.width > 128) return DSA_ERR_UNSUPPORTED;
         if (a->d_v < 1 || a->d_v > a->kv.width) return DSA_ERR_SHAPE;

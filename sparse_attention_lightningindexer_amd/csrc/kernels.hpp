@@ -50,7 +50,7 @@ struct AttnLaunch {
     const int32_t* indices;
     void* out;
     float* lse;
-    float* ws;                 // split partials, attn_ws_bytes
+    void* ws;                  // split partials, attn_ws_bytes
     int splits;
 };
 

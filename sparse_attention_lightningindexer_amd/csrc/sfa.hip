@@ -9,20 +9,19 @@
 // latent row [latent 512 | rope 64] per position is shared by all 128 heads:
 // K is the whole row, V its first 512 channels.
 //
-// Kernel structure (128 heads, d_qk 576, d_v 512), one workgroup of 8 waves
-// per (row, split of the index list):
+// Kernel structure (128 heads, d_qk 576, d_v 512), one workgroup of 4 waves
+// per (row, half of the heads, split of the index list):
 //   0. the split's index slots are validated (0 <= s < L_r, block present)
 //      and compacted in order into LDS as pool-row numbers;
-//   1. per chunk of 32 positions the latent rows are gathered straight into
-//      LDS (global_load_lds, double-buffered, 16-byte units XOR-swizzled by
-//      row so the MFMA operand reads are bank-conflict free).  An MXFP8 cache
-//      is dequantized (e4m3 * 2^(e8m0-127), exact in bf16) on the way in;
-//   2. wave w owns heads 16w..16w+15: S^T = K . Q^T on MFMA with Q held in
-//      registers for the whole kernel;
+//   1. per chunk of 32 positions the latent rows are gathered through
+//      registers into a 3-tile LDS ring (16-byte units XOR-swizzled by row so
+//      the MFMA operand reads are bank-conflict free).  An MXFP8 cache is
+//      dequantized (e4m3 * 2^(e8m0-127), exact in bf16) on the way in;
+//   2. S^T = K . Q^T on MFMA with Q held in registers for the whole kernel;
 //   3. online softmax in the log2 domain, per head, in registers; the
 //      running maximum is only moved when it grows by more than 2^8, which
 //      changes rounding only (numerator and denominator share it);
-//   4. O^T += V^T . P^T on MFMA: P is already laid out as the B operand, and
+//   4. O^T += V^T . P^T on MFMA: P is laid out in LDS as the B operand, and
 //      V^T comes from LDS with the transposing read ds_read_b64_tr_b16;
 //   5. the row's result (or the split's normalized partial and its LSE) is
 //      written; a combine kernel merges the splits by LSE.
@@ -33,7 +32,6 @@ namespace dsa {
 
 constexpr int kH = 128, kDqk = 576, kDv = 512, kCh = 32;
 constexpr int kRowB = kDqk * 2;        // bytes per bf16 latent row
-constexpr int kUnits = kRowB / 16;     // 16-byte units per row (72)
 constexpr int kTileB = kCh * kRowB;    // 36864 bytes per chunk
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -72,29 +70,34 @@ __device__ __forceinline__ void dequant_unit(i32x4 codes, float scale, i32x4& lo
 //
 // Workgroup: 4 waves, one per SIMD (the whole register file each), 64 heads.
 // Per chunk of 32 positions:
-//   QK   wave w owns heads 32(w&1) .. +31 of the half and positions 16(w>>1)
-//        .. +15 of the chunk: S^T = K . Q^T with Q^T resident in registers,
-//        each K fragment read from LDS feeding two MFMAs; the two waves of a
-//        head pair exchange their partial row maxima through LDS, then each
-//        writes its bf16 probabilities P[head][pos] and keeps a partial
-//        denominator (summed at the end);
+//   QK   wave w owns heads 16w .. 16w+15 of the half over all 32 positions:
+//        S^T = K . Q^T with Q^T resident in registers, so the row maxima and
+//        the softmax of the chunk are local to the wave;
 //   PV   wave w owns value channels 128w .. 128w+127 for the half's 64 heads:
 //        O^T[d][h] += V^T . P^T, each V^T fragment (transposing LDS read)
-//        feeding 4 MFMAs and each P^T fragment 8.
-// LDS (one workgroup per CU): 3 x 36 KiB gather ring (bf16 cache), or 3 x
-// 18.75 KiB fp8 staging + 2 bf16 tiles (MXFP8 cache); + P 5 KiB + slot list 8 KiB.
+//        feeding 4 MFMAs and each P^T fragment 8; P and the rescale factors
+//        pass through LDS.
+// Latent rows are gathered through registers (global loads two chunks ahead,
+// written to LDS one chunk ahead), which keeps more row loads in flight per
+// compute unit than LDS-direct loads do.  One barrier per chunk.
+// LDS (one workgroup per CU): 3 x 36 KiB tiles + P 10 KiB + slot list 8 KiB.
 constexpr int kWaves = 4, kThreads = kWaves * kWave;
 constexpr int kHalf = kH / 2;                   // heads per workgroup
-constexpr int kDvPerWave = kDv / kWaves;        // 128 value channels = 8 D-tiles
-constexpr int kRing = 3;                        // chunks resident in LDS (bf16 cache)
-constexpr int kMxRing = 3;                      // fp8 staging slots (MXFP8 cache)
-constexpr int kMxCodeB = kCh * kDqk;            // fp8 codes of a chunk (18432 B)
-constexpr int kMxScaleW = 24;                   // bytes of an aligned window holding a row's 18 scales
-constexpr int kMxStageB = kMxCodeB + kCh * kMxScaleW;
-constexpr int kGatherK = kTileB / (16 * kWave);          // 36 wave-instructions per bf16 chunk
-constexpr int kMxCodeK = kMxCodeB / (16 * kWave);        // 18 per fp8 chunk
-constexpr int kMxScaleK = kCh * kMxScaleW / (4 * kWave); // 3 (dword lanes), waves 1..3
+constexpr int kHeadsPerWave = kHalf / kWaves;   // 16: QK and softmax role
+constexpr int kDvPerWave = kDv / kWaves;        // 128 value channels = 8 D-tiles: PV role
+constexpr int kRing = 3;                        // bf16 tiles resident in LDS
 constexpr int kPRow = kCh * 2 + 16;             // bytes per head row of P (64 + 16 pad)
+constexpr int kRowsPerWave = kCh / kWaves;      // 8 chunk rows staged by each wave
+constexpr int kMxUnitsRow = kDqk / 16;          // 36 16-code units per MXFP8 row
+constexpr int kMxPer = (kRowsPerWave * kMxUnitsRow + kWave - 1) / kWave;  // 5 (the last partial)
+
+// two floats -> two bfloat16 (round to nearest even) packed in 32 bits
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = __builtin_convertvector((f2){a, b}, h2);
+    return __builtin_bit_cast(uint32_t, h);
+}
 
 template <bool MX>
 __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
@@ -102,15 +105,13 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
     int64_t num_blocks, int n_q, int max_seq_len, int rows, const int32_t* __restrict__ indices,
     int top_k, int per_split, int splits, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[MX ? 2 : kRing][kTileB];
-    __shared__ __attribute__((aligned(16))) uint8_t stage[MX ? kMxRing : 1][MX ? kMxStageB : 16];
+    float* __restrict__ lse, uint16_t* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kRing][kTileB];
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][kHalf * kPRow];  // P[head][pos] bf16, by chunk parity
     __shared__ float alpha_s[2][kHalf];  // rescale factor per head, by chunk parity
-    __shared__ float pmax_s[2][kHalf]; // chunk maximum per head over each position half
-    __shared__ float lpart_s[2][kHalf]; // final partial denominators per position half
-    __shared__ int rescale_chunk[2];  // the chunk (by parity) whose factors are not all 1
-    __shared__ int32_t prow[kAttnMaxSplitSlots];
+    __shared__ float l_s[kHalf], m_s[kHalf];
+    __shared__ int rescale_chunk[2];     // the chunk (by parity) whose factors are not all 1
+    __shared__ __attribute__((aligned(16))) int32_t prow[kAttnMaxSplitSlots];
     __shared__ int wave_cnt[kWaves];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -131,30 +132,43 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     const int slot0 = split * per_split;
     const int slot1 = min(top_k, slot0 + per_split);
 
-    // QK role of this wave: head pair hq (32 heads) x position half ph.  Q^T
-    // fragments: qf[ht][ks] holds q[hb + 32hq + 16ht + j][32ks + 8g .. +8].
-    // Loaded first so that they retire, with the index loads below, before the
-    // gather ring starts (a wait for them inside the loop would drain it).
-    const int hq = wave & 1, ph = wave >> 1;
-    const int hl0 = 32 * hq;             // first head of the pair, within the half
-    bf16x8 qf[2][kDqk / 32];
+    // QK role: heads hl0 .. hl0+15 of the half.  qf[ks] holds
+    // q[hb + hl0 + j][32ks + 8g .. +8] (the B operand of S^T = K . Q^T).
+    const int hl0 = kHeadsPerWave * wave;
+    bf16x8 qf[kDqk / 32];
+    auto load_q = [&]() __attribute__((always_inline)) {
+        const uint16_t* qrow = q + ((int64_t)row * kH + hb + hl0 + j) * kDqk + 8 * g;
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-        const uint16_t* qrow = q + ((int64_t)row * kH + hb + hl0 + 16 * ht + j) * kDqk + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < kDqk / 32; ++ks) qf[ht][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-    }
+        for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    };
 
-    // 0. ordered compaction of the valid index slots into pool-row numbers
-    int n_valid = 0;
-    for (int base = slot0; base < slot1; base += kThreads) {
-        const int t = base + tid;
-        const int s = t < slot1 ? indices[(int64_t)row * top_k + t] : -1;
-        int pr = -1;
-        if (s >= 0 && s < L) {
-            const int64_t p = phys_block(table, max_blocks, b, s / kBlock, num_blocks);
-            if (p >= 0) pr = (int)(p * kBlock + (s % kBlock));
+    // 0. ordered compaction of the valid index slots into pool-row numbers.
+    //    All of the split's indices are loaded first, then all of their table
+    //    entries (two memory round trips in total), then compacted.
+    constexpr int kSlotIters = kAttnMaxSplitSlots / kThreads;
+    int pr_[kSlotIters];
+    {
+        int sv[kSlotIters];
+#pragma unroll
+        for (int k = 0; k < kSlotIters; ++k) {
+            const int t = slot0 + kThreads * k + tid;
+            sv[k] = t < slot1 ? indices[(int64_t)row * top_k + t] : -1;
         }
+#pragma unroll
+        for (int k = 0; k < kSlotIters; ++k) {
+            const int sk = sv[k];
+            pr_[k] = -1;
+            if (sk >= 0 && sk < L) {
+                const int64_t p = phys_block(table, max_blocks, b, sk / kBlock, num_blocks);
+                if (p >= 0) pr_[k] = (int)(p * kBlock + (sk % kBlock));
+            }
+        }
+    }
+    int n_valid = 0;
+#pragma unroll
+    for (int k = 0; k < kSlotIters; ++k) {
+        if (slot0 + kThreads * k >= slot1) break;  // workgroup-uniform
+        const int pr = pr_[k];
         const uint64_t m = ballot(pr >= 0);
         if (lane == 0) wave_cnt[wave] = __popcll(m);
         __syncthreads();
@@ -168,8 +182,10 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         __syncthreads();
     }
     const int nchunks = (n_valid + kCh - 1) / kCh;
-    if (tid < 2) rescale_chunk[tid] = -1;  // visible after the first barrier of the ring
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): q and index loads retired (known to the compiler)
+    // pad the last chunk with a valid row, so every chunk row names real data
+    if (tid < nchunks * kCh - n_valid) prow[n_valid + tid] = prow[0];
+    if (tid < 2) rescale_chunk[tid] = -1;
+    __syncthreads();
 
     // O^T accumulators: o[dt][ht] holds O^T[128w + 16dt + 4g + i][head hb + 16ht + j]
     f32x4 o[kDvPerWave / 16][kHalf / 16];
@@ -177,161 +193,153 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     for (int dt = 0; dt < kDvPerWave / 16; ++dt)
 #pragma unroll
         for (int ht = 0; ht < kHalf / 16; ++ht) o[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // softmax state of heads hl0 + 16ht + j (the same m in both waves of the
-    // pair; l over this wave's position half only)
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    // softmax state of head hl0 + j (identical in the four lane groups)
+    float m_run = -INFINITY, l_run = 0.f;
 
-    auto chunk_row = [&](int c, int r_) -> int {  // pool row of chunk row r_ (tail rows repeat a valid one)
-        const int t = c * kCh + r_;
-        return prow[t < n_valid ? t : c * kCh];
-    };
-    // Gathers issued per chunk by this wave (wave-instructions k = wave + 4i).
-    constexpr int kBfPer = kGatherK / kWaves;                                                       // 9
-    const int nk_mx = (kMxCodeK - wave + kWaves - 1) / kWaves + (wave >= kWaves - kMxScaleK ? 1 : 0); // 5 or 6
-    const int per_chunk = MX ? nk_mx : kBfPer;
 
-    // 1. bf16 cache: the chunk's 32 latent rows straight into a ring tile.
-    //    Unit U (row U/72, column U%72) of the tile holds global column
-    //    (U%72) ^ (row & 7): the XOR swizzle keeps the operand reads conflict free.
-    auto issue_bf16 = [&](int c, int buf) {
-        int pr[kBfPer];
-#pragma unroll
-        for (int i = 0; i < kBfPer; ++i) pr[i] = chunk_row(c, ((wave + kWaves * i) * kWave + lane) / kUnits);
-        const uint32_t base = lds_addr(&tile[buf][0]);
-#pragma unroll
-        for (int i = 0; i < kBfPer; ++i) {
-            const int k = wave + kWaves * i;
-            const int U = k * kWave + lane;
-            const int r_ = U / kUnits, col = (U % kUnits) ^ (r_ & 7);
-            lds_gather16(kv + (int64_t)pr[i] * kRowB + col * 16, base + k * kWave * 16);
-        }
+    // 1. Staging.  bf16: wave w loads chunk rows 8w .. 8w+7 whole -- 64 lanes
+    //    x 16 bytes cover a row's 512 latent channels, from a row base held in
+    //    scalar registers -- and thread t loads rope unit 64 + t%8 of row t/8.
+    //    MXFP8: unit U = 64i + lane of the wave's 8 rows x 36 units (row U/36,
+    //    16 codes U%36) with its E8M0 scale byte, dequantized (exact) to two
+    //    bf16 units when stored.  Rows are stored at their XOR-swizzled places.
+    const int prow0 = kRowsPerWave * wave;
+    struct Stage {
+        i32x4 v[kRowsPerWave + 1];
+        uint32_t sc[MX ? kMxPer : 1];
     };
-    // 1'. MXFP8 cache: codes [32][576] and, per row, the 4-byte-aligned 24-byte
-    //     window of the scale pool that holds its 18 E8M0 scales.
-    const int64_t scale_bytes = num_blocks * kBlock * (kDqk / 32);
-    auto scale_window = [&](int pr) -> int64_t {
-        const int64_t w = ((int64_t)pr * (kDqk / 32)) & ~(int64_t)3;
-        return w + kMxScaleW <= scale_bytes ? w : scale_bytes - kMxScaleW;
-    };
-    auto issue_mx = [&](int c, int sb) {
-        const uint32_t base = lds_addr(&stage[sb][0]);
-        int pr[5];
+    Stage stA, stB;  // chunk k is staged in stA (k even) or stB (k odd)
+    auto load_chunk = [&](int c, Stage& st) __attribute__((always_inline)) {
+        const int32_t* pc = prow + c * kCh;
+        if constexpr (!MX) {
+            const int4 a0 = *reinterpret_cast<const int4*>(pc + prow0);
+            const int4 a1 = *reinterpret_cast<const int4*>(pc + prow0 + 4);
+            const int pr[kRowsPerWave] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const int k = wave + kWaves * i;
-            if (k < kMxCodeK) pr[i] = chunk_row(c, (k * kWave + lane) / (kDqk / 16));
-        }
-        const int sk = wave - (kWaves - kMxScaleK);
-        int spr = 0;
-        if (sk >= 0) spr = chunk_row(c, (sk * kWave + lane) / (kMxScaleW / 4));
+            for (int i = 0; i < kRowsPerWave; ++i) {
+                const uint8_t* rowp = kv + (int64_t)__builtin_amdgcn_readfirstlane(pr[i]) * kRowB;
+                st.v[i] = *reinterpret_cast<const i32x4*>(rowp + lane * 16);
+            }
+            const int rt = tid >> 3;
+            st.v[kRowsPerWave] = *reinterpret_cast<const i32x4*>(kv + (int64_t)pc[rt] * kRowB + 16 * (64 + (tid & 7)));
+        } else {
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const int k = wave + kWaves * i;
-            if (k < kMxCodeK) {
-                const int cu = (k * kWave + lane) % (kDqk / 16);
-                lds_gather16(kv + (int64_t)pr[i] * kDqk + cu * 16, base + k * kWave * 16);
+            for (int i = 0; i < kMxPer; ++i) {
+                const int U = opaque(kWave * i + lane);
+                if (i < kMxPer - 1 || U < kRowsPerWave * kMxUnitsRow) {
+                    const int r_ = U / kMxUnitsRow, u = U - r_ * kMxUnitsRow;
+                    const int64_t pr = pc[prow0 + r_];
+                    st.v[i] = *reinterpret_cast<const i32x4*>(kv + pr * kDqk + u * 16);
+                    st.sc[i] = kvscale[pr * (kDqk / 32) + (u >> 1)];
+                }
             }
         }
-        if (sk >= 0) {
-            const int dw = (sk * kWave + lane) % (kMxScaleW / 4);
-            lds_gather4(kvscale + scale_window(spr) + 4 * dw, base + kMxCodeB + sk * kWave * 4);
-        }
     };
-    // staged fp8 chunk -> dequantized bf16 tile (all threads)
-    auto convert_mx = [&](int c, int sb, int tb) {
-#pragma unroll 1
-        for (int u = 0; u < (kMxCodeB / 16 + kThreads - 1) / kThreads; ++u) {
-            const int U = tid + kThreads * u;
-            if (U < kMxCodeB / 16) {
-                const int r_ = U / (kDqk / 16), cu = U % (kDqk / 16);
-                const int pr = chunk_row(c, r_);
-                const int off = (int)((int64_t)pr * (kDqk / 32) - scale_window(pr));
-                const float sc = e8m0_to_f32(stage[sb][kMxCodeB + r_ * kMxScaleW + off + cu / 2]);
-                i32x4 lo, hi;
-                dequant_unit(*reinterpret_cast<const i32x4*>(&stage[sb][U * 16]), sc, lo, hi);
-                *reinterpret_cast<i32x4*>(&tile[tb][lds_unit(r_, 2 * cu)]) = lo;
-                *reinterpret_cast<i32x4*>(&tile[tb][lds_unit(r_, 2 * cu + 1)]) = hi;
+    auto store_chunk = [&](int slot, const Stage& st) __attribute__((always_inline)) {
+        uint8_t* T = tile[slot];
+        if constexpr (!MX) {
+            uint8_t* Tw = T + prow0 * kRowB;  // row 8w + i has (row & 7) == i
+#pragma unroll
+            for (int i = 0; i < kRowsPerWave; ++i)
+                *reinterpret_cast<i32x4*>(Tw + i * kRowB + ((lane ^ i) << 4)) = st.v[i];
+            const int rt = tid >> 3, ut = 64 + (tid & 7);
+            *reinterpret_cast<i32x4*>(T + lds_unit(rt, ut)) = st.v[kRowsPerWave];
+        } else {
+#pragma unroll
+            for (int i = 0; i < kMxPer; ++i) {
+                const int U = opaque(kWave * i + lane);
+                if (i < kMxPer - 1 || U < kRowsPerWave * kMxUnitsRow) {
+                    const int r_ = prow0 + U / kMxUnitsRow, u = U % kMxUnitsRow;
+                    i32x4 lo, hi;
+                    dequant_unit(st.v[i], e8m0_to_f32(st.sc[i]), lo, hi);
+                    *reinterpret_cast<i32x4*>(T + lds_unit(r_, 2 * u)) = lo;
+                    *reinterpret_cast<i32x4*>(T + lds_unit(r_, 2 * u + 1)) = hi;
+                }
             }
         }
     };
 
-    // 2. QK of this wave's 32 heads x 16 positions, then the softmax of the
-    //    chunk with the partner wave (same heads, other position half).
-    //    Lane holds S[head hl0 + 16ht + j][pos 16ph + 4g + i] in s[ht][i].
-    auto qk = [&](const uint8_t* T) -> auto {
-        // The 18 K fragments of the wave's 16 rows are read in two batches of 9,
-        // each batch issued ahead of its MFMAs so that LDS latencies overlap.
-        // Unit 4ks + g of row r sits at ((4(ks&1) + g) ^ (r&7)) + 8(ks>>1).
-        constexpr int KB = kDqk / 64;  // 9
-        const int r_ = 16 * ph + j;
-        const uint8_t* base0 = T + r_ * kRowB + ((g ^ (r_ & 7)) << 4);
-        const uint8_t* base1 = T + r_ * kRowB + (((4 + g) ^ (r_ & 7)) << 4);
-        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int bh = 0; bh < 2; ++bh) {
-            bf16x8 ka[KB];
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk) {
-                const int ks = bh * KB + kk;
-                ka[kk] = *reinterpret_cast<const bf16x8*>(((ks & 1) ? base1 : base0) + 128 * (ks >> 1));
-            }
-            issue_fence();
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht) s[ht] = mfma_bf16(ka[kk], qf[ht][bh * KB + kk], s[ht]);
-        }
+    // 2. QK of this wave's 16 heads over the chunk's 32 positions: lane holds
+    //    S[head hl0 + j][pos 16pt + 4g + i] in s[pt][i].  K fragment (pt, ks):
+    //    row 16pt + j, unit 4ks + g; the two position tiles alternate (two
+    //    independent accumulation chains).  Reads run one batch of 6 ahead of
+    //    the MFMAs that consume them.
+    auto qk = [&](const uint8_t* T) __attribute__((always_inline)) -> auto  {
         struct S2 { f32x4 v[2]; };
-        return S2{{s[0], s[1]}};
-    };
-    auto softmax = [&](const f32x4 (&s)[2], int c) {
-        float t[2][4];
+        S2 s{{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
+        constexpr int NB = 6, NBATCH = 2 * (kDqk / 32) / NB;  // 6 batches of 6 fragments
+        bf16x8 ka[2][NB];
+        // unit 4ks + g of row r sits at 16 * ((4(ks&1) + g) ^ (r&7)) + 128 (ks>>1);
+        // rows j and 16 + j share r&7, so two base addresses and immediate
+        // offsets cover all 36 fragments.
+        const uint8_t* base0 = T + j * kRowB + ((g ^ (j & 7)) << 4);
+        const uint8_t* base1 = T + j * kRowB + (((4 + g) ^ (j & 7)) << 4);
+        auto read_batch = [&](int bt, bf16x8 (&dst)[NB]) {
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
-            float cmax = -INFINITY;
+            for (int kk = 0; kk < NB; ++kk) {
+                const int f = bt * NB + kk, pt = f & 1, ks = f >> 1;
+                dst[kk] = *reinterpret_cast<const bf16x8*>(((ks & 1) ? base1 : base0) + 16 * pt * kRowB +
+                                                           128 * (ks >> 1));
+            }
+        };
+        read_batch(0, ka[0]);
+#pragma unroll
+        for (int bt = 0; bt < NBATCH; ++bt) {
+            issue_fence();
+            if (bt + 1 < NBATCH) read_batch(bt + 1, ka[(bt + 1) & 1]);
+#pragma unroll
+            for (int kk = 0; kk < NB; ++kk) {
+                const int f = bt * NB + kk, pt = f & 1, ks = f >> 1;
+                s.v[pt] = mfma_bf16(ka[bt & 1][kk], qf[ks], s.v[pt]);
+            }
+        }
+        issue_fence();
+        return s;
+    };
+    // softmax of the chunk for head hl0 + j, local to the wave.  Positions
+    // past the valid ones are -inf; exp2 of -inf is 0.
+    auto softmax = [&](const f32x4 (&s)[2], int c) {
+        const int lim = n_valid - c * kCh - 4 * g;  // position 16pt + 4g + i is valid iff 16pt + i < lim
+        float sm[2][4];
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok = c * kCh + 16 * ph + 4 * g + i < n_valid;
-                t[ht][i] = ok ? s[ht][i] * scale_log2 : -INFINITY;
-                cmax = fmaxf(cmax, t[ht][i]);
+                sm[pt][i] = 16 * pt + i < lim ? s[pt][i] : -INFINITY;
+                cmax = fmaxf(cmax, sm[pt][i]);
             }
-            cmax = max_over_groups(cmax);
-            if (g == 0) pmax_s[ph][hl0 + 16 * ht + j] = cmax;
+        cmax = max_over_groups(cmax) * scale_log2;  // scale_log2 > 0
+        float alpha = 1.f;
+        if (cmax > m_run + kRescale) {  // also the first finite maximum (m_run = -inf)
+            alpha = __builtin_amdgcn_exp2f(m_run - cmax);  // 0 when m_run = -inf
+            m_run = cmax;
         }
-        sync_lds();  // partial maxima of both position halves are in LDS
-        bool rescale = false;
+        const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+        float psum = 0.f;
+        const int hl = hl0 + j;
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
-            const int hl = hl0 + 16 * ht + j;
-            const float cmax = fmaxf(pmax_s[0][hl], pmax_s[1][hl]);
-            float alpha = 1.f;
-            if (cmax > m_run[ht] + kRescale || (m_run[ht] == -INFINITY && cmax > -INFINITY)) {
-                alpha = m_run[ht] == -INFINITY ? 0.f : exp2f(m_run[ht] - cmax);
-                m_run[ht] = cmax;
-            }
-            rescale |= alpha != 1.f;
-            float psum = 0.f;
-            uint32_t w2[2];
+        for (int pt = 0; pt < 2; ++pt) {
+            float p[4];
 #pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-                const float p0 = t[ht][i] == -INFINITY ? 0.f : exp2f(t[ht][i] - m_run[ht]);
-                const float p1 = t[ht][i + 1] == -INFINITY ? 0.f : exp2f(t[ht][i + 1] - m_run[ht]);
-                w2[i / 2] = f32_to_bf16_bits(p0) | ((uint32_t)f32_to_bf16_bits(p1) << 16);  // P operand
-                psum += p0 + p1;                                                          // fp32 denominator
+            for (int i = 0; i < 4; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(fmaf(sm[pt][i], scale_log2, mneg));
+                psum += p[i];  // fp32 denominator
             }
-            *reinterpret_cast<uint2*>(pbuf[c & 1] + hl * kPRow + 2 * (16 * ph + 4 * g)) = make_uint2(w2[0], w2[1]);
-            l_run[ht] = l_run[ht] * alpha + sum_over_groups(psum);
-            if (ph == 0 && g == 0) alpha_s[c & 1][hl] = alpha;
+            *reinterpret_cast<uint2*>(pbuf[c & 1] + hl * kPRow + 2 * (16 * pt + 4 * g)) =
+                make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
         }
-        if (ph == 0 && ballot(rescale) != 0ull && lane == 0) rescale_chunk[c & 1] = c;  // every writer stores c
+        l_run = l_run * alpha + sum_over_groups(psum);
+        if (g == 0) alpha_s[c & 1][hl] = alpha;
+        if (ballot(alpha != 1.f) != 0ull && lane == 0) rescale_chunk[c & 1] = c;  // every writer stores c
     };
 
     // 3. PV on this wave's 128 value channels for the half's 64 heads.  V^T
     //    fragment: lane j of group g addresses row 8g + 4h + j/4, channels
     //    d0 + 4(j%4) (two transposing reads give positions 8g .. 8g+7 in
     //    order); P^T fragment: lane reads P[head 16ht + j][pos 8g .. 8g+7].
-    auto pv = [&](const uint8_t* T, int c) {
-        if (rescale_chunk[c & 1] == c) {  // workgroup-uniform
+    auto pv = [&](const uint8_t* T, int c, bool rescale) __attribute__((always_inline)) {
+        if (rescale) {  // workgroup-uniform
 #pragma unroll
             for (int ht = 0; ht < kHalf / 16; ++ht) {
                 const float al = alpha_s[c & 1][16 * ht + j];
@@ -345,88 +353,96 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
 #pragma unroll
         for (int ht = 0; ht < kHalf / 16; ++ht)
             pf[ht] = *reinterpret_cast<const bf16x8*>(pbuf[c & 1] + (16 * ht + j) * kPRow + 16 * g);
+        // channel 128w + 16dt + 4(j%4) is unit 16w + 2dt + (j%4)/2, byte 8((j%4)&1):
+        // d-tiles dt and dt + 4 differ by one 128-byte step, so four bases per
+        // row (dt = 0..3) and an immediate offset cover the eight d-tiles.
         const int e_ = j >> 2, q4 = j & 3;
         const int r0 = 8 * g + e_, r1 = 8 * g + 4 + e_;
-#pragma unroll
-        for (int bh = 0; bh < 2; ++bh) {
-            bf16x8 vf[kDvPerWave / 32];
+        auto vaddr = [&](int r_, int dt) __attribute__((always_inline)) -> const uint8_t*  {
+            const int unit = 16 * wave + 2 * dt + (q4 >> 1);
+            return T + r_ * kRowB + ((unit ^ (r_ & 7)) << 4) + 8 * (q4 & 1);
+        };
+        auto read_v = [&](int bh, bf16x8 (&vf)[kDvPerWave / 32]) {
 #pragma unroll
             for (int dd = 0; dd < kDvPerWave / 32; ++dd) {
-                const int dt = bh * (kDvPerWave / 32) + dd;
-                const int ch = wave * kDvPerWave + 16 * dt + 4 * q4;   // channel this lane addresses
-                const int unit = ch >> 3, byte = (ch & 7) * 2;
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (DSA_LDS v4i16*)(T + r0 * kRowB + ((unit ^ (r0 & 7)) << 4) + byte));
-                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (DSA_LDS v4i16*)(T + r1 * kRowB + ((unit ^ (r1 & 7)) << 4) + byte));
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS v4i16*)(vaddr(r0, dd) + 128 * bh));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS v4i16*)(vaddr(r1, dd) + 128 * bh));
                 const v4i16 both[2] = {lo, hi};
                 vf[dd] = *reinterpret_cast<const bf16x8*>(both);
             }
-            issue_fence();
+        };
+        bf16x8 vf[2][kDvPerWave / 32];
+        read_v(0, vf[0]);
+        issue_fence();
+        read_v(1, vf[1]);
+#pragma unroll
+        for (int bh = 0; bh < 2; ++bh) {
 #pragma unroll
             for (int dd = 0; dd < kDvPerWave / 32; ++dd)
 #pragma unroll
                 for (int ht = 0; ht < kHalf / 16; ++ht)
-                    o[bh * (kDvPerWave / 32) + dd][ht] = mfma_bf16(vf[dd], pf[ht], o[bh * (kDvPerWave / 32) + dd][ht]);
+                    o[bh * (kDvPerWave / 32) + dd][ht] =
+                        mfma_bf16(vf[bh][dd], pf[ht], o[bh * (kDvPerWave / 32) + dd][ht]);
+            issue_fence();
         }
     };
 
-    // The gather ring: chunk c lives in ring slot c % R; at the top of
-    // iteration c this wave has issued the chunks up to c + R - 2 (bf16) or
-    // c + R - 1 (MXFP8, where the extra slot is the bf16 tile being filled).
-    if constexpr (!MX) {
-        // Software pipeline: iteration c runs QK(c), then PV(c-1), then the
-        // softmax of chunk c, so that the softmax's dependent VALU chain runs
-        // while the matrix core executes PV(c-1).  Slots: c-1 (PV), c (QK),
-        // c+1 (in flight).
-        if (nchunks > 0) issue_bf16(0, 0);
-        for (int c = 0; c < nchunks; ++c) {
-            wait_vmcnt(0);  // chunk c has landed
-            sync_lds();     // ... for every wave; softmax(c-1) wrote P and alpha; slot (c+1) % R is free
-            if (c + 1 < nchunks) issue_bf16(c + 1, (c + 1) % kRing);
-            const auto sc = qk(tile[c % kRing]);
-            if (c > 0) pv(tile[(c - 1) % kRing], c - 1);
-            softmax(sc.v, c);
+    // The loop: chunk c lives in tile c % 3 and is staged in registers two
+    // chunks ahead (stA / stB by parity).  At the top of iteration c (after its
+    // barrier) chunk c is in LDS, P and alpha of chunk c-1 are written, and
+    // tile (c+1) % 3 -- last read by PV(c-2) -- is free: the staged chunk c+1
+    // is stored into it and chunk c+3 is loaded into the registers it held.
+    // QK(c) runs, then PV(c-1) (the matrix core busy while the softmax of
+    // chunk c follows), then softmax(c).
+    auto step = [&](int c, Stage& st_next) __attribute__((always_inline)) {
+        sync_lds();
+        // O is still zero after chunk 0, so its factors need not be applied
+        const bool resc = c > 1 && rescale_chunk[(c - 1) & 1] == c - 1;
+        if (c + 1 < nchunks) {
+            store_chunk((c + 1) % kRing, st_next);
+            if (c + 3 < nchunks) load_chunk(c + 3, st_next);
         }
-        if (nchunks > 0) {
-            sync_lds();
-            pv(tile[(nchunks - 1) % kRing], nchunks - 1);
+        const auto sc = qk(tile[c % kRing]);
+        pv(tile[(c - 1) % kRing], c - 1, resc);
+        softmax(sc.v, c);
+    };
+    if (nchunks > 0) {
+        load_chunk(0, stA);
+        if (nchunks > 1) load_chunk(1, stB);
+        load_q();  // in flight with the first gathers
+        store_chunk(0, stA);
+        if (nchunks > 2) load_chunk(2, stA);
+        sync_lds();
+        if (nchunks > 1) {
+            store_chunk(1, stB);
+            if (nchunks > 3) load_chunk(3, stB);
         }
-    } else {
-        for (int c = 0; c < kMxRing && c < nchunks; ++c) issue_mx(c, c);
-        if (nchunks > 0) {
-            wait_vmcnt(per_chunk * min(kMxRing - 1, nchunks - 1));
-            sync_lds();
-            convert_mx(0, 0, 0);
+        {
+            const auto sc = qk(tile[0]);
+            softmax(sc.v, 0);
         }
-        for (int c = 0; c < nchunks; ++c) {
-            const uint8_t* T = tile[c & 1];
-            if (c + 1 < nchunks) wait_vmcnt(per_chunk * min(kMxRing - 2, nchunks - 2 - c));  // chunk c+1 staged
-            sync_lds();  // tile c%2 converted; tile (c+1)%2, stage c%R and P are free
-            if (c + kMxRing < nchunks) issue_mx(c + kMxRing, c % kMxRing);
-            if (c + 1 < nchunks) convert_mx(c + 1, (c + 1) % kMxRing, (c + 1) & 1);
-            const auto sc = qk(T);
-            softmax(sc.v, c);
-            sync_lds();
-            pv(T, c);
+        int c = 1;
+        for (; c + 1 < nchunks; c += 2) {
+            step(c, stA);      // stores chunk c+1 (even), loads c+3 (even)
+            step(c + 1, stB);  // stores chunk c+2 (odd), loads c+4 (odd)
         }
+        if (c < nchunks) step(c, stA);
+        sync_lds();
+        c = nchunks - 1;
+        pv(tile[c % kRing], c, c > 0 && rescale_chunk[c & 1] == c);
     }
 
-    // 4. results.  The denominators of the two position halves are summed.
+    // 4. results
     if (g == 0) {
-        lpart_s[ph][hl0 + j] = l_run[0];
-        lpart_s[ph][hl0 + 16 + j] = l_run[1];
-        if (ph == 0) {
-            pmax_s[0][hl0 + j] = m_run[0];
-            pmax_s[0][hl0 + 16 + j] = m_run[1];
-        }
+        l_s[hl0 + j] = l_run;
+        m_s[hl0 + j] = m_run;
     }
     __syncthreads();
     const int64_t part = (int64_t)row * splits + split;
 #pragma unroll
     for (int ht = 0; ht < kHalf / 16; ++ht) {
         const int h = hb + 16 * ht + j;
-        const float lsum = lpart_s[0][16 * ht + j] + lpart_s[1][16 * ht + j];
+        const float lsum = l_s[16 * ht + j];
         const float inv_l = lsum > 0.f ? 1.f / lsum : 0.f;
         const int d0 = wave * kDvPerWave + 4 * g;
         if (splits == 1) {
@@ -434,22 +450,22 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
 #pragma unroll
             for (int dt = 0; dt < kDvPerWave / 16; ++dt) {
                 const f32x4 v = o[dt][ht];
-                const uint32_t lo = f32_to_bf16_bits(v[0] * inv_l) | ((uint32_t)f32_to_bf16_bits(v[1] * inv_l) << 16);
-                const uint32_t hi = f32_to_bf16_bits(v[2] * inv_l) | ((uint32_t)f32_to_bf16_bits(v[3] * inv_l) << 16);
-                *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(lo, hi);
+                *reinterpret_cast<uint2*>(orow + 16 * dt) =
+                    make_uint2(pack_bf16x2(v[0] * inv_l, v[1] * inv_l), pack_bf16x2(v[2] * inv_l, v[3] * inv_l));
             }
-        } else {
-            float* orow = ws_o + (part * kH + h) * kDv + d0;
+        } else {  // the split's normalized partial, in bf16 like the output
+            uint16_t* orow = ws_o + (part * kH + h) * kDv + d0;
 #pragma unroll
             for (int dt = 0; dt < kDvPerWave / 16; ++dt) {
                 const f32x4 v = o[dt][ht];
-                *reinterpret_cast<f32x4*>(orow + 16 * dt) = f32x4{v[0] * inv_l, v[1] * inv_l, v[2] * inv_l, v[3] * inv_l};
+                *reinterpret_cast<uint2*>(orow + 16 * dt) =
+                    make_uint2(pack_bf16x2(v[0] * inv_l, v[1] * inv_l), pack_bf16x2(v[2] * inv_l, v[3] * inv_l));
             }
         }
     }
     if (tid < kHalf) {
-        const float lsum = lpart_s[0][tid] + lpart_s[1][tid];
-        const float hl_lse = lsum > 0.f ? (pmax_s[0][tid] + log2f(lsum)) * kLn2 : -INFINITY;
+        const float lsum = l_s[tid];
+        const float hl_lse = lsum > 0.f ? (m_s[tid] + __log2f(lsum)) * kLn2 : -INFINITY;
         if (splits == 1) {
             if (lse != nullptr) lse[(int64_t)row * kH + hb + tid] = hl_lse;
         } else {
@@ -459,12 +475,12 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
 }
 
 // Merge split partials: out = sum_s exp(lse_s - LSE) * O_s, LSE = log sum_s exp(lse_s).
-// grid (rows, H/4), block 256: wave w -> head 4*blockIdx.y + w, lane -> 8 channels,
-// so every load instruction of a wave reads 2 KB of contiguous partials.
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void sfa_combine_kernel(const float* __restrict__ ws_o,
+// The partials O_s are bf16.  grid (rows, H/4), block 256: wave w -> head
+// 4*blockIdx.y + w, lane -> 8 channels, so every load instruction of a wave
+// reads 1 KB of contiguous partials.
+__global__ __launch_bounds__(256) void sfa_combine_kernel(const uint16_t* __restrict__ ws_o,
                                                           const float* __restrict__ ws_lse, int splits,
-                                                          int H, int Dv, void* __restrict__ out,
+                                                          int H, int Dv, uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
     const int row = blockIdx.x;
     const int h = 4 * blockIdx.y + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -478,32 +494,24 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const float* __restric
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
     for (int d = 8 * lane; d < Dv; d += 8 * 64) {
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < splits; ++s) {
             const float ls = ws_lse[((int64_t)row * splits + s) * H + h];
             if (M == -INFINITY || ls == -INFINITY) continue;
             const float wgt = expf(ls - M);
-            const float* src = ws_o + (((int64_t)row * splits + s) * H + h) * Dv + d;
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
-            const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+            const uint4 v = *reinterpret_cast<const uint4*>(ws_o + (((int64_t)row * splits + s) * H + h) * Dv + d);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
-                a0[i] = fmaf(wgt, v0[i], a0[i]);
-                a1[i] = fmaf(wgt, v1[i], a1[i]);
+                acc[2 * i] = fmaf(wgt, __uint_as_float(w4[i] << 16), acc[2 * i]);
+                acc[2 * i + 1] = fmaf(wgt, __uint_as_float(w4[i] & 0xffff0000u), acc[2 * i + 1]);
             }
         }
-        if constexpr (OUT_BF16) {
-            uint16_t* o = (uint16_t*)out + ((int64_t)row * H + h) * Dv + d;
-            uint32_t w4[4];
-            for (int i = 0; i < 2; ++i) {
-                w4[i] = f32_to_bf16_bits(a0[2 * i] * inv) | ((uint32_t)f32_to_bf16_bits(a0[2 * i + 1] * inv) << 16);
-                w4[2 + i] = f32_to_bf16_bits(a1[2 * i] * inv) | ((uint32_t)f32_to_bf16_bits(a1[2 * i + 1] * inv) << 16);
-            }
-            *reinterpret_cast<uint4*>(o) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-        } else {
-            float* o = (float*)out + ((int64_t)row * H + h) * Dv + d;
-            *reinterpret_cast<f32x4*>(o) = f32x4{a0[0] * inv, a0[1] * inv, a0[2] * inv, a0[3] * inv};
-            *reinterpret_cast<f32x4*>(o + 4) = f32x4{a1[0] * inv, a1[1] * inv, a1[2] * inv, a1[3] * inv};
-        }
+        uint16_t* o = out + ((int64_t)row * H + h) * Dv + d;
+        uint32_t w4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w4[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+        *reinterpret_cast<uint4*>(o) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
     if (lse != nullptr && lane == 0) lse[(int64_t)row * H + h] = W > 0.f ? M + logf(W) : -INFINITY;
 }
@@ -596,28 +604,30 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st) {
     const int per = splits == 1 ? a.top_k : attn_per_split(a.top_k, splits);
     const int grid = ((rows + 7) / 8) * 8 * 2 * splits;   // (row, head half, split)
     const float scale_log2 = a.sm_scale * kLog2e;
-    float* ws_lse = splits == 1 ? nullptr : a.ws + (size_t)rows * splits * kH * kDv;
+    uint16_t* ws_o = (uint16_t*)a.ws;
+    float* ws_lse = splits == 1 ? nullptr : (float*)(ws_o + (size_t)rows * splits * kH * kDv);
     if (a.kv_kind == 2)
         hipLaunchKernelGGL((sfa_mla_kernel<true>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,
                            (const uint8_t*)a.kv, a.kvscale, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
                            a.n_q, a.max_seq_len, rows, a.indices, a.top_k, per, splits, scale_log2,
-                           (uint16_t*)a.out, a.lse, a.ws, ws_lse);
+                           (uint16_t*)a.out, a.lse, ws_o, ws_lse);
     else
         hipLaunchKernelGGL((sfa_mla_kernel<false>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,
                            (const uint8_t*)a.kv, a.kvscale, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
                            a.n_q, a.max_seq_len, rows, a.indices, a.top_k, per, splits, scale_log2,
-                           (uint16_t*)a.out, a.lse, a.ws, ws_lse);
+                           (uint16_t*)a.out, a.lse, ws_o, ws_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
-    hipLaunchKernelGGL((sfa_combine_kernel<true>), dim3(rows, kH / 4), dim3(256), 0, st, a.ws, ws_lse, splits, kH,
-                       kDv, a.out, a.lse);
+    hipLaunchKernelGGL(sfa_combine_kernel, dim3(rows, kH / 4), dim3(256), 0, st, ws_o, ws_lse, splits, kH, kDv,
+                       (uint16_t*)a.out, a.lse);
     return hipGetLastError();
 }
 
 size_t attn_ws_bytes(int rows, int top_k, int Dqk, int H, int Dv) {
     const int s = attn_splits(rows, top_k, Dqk);
     if (s == 1) return 0;
-    return sizeof(float) * (size_t)rows * s * H * ((size_t)Dv + 1);
+    // bf16 partial outputs, then fp32 partial LSEs
+    return (size_t)rows * s * H * (sizeof(uint16_t) * (size_t)Dv + sizeof(float));
 }
 
 }  // namespace dsa

@@ -2,7 +2,7 @@
 //
 // Keeps the k_r = min(top_k, L_r) highest-scoring history positions of each
 // row ("Day0 Inference Adaptation and Performance Optimization for
-// New-Architecture LLMs", §4.1, the topk(scores, top_k) step; only the set
+// New-Architecture LLMs", §4.1, the top-k step of the indexer; only the set
 // matters downstream, §5.1).  Ties go to the lowest position and the output
 // is ascending, padded with -1.
 //
