@@ -37,8 +37,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f;       // move the running max when it grows by > 2^8
 
-// LDS byte offset of 16-byte unit u of tile row `row`.
-__device__ __forceinline__ int lds_unit(int row, int u) { return row * kRowB + ((u ^ (row & 7)) << 4); }
+// LDS byte offset of 16-byte unit u of tile row `row`: the low three unit bits
+// are XORed with bits 1..3 of the row.  With the 1152-byte row stride this
+// keeps the 16-row fragment reads (16 lanes per LDS pass, 64 banks) and whole-
+// row stores free of bank conflicts, and changes units only within aligned
+// groups of eight (so offsets of 8 units stay immediates).
+__device__ __forceinline__ int row_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int lds_unit(int row, int u) { return row * kRowB + ((u ^ row_swz(row)) << 4); }
 
 // E8M0 byte -> fp32 2^(b-127) (b = 0 gives the subnormal 2^-127; 255 is NaN).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
@@ -209,26 +214,44 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         uint32_t sc[MX ? kMxPer : 1];
     };
     Stage stA, stB;  // chunk k is staged in stA (k even) or stB (k odd)
-    auto load_chunk = [&](int c, Stage& st) __attribute__((always_inline)) {
+    // Pool rows of a chunk's staged units, read from the slot list one chunk
+    // before their loads are issued (the LDS latency stays off the issue path).
+    struct Rows {
+        int v[MX ? kMxPer : kRowsPerWave + 1];
+    };
+    Rows rows_next;
+    auto read_rows = [&](int c, Rows& R) __attribute__((always_inline)) {
         const int32_t* pc = prow + c * kCh;
         if constexpr (!MX) {
             const int4 a0 = *reinterpret_cast<const int4*>(pc + prow0);
             const int4 a1 = *reinterpret_cast<const int4*>(pc + prow0 + 4);
-            const int pr[kRowsPerWave] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            R.v[0] = a0.x; R.v[1] = a0.y; R.v[2] = a0.z; R.v[3] = a0.w;
+            R.v[4] = a1.x; R.v[5] = a1.y; R.v[6] = a1.z; R.v[7] = a1.w;
+            R.v[kRowsPerWave] = pc[tid >> 3];
+        } else {
+#pragma unroll
+            for (int i = 0; i < kMxPer; ++i) {
+                const int U = opaque(kWave * i + lane);
+                R.v[i] = (i < kMxPer - 1 || U < kRowsPerWave * kMxUnitsRow) ? pc[prow0 + U / kMxUnitsRow] : 0;
+            }
+        }
+    };
+    auto load_chunk = [&](const Rows& R, Stage& st) __attribute__((always_inline)) {
+        if constexpr (!MX) {
 #pragma unroll
             for (int i = 0; i < kRowsPerWave; ++i) {
-                const uint8_t* rowp = kv + (int64_t)__builtin_amdgcn_readfirstlane(pr[i]) * kRowB;
+                const uint8_t* rowp = kv + (int64_t)__builtin_amdgcn_readfirstlane(R.v[i]) * kRowB;
                 st.v[i] = *reinterpret_cast<const i32x4*>(rowp + lane * 16);
             }
-            const int rt = tid >> 3;
-            st.v[kRowsPerWave] = *reinterpret_cast<const i32x4*>(kv + (int64_t)pc[rt] * kRowB + 16 * (64 + (tid & 7)));
+            st.v[kRowsPerWave] =
+                *reinterpret_cast<const i32x4*>(kv + (int64_t)R.v[kRowsPerWave] * kRowB + 16 * (64 + (tid & 7)));
         } else {
 #pragma unroll
             for (int i = 0; i < kMxPer; ++i) {
                 const int U = opaque(kWave * i + lane);
                 if (i < kMxPer - 1 || U < kRowsPerWave * kMxUnitsRow) {
-                    const int r_ = U / kMxUnitsRow, u = U - r_ * kMxUnitsRow;
-                    const int64_t pr = pc[prow0 + r_];
+                    const int u = U % kMxUnitsRow;
+                    const int64_t pr = R.v[i];
                     st.v[i] = *reinterpret_cast<const i32x4*>(kv + pr * kDqk + u * 16);
                     st.sc[i] = kvscale[pr * (kDqk / 32) + (u >> 1)];
                 }
@@ -238,10 +261,10 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     auto store_chunk = [&](int slot, const Stage& st) __attribute__((always_inline)) {
         uint8_t* T = tile[slot];
         if constexpr (!MX) {
-            uint8_t* Tw = T + prow0 * kRowB;  // row 8w + i has (row & 7) == i
+            uint8_t* Tw = T + prow0 * kRowB;
 #pragma unroll
             for (int i = 0; i < kRowsPerWave; ++i)
-                *reinterpret_cast<i32x4*>(Tw + i * kRowB + ((lane ^ i) << 4)) = st.v[i];
+                *reinterpret_cast<i32x4*>(Tw + i * kRowB + ((lane ^ row_swz(prow0 + i)) << 4)) = st.v[i];
             const int rt = tid >> 3, ut = 64 + (tid & 7);
             *reinterpret_cast<i32x4*>(T + lds_unit(rt, ut)) = st.v[kRowsPerWave];
         } else {
@@ -269,11 +292,11 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         S2 s{{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
         constexpr int NB = 6, NBATCH = 2 * (kDqk / 32) / NB;  // 6 batches of 6 fragments
         bf16x8 ka[2][NB];
-        // unit 4ks + g of row r sits at 16 * ((4(ks&1) + g) ^ (r&7)) + 128 (ks>>1);
-        // rows j and 16 + j share r&7, so two base addresses and immediate
+        // unit 4ks + g of row r sits at 16 * ((4(ks&1) + g) ^ swz(r)) + 128 (ks>>1);
+        // rows j and 16 + j share swz, so two base addresses and immediate
         // offsets cover all 36 fragments.
-        const uint8_t* base0 = T + j * kRowB + ((g ^ (j & 7)) << 4);
-        const uint8_t* base1 = T + j * kRowB + (((4 + g) ^ (j & 7)) << 4);
+        const uint8_t* base0 = T + j * kRowB + ((g ^ row_swz(j)) << 4);
+        const uint8_t* base1 = T + j * kRowB + (((4 + g) ^ row_swz(j)) << 4);
         auto read_batch = [&](int bt, bf16x8 (&dst)[NB]) {
 #pragma unroll
             for (int kk = 0; kk < NB; ++kk) {
@@ -360,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         const int r0 = 8 * g + e_, r1 = 8 * g + 4 + e_;
         auto vaddr = [&](int r_, int dt) __attribute__((always_inline)) -> const uint8_t*  {
             const int unit = 16 * wave + 2 * dt + (q4 >> 1);
-            return T + r_ * kRowB + ((unit ^ (r_ & 7)) << 4) + 8 * (q4 & 1);
+            return T + r_ * kRowB + ((unit ^ row_swz(r_)) << 4) + 8 * (q4 & 1);
         };
         auto read_v = [&](int bh, bf16x8 (&vf)[kDvPerWave / 32]) {
 #pragma unroll
@@ -400,22 +423,36 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         const bool resc = c > 1 && rescale_chunk[(c - 1) & 1] == c - 1;
         if (c + 1 < nchunks) {
             store_chunk((c + 1) % kRing, st_next);
-            if (c + 3 < nchunks) load_chunk(c + 3, st_next);
+            if (c + 3 < nchunks) {
+                load_chunk(rows_next, st_next);
+                if (c + 4 < nchunks) read_rows(c + 4, rows_next);
+            }
         }
         const auto sc = qk(tile[c % kRing]);
         pv(tile[(c - 1) % kRing], c - 1, resc);
         softmax(sc.v, c);
     };
     if (nchunks > 0) {
-        load_chunk(0, stA);
-        if (nchunks > 1) load_chunk(1, stB);
+        read_rows(0, rows_next);
+        load_chunk(rows_next, stA);
+        if (nchunks > 1) {
+            read_rows(1, rows_next);
+            load_chunk(rows_next, stB);
+        }
         load_q();  // in flight with the first gathers
+        if (nchunks > 2) read_rows(2, rows_next);
         store_chunk(0, stA);
-        if (nchunks > 2) load_chunk(2, stA);
+        if (nchunks > 2) {
+            load_chunk(rows_next, stA);
+            if (nchunks > 3) read_rows(3, rows_next);
+        }
         sync_lds();
         if (nchunks > 1) {
             store_chunk(1, stB);
-            if (nchunks > 3) load_chunk(3, stB);
+            if (nchunks > 3) {
+                load_chunk(rows_next, stB);
+                if (nchunks > 4) read_rows(4, rows_next);
+            }
         }
         {
             const auto sc = qk(tile[0]);
@@ -432,36 +469,36 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         pv(tile[c % kRing], c, c > 0 && rescale_chunk[c & 1] == c);
     }
 
-    // 4. results
+    // 4. results: the normalized bf16 rows pass through LDS (the tiles are
+    //    free now) so that every store instruction writes one contiguous 1 KB
+    //    head row: O[row][hb + h][:] (or the split's partial).
     if (g == 0) {
         l_s[hl0 + j] = l_run;
         m_s[hl0 + j] = m_run;
     }
     __syncthreads();
-    const int64_t part = (int64_t)row * splits + split;
+    constexpr int kORow = kDv * 2 + 16;  // padded LDS row of one head
+    uint8_t* obuf = &tile[0][0];
 #pragma unroll
     for (int ht = 0; ht < kHalf / 16; ++ht) {
-        const int h = hb + 16 * ht + j;
         const float lsum = l_s[16 * ht + j];
         const float inv_l = lsum > 0.f ? 1.f / lsum : 0.f;
-        const int d0 = wave * kDvPerWave + 4 * g;
-        if (splits == 1) {
-            uint16_t* orow = out + ((int64_t)row * kH + h) * kDv + d0;
+        uint8_t* orow = obuf + (16 * ht + j) * kORow + 2 * (wave * kDvPerWave + 4 * g);
 #pragma unroll
-            for (int dt = 0; dt < kDvPerWave / 16; ++dt) {
-                const f32x4 v = o[dt][ht];
-                *reinterpret_cast<uint2*>(orow + 16 * dt) =
-                    make_uint2(pack_bf16x2(v[0] * inv_l, v[1] * inv_l), pack_bf16x2(v[2] * inv_l, v[3] * inv_l));
-            }
-        } else {  // the split's normalized partial, in bf16 like the output
-            uint16_t* orow = ws_o + (part * kH + h) * kDv + d0;
-#pragma unroll
-            for (int dt = 0; dt < kDvPerWave / 16; ++dt) {
-                const f32x4 v = o[dt][ht];
-                *reinterpret_cast<uint2*>(orow + 16 * dt) =
-                    make_uint2(pack_bf16x2(v[0] * inv_l, v[1] * inv_l), pack_bf16x2(v[2] * inv_l, v[3] * inv_l));
-            }
+        for (int dt = 0; dt < kDvPerWave / 16; ++dt) {
+            const f32x4 v = o[dt][ht];
+            *reinterpret_cast<uint2*>(orow + 32 * dt) =
+                make_uint2(pack_bf16x2(v[0] * inv_l, v[1] * inv_l), pack_bf16x2(v[2] * inv_l, v[3] * inv_l));
         }
+    }
+    __syncthreads();
+    const int64_t part = (int64_t)row * splits + split;
+    uint16_t* dst = splits == 1 ? out + ((int64_t)row * kH + hb) * kDv : ws_o + (part * kH + hb) * kDv;
+#pragma unroll
+    for (int k = 0; k < kHalf / kWaves; ++k) {
+        const int h = wave + kWaves * k;
+        *reinterpret_cast<uint4*>(dst + (int64_t)h * kDv + 8 * lane) =
+            *reinterpret_cast<const uint4*>(obuf + h * kORow + 16 * lane);
     }
     if (tid < kHalf) {
         const float lsum = l_s[tid];
