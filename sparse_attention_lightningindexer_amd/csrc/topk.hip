@@ -124,14 +124,146 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     }
 }
 
+// Register-resident variant for rows up to 1024 * KPT positions: thread t holds
+// the keys of positions KPT*t .. KPT*t + KPT - 1, so the keys are read from
+// memory once.  The MSB-first radix select uses digits of 12, 10 and 10 bits
+// (one LDS histogram per pass, bins owned by threads for the suffix scan), and
+// the ordered output comes from one block scan of the per-thread counts.
+template <int KPT>
+__global__ __launch_bounds__(1024) void topk_reg_kernel(const float* __restrict__ scores, int64_t ld,
+                                                        const int32_t* __restrict__ seq_lens, int n_q,
+                                                        int max_seq_len, int rows, int top_k, bool vec,
+                                                        int32_t* __restrict__ indices) {
+    constexpr int NT = 1024, NW = NT / kWave;
+    __shared__ uint32_t hist[4096];
+    __shared__ __attribute__((aligned(16))) uint32_t wsum[NW];
+    __shared__ uint32_t cut_digit, cut_above;
+    // sum of the per-wave totals of the waves w with pick(w)
+    auto wsum_where = [&](auto pick) -> uint32_t {
+        uint32_t t = 0u;
+#pragma unroll
+        for (int q = 0; q < NW / 4; ++q) {
+            const uint4 v = reinterpret_cast<const uint4*>(wsum)[q];
+            t += (pick(4 * q) ? v.x : 0u) + (pick(4 * q + 1) ? v.y : 0u) + (pick(4 * q + 2) ? v.z : 0u) +
+                 (pick(4 * q + 3) ? v.w : 0u);
+        }
+        return t;
+    };
+
+    const int r = rows - 1 - (int)blockIdx.x;
+    const int b = r / n_q, i0 = r % n_q;
+    const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, i0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int32_t* out = indices + (int64_t)r * top_k;
+    const float* row = scores + (int64_t)r * ld;
+
+    if (L <= top_k) {  // keep the whole history
+        for (int t = tid; t < top_k; t += NT) out[t] = t < L ? t : -1;
+        return;
+    }
+
+    const int base = KPT * tid;
+    const int nv = min(max(L - base, 0), KPT);  // valid keys of this thread (a prefix)
+    uint32_t key[KPT];
+    if (vec && nv == KPT) {
+#pragma unroll
+        for (int q = 0; q < KPT / 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(row + base + 4 * q);
+            key[4 * q] = score_key(v.x);
+            key[4 * q + 1] = score_key(v.y);
+            key[4 * q + 2] = score_key(v.z);
+            key[4 * q + 3] = score_key(v.w);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < KPT; ++q) key[q] = q < nv ? score_key(row[base + q]) : 0u;
+    }
+    for (int t = tid; t < 4096; t += NT) hist[t] = 0u;
+    __syncthreads();
+
+    uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)top_k;
+    auto pass = [&](int shift, int bits) {
+        const uint32_t nb = 1u << bits, dm = nb - 1u;
+#pragma unroll
+        for (int q = 0; q < KPT; ++q)
+            if (q < nv && (key[q] & mask) == prefix) atomicAdd(&hist[(key[q] >> shift) & dm], 1u);
+        __syncthreads();
+        // thread t owns bins [per*t, per*t + per); its counts are read, cleared
+        // for the next pass, and scanned from the top digit down.
+        const int per = (int)nb / NT;  // 4 or 1
+        uint32_t cnt[4] = {0u, 0u, 0u, 0u}, own = 0u;
+        for (int k = 0; k < per; ++k) {
+            cnt[k] = hist[per * tid + k];
+            hist[per * tid + k] = 0u;
+            own += cnt[k];
+        }
+        const uint32_t P = wave_scan_incl(own);                    // lanes <= this one
+        const uint32_t wtot = __builtin_amdgcn_readlane(P, kWave - 1);
+        if (lane == 0) wsum[wave] = wtot;
+        __syncthreads();
+        // keys in higher bins: later lanes of this wave, then later waves
+        const uint32_t above = (wtot - P) + wsum_where([&](int w) { return w > wave; });
+        // S(d) = keys with digit >= d; the cut digit D has S(D) >= krem > S(D+1)
+        if (above < krem && above + own >= krem) {
+            uint32_t sfx = above;
+            for (int k = per - 1; k >= 0; --k) {
+                if (sfx + cnt[k] >= krem) {
+                    cut_digit = (uint32_t)(per * tid + k);
+                    cut_above = sfx;
+                    break;
+                }
+                sfx += cnt[k];
+            }
+        }
+        __syncthreads();
+        prefix |= cut_digit << shift;
+        mask |= dm << shift;
+        krem -= cut_above;
+    };
+    pass(20, 12);
+    pass(10, 10);
+    pass(0, 10);
+
+    // prefix is the k-th largest key; krem keys equal to it are taken, lowest first.
+    const uint32_t T = prefix;
+    uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+        gt += (q < nv && key[q] > T) ? 1u : 0u;
+        eq += (q < nv && key[q] == T) ? 1u : 0u;
+    }
+    const uint32_t packed = (gt << 16) | eq;  // both totals stay below 2^16
+    const uint32_t incl = wave_scan_incl(packed);
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    const uint32_t excl = (incl - packed) + wsum_where([&](int w) { return w < wave; });
+    const uint32_t gt_before = excl >> 16, eq_before = excl & 0xffffu;
+    int slot = (int)(gt_before + min(eq_before, krem));
+    uint32_t eq_seen = eq_before;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+        if (q < nv) {
+            const bool is_eq = key[q] == T;
+            const bool sel = key[q] > T || (is_eq && eq_seen < krem);
+            eq_seen += is_eq ? 1u : 0u;
+            if (sel) out[slot++] = base + q;
+        }
+    }
+}
+
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
     const int rows = a.batch * a.n_q;
     if (rows == 0) return hipSuccess;
-    const bool cache = a.max_seq_len <= kTopkCacheMax;
-    const size_t sh = cache ? sizeof(uint32_t) * (size_t)a.max_seq_len : 0;
-    if (cache)
-        hipLaunchKernelGGL((topk_kernel<512, true>), dim3(rows), dim3(512), sh, st, a.scores, a.ld,
-                           a.seq_lens, a.n_q, a.max_seq_len, rows, a.top_k, a.indices);
+    const bool vec = (a.ld % 4) == 0 && ((uintptr_t)a.scores % 16) == 0;
+    if (a.max_seq_len <= 8 * 1024)
+        hipLaunchKernelGGL((topk_reg_kernel<8>), dim3(rows), dim3(1024), 0, st, a.scores, a.ld, a.seq_lens, a.n_q,
+                           a.max_seq_len, rows, a.top_k, vec, a.indices);
+    else if (a.max_seq_len <= 16 * 1024)
+        hipLaunchKernelGGL((topk_reg_kernel<16>), dim3(rows), dim3(1024), 0, st, a.scores, a.ld, a.seq_lens, a.n_q,
+                           a.max_seq_len, rows, a.top_k, vec, a.indices);
+    else if (a.max_seq_len <= 32 * 1024)
+        hipLaunchKernelGGL((topk_reg_kernel<32>), dim3(rows), dim3(1024), 0, st, a.scores, a.ld, a.seq_lens, a.n_q,
+                           a.max_seq_len, rows, a.top_k, vec, a.indices);
     else
         hipLaunchKernelGGL((topk_kernel<1024, false>), dim3(rows), dim3(1024), 0, st, a.scores, a.ld,
                            a.seq_lens, a.n_q, a.max_seq_len, rows, a.top_k, a.indices);

@@ -148,6 +148,21 @@ def test_topk_extreme_k_and_long_rows(top_k):
     check_indices_exact(idx, O.topk(s.astype(np.float64), wl.row_lens(), top_k))
 
 
+@pytest.mark.parametrize("long_len,top_k", [(32768, 1), (32768, 2048), (20000, 4096), (16384, 7),
+                                             (16384, 2048), (8192, 2047), (8192, 1)])
+def test_topk_register_resident_lengths_with_ties(long_len, top_k):
+    # rows up to 8192 / 16384 / 32768 positions take the register-resident kernel
+    wl = make_workload(4, batch=2, lens=[long_len, long_len // 3 + 5], top_k=top_k)
+    dev = B.DeviceInputs(wl)
+    rng = np.random.default_rng(long_len + top_k)
+    s = rng.standard_normal((wl.rows, long_len)).astype(np.float32)
+    s[:, ::89] = s[:, 5:6]                                # ties across the row
+    s[:, 1::13] = np.round(s[:, 1::13], 1)                # more ties near the cut
+    st = torch.from_numpy(s).cuda()
+    idx = B.dsa_topk(dev, st).cpu().numpy()
+    check_indices_exact(idx, O.topk(s.astype(np.float64), wl.row_lens(), top_k))
+
+
 # ------------------------------------------------------- full workload sizes
 
 FULL_SAMPLES = {
