@@ -80,22 +80,32 @@ __device__ __forceinline__ typename T::frag load_frag(const uint8_t* vec, int ks
     return *reinterpret_cast<const typename T::frag*>(vec + ks * 4 * T::FB + g * T::FB);
 }
 
+// Query fragments and head weights of one row.  Loads are unconditional
+// (a row past the end reads row 0 and is zeroed afterwards), so they issue
+// back to back.
 template <class T>
 __device__ __forceinline__ void load_row_query(const uint8_t* q, const float* q_scale, const float* w,
                                                int64_t row, bool valid, int g, int j,
                                                typename T::frag (&qa)[4][T::KSTEPS], float (&wr)[4][4]) {
+    const int64_t rr = valid ? row : 0;
+#pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        const uint8_t* v = q + ((row * kIdxHeads) + 16 * mt + j) * (int64_t)T::ROW;
-        for (int ks = 0; ks < T::KSTEPS; ++ks) {
-            if (valid) qa[mt][ks] = load_frag<T>(v, ks, g);
-            else qa[mt][ks] = typename T::frag{};
-        }
+        const uint8_t* v = q + ((rr * kIdxHeads) + 16 * mt + j) * (int64_t)T::ROW;
+#pragma unroll
+        for (int ks = 0; ks < T::KSTEPS; ++ks) qa[mt][ks] = load_frag<T>(v, ks, g);
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int h = 16 * mt + 4 * g + i;
-            float x = valid ? w[row * kIdxHeads + h] : 0.f;
-            if constexpr (T::SCALED) x *= valid ? q_scale[row * kIdxHeads + h] : 0.f;
-            wr[mt][i] = x;
+            float x = w[rr * kIdxHeads + h];
+            if constexpr (T::SCALED) x *= q_scale[rr * kIdxHeads + h];
+            wr[mt][i] = valid ? x : 0.f;
         }
+    }
+    if (!valid) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < T::KSTEPS; ++ks) qa[mt][ks] = typename T::frag{};
     }
 }
 
@@ -108,65 +118,114 @@ __device__ __forceinline__ float head_weighted_relu_sum(const f32x4 (&acc)[4], c
     return sum_over_groups(v);
 }
 
-// Decode: a sequence's n_q <= NQ rows share every K tile.  Each wave walks
-// `tiles_per_wave` consecutive 64-position tiles of one sequence, loading the
-// K fragments straight from HBM into registers (no reuse across waves).
-// grid (ceil(tiles / (4*tiles_per_wave)), batch), block 256.
-template <class T, int NQ>
+// Decode: a sequence's n_q <= NQ rows share every K tile.  Each wave owns TPW
+// consecutive 64-position tiles of one sequence; their K fragments come
+// straight from HBM into registers (no reuse across waves), two tiles in
+// flight while the previous one is scored.  grid (ceil(tiles / (4*TPW)),
+// batch), block 256.
+template <class T, int NQ, int TPW>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kpool, const float* __restrict__ kscale,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
-    int64_t num_blocks, int n_q, int max_seq_len, float* __restrict__ scores, int64_t ld,
-    int tiles_per_wave) {
+    int64_t num_blocks, int n_q, int max_seq_len, float* __restrict__ scores, int64_t ld) {
+    static_assert(NQ <= 2, "decode rows per sequence");
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, j = lane & 15;
     const int Lb = clamp_len(seq_lens, b, max_seq_len);
-    const int tile0 = (blockIdx.x * 4 + wave) * tiles_per_wave;
-    if (tile0 * kBlock >= Lb) return;  // wave-uniform; no block barrier below
+    if ((int)blockIdx.x * 4 * TPW * kBlock >= Lb) return;  // block-uniform
+    const int tile0 = (blockIdx.x * 4 + wave) * TPW;
+
+    // the sequence's query rows, staged once per workgroup (padded rows keep
+    // the 16-row fragment reads conflict free)
+    constexpr int QROW = T::ROW + 16;
+    __shared__ __attribute__((aligned(16))) uint8_t q_s[NQ * kIdxHeads * QROW];
+    {
+        constexpr int UNITS = NQ * kIdxHeads * T::ROW / 16;
+        for (int u = threadIdx.x; u < UNITS; u += 256) {
+            const int hr = u / (T::ROW / 16), c = u % (T::ROW / 16);  // head row (qi*64 + h), unit
+            const int qi = hr / kIdxHeads;
+            const int64_t rr = (int64_t)b * n_q + (qi < n_q ? qi : 0);
+            *reinterpret_cast<i32x4*>(q_s + hr * QROW + 16 * c) = *reinterpret_cast<const i32x4*>(
+                q + (rr * kIdxHeads + hr % kIdxHeads) * (int64_t)T::ROW + 16 * c);
+        }
+    }
+
+    int64_t pt[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int t = tile0 + u;
+        const int64_t p = phys_block(table, max_blocks, b, t, num_blocks);  // unconditional read
+        pt[u] = t * kBlock < Lb ? p : -1;
+    }
+    typename T::frag kf[2][4][T::KSTEPS];
+    float ksc[2][4];
+    auto load_tile = [&](int u, typename T::frag (&f)[4][T::KSTEPS], float (&sc)[4]) {
+        const int64_t p = pt[u] < 0 ? 0 : pt[u];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {  // an absent block reads block 0 (its scores are -inf)
+            const uint8_t* v = kpool + (p * kBlock + 16 * nt + j) * (int64_t)T::ROW;
+#pragma unroll
+            for (int ks = 0; ks < T::KSTEPS; ++ks) f[nt][ks] = load_frag<T>(v, ks, g);
+            if constexpr (T::SCALED) sc[nt] = kscale[p * kBlock + 16 * nt + j];
+        }
+    };
+    load_tile(0, kf[0], ksc[0]);
+    if (TPW > 1) load_tile(1, kf[1], ksc[1]);
 
     typename T::frag qa[NQ][4][T::KSTEPS];
     float wr[NQ][4][4];
-    int Lr[NQ];
+    __syncthreads();
+#pragma unroll
     for (int qi = 0; qi < NQ; ++qi) {
         const bool valid = qi < n_q;
-        const int64_t row = (int64_t)b * n_q + qi;
-        Lr[qi] = valid ? history_len(Lb, n_q, qi) : 0;
-        load_row_query<T>(q, q_scale, w, row, valid, g, j, qa[qi], wr[qi]);
-    }
-
-    for (int t = tile0; t < tile0 + tiles_per_wave; ++t) {
-        const int s0 = t * kBlock;
-        if (s0 >= Lb) break;
-        const int64_t p = phys_block(table, max_blocks, b, t, num_blocks);
-        if (p < 0) {
-            for (int qi = 0; qi < NQ; ++qi)
-                if (s0 + lane < Lr[qi]) scores[((int64_t)b * n_q + qi) * ld + s0 + lane] = -INFINITY;
-            continue;
-        }
-        typename T::frag kf[4][T::KSTEPS];
-        float ksc[4];
-        for (int nt = 0; nt < 4; ++nt) {
-            const uint8_t* v = kpool + (p * kBlock + 16 * nt + j) * (int64_t)T::ROW;
-            for (int ks = 0; ks < T::KSTEPS; ++ks) kf[nt][ks] = load_frag<T>(v, ks, g);
-            if constexpr (T::SCALED) ksc[nt] = kscale[p * kBlock + 16 * nt + j];
-        }
-        for (int qi = 0; qi < NQ; ++qi) {
-            if (s0 >= Lr[qi]) continue;
-            const int64_t row = (int64_t)b * n_q + qi;
-            for (int nt = 0; nt < 4; ++nt) {
-                f32x4 acc[4];
-                for (int mt = 0; mt < 4; ++mt) {
-                    acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    for (int ks = 0; ks < T::KSTEPS; ++ks) acc[mt] = mma(qa[qi][mt][ks], kf[nt][ks], acc[mt]);
-                }
-                float v = head_weighted_relu_sum(acc, wr[qi]);
-                if constexpr (T::SCALED) v *= ksc[nt];
-                const int s = s0 + 16 * nt + j;
-                if (g == 0 && s < Lr[qi]) scores[row * ld + s] = v;
+        const int64_t rr = (int64_t)b * n_q + (valid ? qi : 0);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const uint8_t* v = q_s + (qi * kIdxHeads + 16 * mt + j) * QROW;
+#pragma unroll
+            for (int ks = 0; ks < T::KSTEPS; ++ks) qa[qi][mt][ks] = load_frag<T>(v, ks, g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = 16 * mt + 4 * g + i;
+                float x = w[rr * kIdxHeads + h];
+                if constexpr (T::SCALED) x *= q_scale[rr * kIdxHeads + h];
+                wr[qi][mt][i] = valid ? x : 0.f;
             }
         }
+    }
+
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int s0 = (tile0 + u) * kBlock;
+        const auto& f = kf[u & 1];
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            if (qi >= n_q) continue;
+            const int64_t row = (int64_t)b * n_q + qi;
+            const int Lr = history_len(Lb, n_q, qi);
+            if (s0 >= Lr) continue;
+            if (pt[u] < 0) {  // absent block: every position scores -inf
+                if (s0 + lane < Lr) scores[row * ld + s0 + lane] = -INFINITY;
+                continue;
+            }
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                f32x4 acc[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < T::KSTEPS; ++ks) acc[mt] = mma(qa[qi][mt][ks], f[nt][ks], acc[mt]);
+                }
+                float v = head_weighted_relu_sum(acc, wr[qi]);
+                if constexpr (T::SCALED) v *= ksc[u & 1][nt];
+                const int s = s0 + 16 * nt + j;
+                if (g == 0 && s < Lr) scores[row * ld + s] = v;
+            }
+        }
+        if (u + 2 < TPW) load_tile(u + 2, kf[u & 1], ksc[u & 1]);
     }
 }
 
@@ -301,21 +360,19 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
         return hipGetLastError();
     }
     const bool fp8 = a.dtype == 2;
-    if (a.n_q <= 8) {
+    if (a.n_q <= 2) {
+        constexpr int TPW = 4;   // tiles per wave
         const int tiles = (a.max_seq_len + kBlock - 1) / kBlock;
-        const int tpw = tiles >= 4096 ? 4 : 2;   // tiles per wave
-        dim3 grid((tiles + 4 * tpw - 1) / (4 * tpw), a.batch);
+        dim3 grid((tiles + 4 * TPW - 1) / (4 * TPW), a.batch);
 #define DSA_DEC(T, NQ)                                                                          \
-    hipLaunchKernelGGL((indexer_decode_kernel<T, NQ>), grid, dim3(256), 0, st,                  \
+    hipLaunchKernelGGL((indexer_decode_kernel<T, NQ, TPW>), grid, dim3(256), 0, st,             \
                        (const uint8_t*)a.q, a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale,  \
                        a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len,  \
-                       a.scores, a.ld, tpw)
+                       a.scores, a.ld)
         if (fp8) {
-            if (a.n_q == 1) DSA_DEC(IdxFp8, 1); else if (a.n_q == 2) DSA_DEC(IdxFp8, 2);
-            else if (a.n_q <= 4) DSA_DEC(IdxFp8, 4); else DSA_DEC(IdxFp8, 8);
+            if (a.n_q == 1) DSA_DEC(IdxFp8, 1); else DSA_DEC(IdxFp8, 2);
         } else {
-            if (a.n_q == 1) DSA_DEC(IdxBf16, 1); else if (a.n_q == 2) DSA_DEC(IdxBf16, 2);
-            else if (a.n_q <= 4) DSA_DEC(IdxBf16, 4); else DSA_DEC(IdxBf16, 8);
+            if (a.n_q == 1) DSA_DEC(IdxBf16, 1); else DSA_DEC(IdxBf16, 2);
         }
 #undef DSA_DEC
         return hipGetLastError();

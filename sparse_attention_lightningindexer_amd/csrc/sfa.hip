@@ -153,20 +153,20 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     constexpr int kSlotIters = kAttnMaxSplitSlots / kThreads;
     int pr_[kSlotIters];
     {
+        // reads are unconditional (clamped to in-range slots and blocks) so
+        // that each round trip is one batch of loads
         int sv[kSlotIters];
 #pragma unroll
         for (int k = 0; k < kSlotIters; ++k) {
             const int t = slot0 + kThreads * k + tid;
-            sv[k] = t < slot1 ? indices[(int64_t)row * top_k + t] : -1;
+            const int v = indices[(int64_t)row * top_k + min(t, top_k - 1)];
+            sv[k] = t < slot1 && v >= 0 && v < L ? v : -1;
         }
 #pragma unroll
         for (int k = 0; k < kSlotIters; ++k) {
             const int sk = sv[k];
-            pr_[k] = -1;
-            if (sk >= 0 && sk < L) {
-                const int64_t p = phys_block(table, max_blocks, b, sk / kBlock, num_blocks);
-                if (p >= 0) pr_[k] = (int)(p * kBlock + (sk % kBlock));
-            }
+            const int64_t p = phys_block(table, max_blocks, b, sk < 0 ? 0 : sk / kBlock, num_blocks);
+            pr_[k] = (sk >= 0 && p >= 0) ? (int)(p * kBlock + (sk % kBlock)) : -1;
         }
     }
     int n_valid = 0;
