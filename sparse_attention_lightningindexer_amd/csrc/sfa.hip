@@ -25,6 +25,8 @@
 //      V^T comes from LDS with the transposing read ds_read_b64_tr_b16;
 //   5. the row's result (or the split's normalized partial and its LSE) is
 //      written; a combine kernel merges the splits by LSE.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -73,28 +75,27 @@ __device__ __forceinline__ void dequant_unit(i32x4 codes, float scale, i32x4& lo
 // of one row are consecutive on one XCD, so the two halves' gathers of the
 // same latent rows meet in that XCD's L2.
 //
-// Workgroup: 4 waves, one per SIMD (the whole register file each), 64 heads.
-// Per chunk of 32 positions:
-//   QK   wave w owns heads 16w .. 16w+15 of the half over all 32 positions:
-//        S^T = K . Q^T with Q^T resident in registers, so the row maxima and
-//        the softmax of the chunk are local to the wave;
-//   PV   wave w owns value channels 128w .. 128w+127 for the half's 64 heads:
+// Workgroup: 4 waves, one per SIMD (the whole register file each), 64 heads,
+// in two roles.  Per chunk of 32 positions:
+//   QK   waves 0, 1 own heads 32w .. 32w+31 of the half over all 32 positions:
+//        S^T = K . Q^T with Q^T resident in registers, each K fragment read
+//        from LDS feeding two MFMAs; the row maxima and the softmax of the
+//        chunk are local to the wave, which writes bf16 P[head][pos] and the
+//        rescale factors to LDS;
+//   PV   waves 2, 3 own value channels 256(w-2) .. +255 for all 64 heads:
 //        O^T[d][h] += V^T . P^T, each V^T fragment (transposing LDS read)
-//        feeding 4 MFMAs and each P^T fragment 8; P and the rescale factors
-//        pass through LDS.
-// Latent rows are gathered through registers (global loads two chunks ahead,
-// written to LDS one chunk ahead), which keeps more row loads in flight per
-// compute unit than LDS-direct loads do.  One barrier per chunk.
+//        feeding 4 MFMAs and each P^T fragment 16.
+// QK(c) and PV(c-1) run at the same time on different SIMDs; one barrier per
+// chunk hands P(c) over.  Latent rows are gathered through registers by the
+// two PV waves (loaded one iteration before they are written to LDS).
 // LDS (one workgroup per CU): 3 x 36 KiB tiles + P 10 KiB + slot list 8 KiB.
 constexpr int kWaves = 4, kThreads = kWaves * kWave;
 constexpr int kHalf = kH / 2;                   // heads per workgroup
-constexpr int kHeadsPerWave = kHalf / kWaves;   // 16: QK and softmax role
-constexpr int kDvPerWave = kDv / kWaves;        // 128 value channels = 8 D-tiles: PV role
+constexpr int kQkHeads = kHalf / 2;             // 32 heads per QK wave
+constexpr int kDvPerPv = kDv / 2;               // 256 value channels = 16 D-tiles per PV wave
 constexpr int kRing = 3;                        // bf16 tiles resident in LDS
 constexpr int kPRow = kCh * 2 + 16;             // bytes per head row of P (64 + 16 pad)
-constexpr int kRowsPerWave = kCh / kWaves;      // 8 chunk rows staged by each wave
 constexpr int kMxUnitsRow = kDqk / 16;          // 36 16-code units per MXFP8 row
-constexpr int kMxPer = (kRowsPerWave * kMxUnitsRow + kWave - 1) / kWave;  // 5 (the last partial)
 
 // two floats -> two bfloat16 (round to nearest even) packed in 32 bits
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -136,16 +137,6 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, qi);
     const int slot0 = split * per_split;
     const int slot1 = min(top_k, slot0 + per_split);
-
-    // QK role: heads hl0 .. hl0+15 of the half.  qf[ks] holds
-    // q[hb + hl0 + j][32ks + 8g .. +8] (the B operand of S^T = K . Q^T).
-    const int hl0 = kHeadsPerWave * wave;
-    bf16x8 qf[kDqk / 32];
-    auto load_q = [&]() __attribute__((always_inline)) {
-        const uint16_t* qrow = q + ((int64_t)row * kH + hb + hl0 + j) * kDqk + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-    };
 
     // 0. ordered compaction of the valid index slots into pool-row numbers.
     //    All of the split's indices are loaded first, then all of their table
@@ -192,306 +183,360 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     if (tid < 2) rescale_chunk[tid] = -1;
     __syncthreads();
 
-    // O^T accumulators: o[dt][ht] holds O^T[128w + 16dt + 4g + i][head hb + 16ht + j]
-    f32x4 o[kDvPerWave / 16][kHalf / 16];
-#pragma unroll
-    for (int dt = 0; dt < kDvPerWave / 16; ++dt)
-#pragma unroll
-        for (int ht = 0; ht < kHalf / 16; ++ht) o[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // softmax state of head hl0 + j (identical in the four lane groups)
-    float m_run = -INFINITY, l_run = 0.f;
-
-
-    // 1. Staging.  bf16: wave w loads chunk rows 8w .. 8w+7 whole -- 64 lanes
-    //    x 16 bytes cover a row's 512 latent channels, from a row base held in
-    //    scalar registers -- and thread t loads rope unit 64 + t%8 of row t/8.
-    //    MXFP8: unit U = 64i + lane of the wave's 8 rows x 36 units (row U/36,
-    //    16 codes U%36) with its E8M0 scale byte, dequantized (exact) to two
-    //    bf16 units when stored.  Rows are stored at their XOR-swizzled places.
-    const int prow0 = kRowsPerWave * wave;
+    // 1. Staging, by the two PV waves (w = 2, 3; sw = w - 2).  bf16: wave sw
+    //    loads chunk rows 16sw .. 16sw+15 whole -- 64 lanes x 16 bytes cover a
+    //    row's 512 latent channels, from a row base held in scalar registers --
+    //    and each of its lanes two rope units (unit 64 + U%8 of row U/8 for
+    //    U = 64sw + lane + 128k).  MXFP8: unit U = 128k + 64sw + lane of the
+    //    chunk's 32 rows x 36 units (row U/36, 16 codes U%36) with its E8M0
+    //    scale byte, dequantized (exact) to two bf16 units when stored.  Rows
+    //    are stored at their XOR-swizzled places.
+    constexpr int kStRows = kCh / 2;                 // 16 rows per staging wave
+    constexpr int kMxPer = kCh * kMxUnitsRow / (2 * kWave);  // 9 MXFP8 units per lane
+    constexpr int kStN = MX ? kMxPer : kStRows + 2;  // staged 16-byte units per lane
+    const int sw = wave - 2;
+    const int srow0 = kStRows * sw;
     struct Stage {
-        i32x4 v[kRowsPerWave + 1];
+        i32x4 v[kStN];
         uint32_t sc[MX ? kMxPer : 1];
     };
-    Stage stA, stB;  // chunk k is staged in stA (k even) or stB (k odd)
     // Pool rows of a chunk's staged units, read from the slot list one chunk
     // before their loads are issued (the LDS latency stays off the issue path).
     struct Rows {
-        int v[MX ? kMxPer : kRowsPerWave + 1];
+        int v[kStN];
     };
-    Rows rows_next;
+    auto tail_unit = [&](int k) -> int { return kWave * sw + lane + 2 * kWave * k; };  // rope unit index
     auto read_rows = [&](int c, Rows& R) __attribute__((always_inline)) {
         const int32_t* pc = prow + c * kCh;
         if constexpr (!MX) {
-            const int4 a0 = *reinterpret_cast<const int4*>(pc + prow0);
-            const int4 a1 = *reinterpret_cast<const int4*>(pc + prow0 + 4);
-            R.v[0] = a0.x; R.v[1] = a0.y; R.v[2] = a0.z; R.v[3] = a0.w;
-            R.v[4] = a1.x; R.v[5] = a1.y; R.v[6] = a1.z; R.v[7] = a1.w;
-            R.v[kRowsPerWave] = pc[tid >> 3];
+#pragma unroll
+            for (int q4 = 0; q4 < kStRows / 4; ++q4) {
+                const int4 a = *reinterpret_cast<const int4*>(pc + srow0 + 4 * q4);
+                R.v[4 * q4] = a.x; R.v[4 * q4 + 1] = a.y; R.v[4 * q4 + 2] = a.z; R.v[4 * q4 + 3] = a.w;
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) R.v[kStRows + k] = pc[tail_unit(k) >> 3];
         } else {
 #pragma unroll
-            for (int i = 0; i < kMxPer; ++i) {
-                const int U = opaque(kWave * i + lane);
-                R.v[i] = (i < kMxPer - 1 || U < kRowsPerWave * kMxUnitsRow) ? pc[prow0 + U / kMxUnitsRow] : 0;
-            }
+            for (int i = 0; i < kMxPer; ++i) R.v[i] = pc[opaque(2 * kWave * i + kWave * sw + lane) / kMxUnitsRow];
         }
     };
     auto load_chunk = [&](const Rows& R, Stage& st) __attribute__((always_inline)) {
         if constexpr (!MX) {
 #pragma unroll
-            for (int i = 0; i < kRowsPerWave; ++i) {
+            for (int i = 0; i < kStRows; ++i) {
                 const uint8_t* rowp = kv + (int64_t)__builtin_amdgcn_readfirstlane(R.v[i]) * kRowB;
                 st.v[i] = *reinterpret_cast<const i32x4*>(rowp + lane * 16);
             }
-            st.v[kRowsPerWave] =
-                *reinterpret_cast<const i32x4*>(kv + (int64_t)R.v[kRowsPerWave] * kRowB + 16 * (64 + (tid & 7)));
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                st.v[kStRows + k] = *reinterpret_cast<const i32x4*>(kv + (int64_t)R.v[kStRows + k] * kRowB +
+                                                                    16 * (64 + (tail_unit(k) & 7)));
         } else {
 #pragma unroll
             for (int i = 0; i < kMxPer; ++i) {
-                const int U = opaque(kWave * i + lane);
-                if (i < kMxPer - 1 || U < kRowsPerWave * kMxUnitsRow) {
-                    const int u = U % kMxUnitsRow;
-                    const int64_t pr = R.v[i];
-                    st.v[i] = *reinterpret_cast<const i32x4*>(kv + pr * kDqk + u * 16);
-                    st.sc[i] = kvscale[pr * (kDqk / 32) + (u >> 1)];
-                }
+                const int U = opaque(2 * kWave * i + kWave * sw + lane);
+                const int u = U % kMxUnitsRow;
+                const int64_t pr = R.v[i];
+                st.v[i] = *reinterpret_cast<const i32x4*>(kv + pr * kDqk + u * 16);
+                st.sc[i] = kvscale[pr * (kDqk / 32) + (u >> 1)];
             }
         }
     };
     auto store_chunk = [&](int slot, const Stage& st) __attribute__((always_inline)) {
         uint8_t* T = tile[slot];
         if constexpr (!MX) {
-            uint8_t* Tw = T + prow0 * kRowB;
+            uint8_t* Tw = T + srow0 * kRowB;
 #pragma unroll
-            for (int i = 0; i < kRowsPerWave; ++i)
-                *reinterpret_cast<i32x4*>(Tw + i * kRowB + ((lane ^ row_swz(prow0 + i)) << 4)) = st.v[i];
-            const int rt = tid >> 3, ut = 64 + (tid & 7);
-            *reinterpret_cast<i32x4*>(T + lds_unit(rt, ut)) = st.v[kRowsPerWave];
+            for (int i = 0; i < kStRows; ++i)
+                *reinterpret_cast<i32x4*>(Tw + i * kRowB + ((lane ^ row_swz(srow0 + i)) << 4)) = st.v[i];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int U = tail_unit(k);
+                *reinterpret_cast<i32x4*>(T + lds_unit(U >> 3, 64 + (U & 7))) = st.v[kStRows + k];
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < kMxPer; ++i) {
-                const int U = opaque(kWave * i + lane);
-                if (i < kMxPer - 1 || U < kRowsPerWave * kMxUnitsRow) {
-                    const int r_ = prow0 + U / kMxUnitsRow, u = U % kMxUnitsRow;
-                    i32x4 lo, hi;
-                    dequant_unit(st.v[i], e8m0_to_f32(st.sc[i]), lo, hi);
-                    *reinterpret_cast<i32x4*>(T + lds_unit(r_, 2 * u)) = lo;
-                    *reinterpret_cast<i32x4*>(T + lds_unit(r_, 2 * u + 1)) = hi;
+                const int U = opaque(2 * kWave * i + kWave * sw + lane);
+                const int r_ = U / kMxUnitsRow, u = U % kMxUnitsRow;
+                i32x4 lo, hi;
+                dequant_unit(st.v[i], e8m0_to_f32(st.sc[i]), lo, hi);
+                *reinterpret_cast<i32x4*>(T + lds_unit(r_, 2 * u)) = lo;
+                *reinterpret_cast<i32x4*>(T + lds_unit(r_, 2 * u + 1)) = hi;
+            }
+        }
+    };
+
+    // The chunk pipeline, common to both roles: chunk c lives in tile c % 3.
+    // At the top of iteration c (after its barrier) chunk c is in LDS, P and
+    // alpha of chunk c-1 are written, and tile (c+1) % 3 -- last read by
+    // PV(c-2) -- is free: the staged chunk c+1 is stored into it and chunk c+2
+    // is loaded into the registers it held.  `first` runs for chunk 0, `work(c)` in iteration c
+    // >= 1, `last` after the final barrier.  Both roles execute the same
+    // barriers.
+    // One chunk is staged in registers ahead of its store: chunk c+1 is
+    // loaded in iteration c-1 and stored in iteration c.
+    auto pipeline = [&](auto stage_tag, auto&& after_first_loads, auto&& first, auto&& work, auto&& last)
+                        __attribute__((always_inline)) {
+        constexpr bool STAGE = decltype(stage_tag)::value;
+        if (nchunks == 0) return;
+        Stage st;
+        Rows rows_next;
+        if constexpr (STAGE) {
+            read_rows(0, rows_next);
+            load_chunk(rows_next, st);
+            if (nchunks > 1) read_rows(1, rows_next);
+        }
+        after_first_loads();
+        if constexpr (STAGE) {
+            store_chunk(0, st);
+            if (nchunks > 1) {
+                load_chunk(rows_next, st);
+                if (nchunks > 2) read_rows(2, rows_next);
+            }
+        }
+        sync_lds();
+        if constexpr (STAGE) {
+            if (nchunks > 1) {
+                store_chunk(1, st);
+                if (nchunks > 2) {
+                    load_chunk(rows_next, st);
+                    if (nchunks > 3) read_rows(3, rows_next);
                 }
             }
         }
+        first();
+        for (int c = 1; c < nchunks; ++c) {
+            sync_lds();
+            if constexpr (STAGE) {
+                if (c + 1 < nchunks) {
+                    store_chunk((c + 1) % kRing, st);
+                    if (c + 2 < nchunks) {
+                        load_chunk(rows_next, st);
+                        if (c + 3 < nchunks) read_rows(c + 3, rows_next);
+                    }
+                }
+            }
+            work(c);
+        }
+        sync_lds();
+        last();
     };
 
-    // 2. QK of this wave's 16 heads over the chunk's 32 positions: lane holds
-    //    S[head hl0 + j][pos 16pt + 4g + i] in s[pt][i].  K fragment (pt, ks):
-    //    row 16pt + j, unit 4ks + g; the two position tiles alternate (two
-    //    independent accumulation chains).  Reads run one batch of 6 ahead of
-    //    the MFMAs that consume them.
-    auto qk = [&](const uint8_t* T) __attribute__((always_inline)) -> auto  {
-        struct S2 { f32x4 v[2]; };
-        S2 s{{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
-        constexpr int NB = 6, NBATCH = 2 * (kDqk / 32) / NB;  // 6 batches of 6 fragments
-        bf16x8 ka[2][NB];
-        // unit 4ks + g of row r sits at 16 * ((4(ks&1) + g) ^ swz(r)) + 128 (ks>>1);
-        // rows j and 16 + j share swz, so two base addresses and immediate
-        // offsets cover all 36 fragments.
-        const uint8_t* base0 = T + j * kRowB + ((g ^ row_swz(j)) << 4);
-        const uint8_t* base1 = T + j * kRowB + (((4 + g) ^ row_swz(j)) << 4);
-        auto read_batch = [&](int bt, bf16x8 (&dst)[NB]) {
+    if (wave < 2) {
+        // ---------------------------------------------------------- QK role
+        // heads hl0 .. hl0+31 of the half.  qf[ht][ks] holds
+        // q[hb + hl0 + 16ht + j][32ks + 8g .. +8] (the B operand of S^T = K . Q^T).
+        const int hl0 = kQkHeads * wave;
+        bf16x8 qf[2][kDqk / 32];
+        auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int kk = 0; kk < NB; ++kk) {
-                const int f = bt * NB + kk, pt = f & 1, ks = f >> 1;
-                dst[kk] = *reinterpret_cast<const bf16x8*>(((ks & 1) ? base1 : base0) + 16 * pt * kRowB +
-                                                           128 * (ks >> 1));
+            for (int ht = 0; ht < 2; ++ht) {
+                const uint16_t* qrow = q + ((int64_t)row * kH + hb + hl0 + 16 * ht + j) * kDqk + 8 * g;
+#pragma unroll
+                for (int ks = 0; ks < kDqk / 32; ++ks)
+                    qf[ht][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
             }
         };
-        read_batch(0, ka[0]);
+        // softmax state of heads hl0 + 16ht + j (identical in the four lane groups)
+        float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+        // S for 32 heads x 32 positions: lane holds S[head hl0 + 16ht + j][pos
+        // 16pt + 4g + i] in s[ht][pt][i].  K fragment (pt, ks): row 16pt + j,
+        // unit 4ks + g; each feeds the MFMAs of both head tiles.  Reads run
+        // one batch of 6 fragments ahead of the MFMAs that consume them.
+        struct S4 { f32x4 v[2][2]; };
+        auto qk = [&](const uint8_t* T) __attribute__((always_inline)) -> S4 {
+            S4 s;
 #pragma unroll
-        for (int bt = 0; bt < NBATCH; ++bt) {
+            for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) s.v[ht][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            constexpr int NB = 6, NBATCH = 2 * (kDqk / 32) / NB;  // 6 batches of 6 fragments
+            // unit 4ks + g of row r sits at 16 * ((4(ks&1) + g) ^ swz(r)) + 128 (ks>>1);
+            // rows j and 16 + j share swz, so two base addresses and immediate
+            // offsets cover all 36 fragments.
+            const uint8_t* base0 = T + j * kRowB + ((g ^ row_swz(j)) << 4);
+            const uint8_t* base1 = T + j * kRowB + (((4 + g) ^ row_swz(j)) << 4);
+            bf16x8 ka[2][NB];
+            auto read_batch = [&](int bt, bf16x8 (&dst)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int kk = 0; kk < NB; ++kk) {
+                    const int f = bt * NB + kk, pt = f & 1, ks = f >> 1;
+                    dst[kk] = *reinterpret_cast<const bf16x8*>(((ks & 1) ? base1 : base0) + 16 * pt * kRowB +
+                                                               128 * (ks >> 1));
+                }
+            };
+            read_batch(0, ka[0]);
+#pragma unroll
+            for (int bt = 0; bt < NBATCH; ++bt) {
+                issue_fence();
+                if (bt + 1 < NBATCH) read_batch(bt + 1, ka[(bt + 1) & 1]);
+#pragma unroll
+                for (int kk = 0; kk < NB; ++kk) {
+                    const int f = bt * NB + kk, pt = f & 1, ks = f >> 1;
+#pragma unroll
+                    for (int ht = 0; ht < 2; ++ht) s.v[ht][pt] = mfma_bf16(ka[bt & 1][kk], qf[ht][ks], s.v[ht][pt]);
+                }
+            }
             issue_fence();
-            if (bt + 1 < NBATCH) read_batch(bt + 1, ka[(bt + 1) & 1]);
+            return s;
+        };
+        // softmax of the chunk for heads hl0 + 16ht + j, local to the wave.
+        // Positions past the valid ones are -inf; exp2 of -inf is 0.
+        auto softmax = [&](const S4& s, int c) __attribute__((always_inline)) {
+            const int lim = n_valid - c * kCh - 4 * g;  // position 16pt + 4g + i is valid iff 16pt + i < lim
+            bool rescale = false;
 #pragma unroll
-            for (int kk = 0; kk < NB; ++kk) {
-                const int f = bt * NB + kk, pt = f & 1, ks = f >> 1;
-                s.v[pt] = mfma_bf16(ka[bt & 1][kk], qf[ks], s.v[pt]);
+            for (int ht = 0; ht < 2; ++ht) {
+                float sm[2][4];
+                float cmax = -INFINITY;
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sm[pt][i] = 16 * pt + i < lim ? s.v[ht][pt][i] : -INFINITY;
+                        cmax = fmaxf(cmax, sm[pt][i]);
+                    }
+                cmax = max_over_groups(cmax) * scale_log2;  // scale_log2 > 0
+                float alpha = 1.f;
+                if (cmax > m_run[ht] + kRescale) {  // also the first finite maximum (m_run = -inf)
+                    alpha = __builtin_amdgcn_exp2f(m_run[ht] - cmax);  // 0 when m_run = -inf
+                    m_run[ht] = cmax;
+                }
+                rescale |= alpha != 1.f;
+                const float mneg = m_run[ht] == -INFINITY ? 0.f : -m_run[ht];
+                float psum = 0.f;
+                const int hl = hl0 + 16 * ht + j;
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    float p[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        p[i] = __builtin_amdgcn_exp2f(fmaf(sm[pt][i], scale_log2, mneg));
+                        psum += p[i];  // fp32 denominator
+                    }
+                    *reinterpret_cast<uint2*>(pbuf[c & 1] + hl * kPRow + 2 * (16 * pt + 4 * g)) =
+                        make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+                }
+                l_run[ht] = l_run[ht] * alpha + sum_over_groups(psum);
+                if (g == 0) alpha_s[c & 1][hl] = alpha;
             }
-        }
-        issue_fence();
-        return s;
-    };
-    // softmax of the chunk for head hl0 + j, local to the wave.  Positions
-    // past the valid ones are -inf; exp2 of -inf is 0.
-    auto softmax = [&](const f32x4 (&s)[2], int c) {
-        const int lim = n_valid - c * kCh - 4 * g;  // position 16pt + 4g + i is valid iff 16pt + i < lim
-        float sm[2][4];
-        float cmax = -INFINITY;
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sm[pt][i] = 16 * pt + i < lim ? s[pt][i] : -INFINITY;
-                cmax = fmaxf(cmax, sm[pt][i]);
-            }
-        cmax = max_over_groups(cmax) * scale_log2;  // scale_log2 > 0
-        float alpha = 1.f;
-        if (cmax > m_run + kRescale) {  // also the first finite maximum (m_run = -inf)
-            alpha = __builtin_amdgcn_exp2f(m_run - cmax);  // 0 when m_run = -inf
-            m_run = cmax;
-        }
-        const float mneg = m_run == -INFINITY ? 0.f : -m_run;
-        float psum = 0.f;
-        const int hl = hl0 + j;
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-            float p[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[i] = __builtin_amdgcn_exp2f(fmaf(sm[pt][i], scale_log2, mneg));
-                psum += p[i];  // fp32 denominator
-            }
-            *reinterpret_cast<uint2*>(pbuf[c & 1] + hl * kPRow + 2 * (16 * pt + 4 * g)) =
-                make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-        }
-        l_run = l_run * alpha + sum_over_groups(psum);
-        if (g == 0) alpha_s[c & 1][hl] = alpha;
-        if (ballot(alpha != 1.f) != 0ull && lane == 0) rescale_chunk[c & 1] = c;  // every writer stores c
-    };
+            if (ballot(rescale) != 0ull && lane == 0) rescale_chunk[c & 1] = c;  // every writer stores c
+        };
 
-    // 3. PV on this wave's 128 value channels for the half's 64 heads.  V^T
-    //    fragment: lane j of group g addresses row 8g + 4h + j/4, channels
-    //    d0 + 4(j%4) (two transposing reads give positions 8g .. 8g+7 in
-    //    order); P^T fragment: lane reads P[head 16ht + j][pos 8g .. 8g+7].
-    auto pv = [&](const uint8_t* T, int c, bool rescale) __attribute__((always_inline)) {
-        if (rescale) {  // workgroup-uniform
+        pipeline(std::false_type{}, [&]() __attribute__((always_inline)) { load_q(); },
+                 [&]() __attribute__((always_inline)) { softmax(qk(tile[0]), 0); },
+                 [&](int c) __attribute__((always_inline)) { softmax(qk(tile[c % kRing]), c); },
+                 [&]() __attribute__((always_inline)) {});
+        if (g == 0) {
 #pragma unroll
-            for (int ht = 0; ht < kHalf / 16; ++ht) {
-                const float al = alpha_s[c & 1][16 * ht + j];
-#pragma unroll
-                for (int dt = 0; dt < kDvPerWave / 16; ++dt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[dt][ht][i] *= al;
+            for (int ht = 0; ht < 2; ++ht) {
+                l_s[hl0 + 16 * ht + j] = l_run[ht];
+                m_s[hl0 + 16 * ht + j] = m_run[ht];
             }
         }
-        bf16x8 pf[kHalf / 16];
+        __syncthreads();  // l and m are in LDS
+        __syncthreads();  // the PV waves' results are in LDS
+    } else {
+        // ---------------------------------------------------------- PV role
+        // value channels 256pw + 16dt + 4g + i for the half's 64 heads:
+        // o[dt][ht] holds O^T[256pw + 16dt + 4g + i][head hb + 16ht + j].
+        const int pw = wave - 2;
+        f32x4 o[kDvPerPv / 16][kHalf / 16];
 #pragma unroll
-        for (int ht = 0; ht < kHalf / 16; ++ht)
-            pf[ht] = *reinterpret_cast<const bf16x8*>(pbuf[c & 1] + (16 * ht + j) * kPRow + 16 * g);
-        // channel 128w + 16dt + 4(j%4) is unit 16w + 2dt + (j%4)/2, byte 8((j%4)&1):
-        // d-tiles dt and dt + 4 differ by one 128-byte step, so four bases per
-        // row (dt = 0..3) and an immediate offset cover the eight d-tiles.
-        const int e_ = j >> 2, q4 = j & 3;
-        const int r0 = 8 * g + e_, r1 = 8 * g + 4 + e_;
-        auto vaddr = [&](int r_, int dt) __attribute__((always_inline)) -> const uint8_t*  {
-            const int unit = 16 * wave + 2 * dt + (q4 >> 1);
-            return T + r_ * kRowB + ((unit ^ row_swz(r_)) << 4) + 8 * (q4 & 1);
-        };
-        auto read_v = [&](int bh, bf16x8 (&vf)[kDvPerWave / 32]) {
+        for (int dt = 0; dt < kDvPerPv / 16; ++dt)
 #pragma unroll
-            for (int dd = 0; dd < kDvPerWave / 32; ++dd) {
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS v4i16*)(vaddr(r0, dd) + 128 * bh));
-                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS v4i16*)(vaddr(r1, dd) + 128 * bh));
-                const v4i16 both[2] = {lo, hi};
-                vf[dd] = *reinterpret_cast<const bf16x8*>(both);
+            for (int ht = 0; ht < kHalf / 16; ++ht) o[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // V^T fragment (d-tile dt): lane j of group g addresses row 8g + 4h +
+        // j/4, channels 256pw + 16dt + 4(j%4) (two transposing reads give
+        // positions 8g .. 8g+7 in order); P^T fragment: lane reads P[head
+        // 16ht + j][pos 8g .. 8g+7].  Channel 256pw + 16dt + 4(j%4) is unit
+        // 32pw + 2dt + (j%4)/2, byte 8((j%4)&1); d-tiles 4 apart differ by one
+        // 128-byte step, so four bases per row and immediates cover all 16.
+        auto pv = [&](const uint8_t* T, int c, bool rescale) __attribute__((always_inline)) {
+            if (rescale) {  // workgroup-uniform
+#pragma unroll
+                for (int ht = 0; ht < kHalf / 16; ++ht) {
+                    const float al = alpha_s[c & 1][16 * ht + j];
+#pragma unroll
+                    for (int dt = 0; dt < kDvPerPv / 16; ++dt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o[dt][ht][i] *= al;
+                }
             }
-        };
-        bf16x8 vf[2][kDvPerWave / 32];
-        read_v(0, vf[0]);
-        issue_fence();
-        read_v(1, vf[1]);
+            bf16x8 pf[kHalf / 16];
 #pragma unroll
-        for (int bh = 0; bh < 2; ++bh) {
+            for (int ht = 0; ht < kHalf / 16; ++ht)
+                pf[ht] = *reinterpret_cast<const bf16x8*>(pbuf[c & 1] + (16 * ht + j) * kPRow + 16 * g);
+            const int e_ = j >> 2, q4 = j & 3;
+            const int r0 = 8 * g + e_, r1 = 8 * g + 4 + e_;
+            auto vaddr = [&](int r_, int dd) __attribute__((always_inline)) -> const uint8_t* {
+                const int unit = 32 * pw + 2 * dd + (q4 >> 1);
+                return T + r_ * kRowB + ((unit ^ row_swz(r_)) << 4) + 8 * (q4 & 1);
+            };
+            constexpr int NBT = 4;  // d-tiles per batch
+            auto read_v = [&](int bt, bf16x8 (&vf)[NBT]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int dd = 0; dd < kDvPerWave / 32; ++dd)
+                for (int dd = 0; dd < NBT; ++dd) {
+                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS v4i16*)(vaddr(r0, dd) + 128 * bt));
+                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS v4i16*)(vaddr(r1, dd) + 128 * bt));
+                    const v4i16 both[2] = {lo, hi};
+                    vf[dd] = *reinterpret_cast<const bf16x8*>(both);
+                }
+            };
+            bf16x8 vf[2][NBT];
+            read_v(0, vf[0]);
 #pragma unroll
-                for (int ht = 0; ht < kHalf / 16; ++ht)
-                    o[bh * (kDvPerWave / 32) + dd][ht] =
-                        mfma_bf16(vf[bh][dd], pf[ht], o[bh * (kDvPerWave / 32) + dd][ht]);
+            for (int bt = 0; bt < kDvPerPv / 16 / NBT; ++bt) {
+                issue_fence();
+                if (bt + 1 < kDvPerPv / 16 / NBT) read_v(bt + 1, vf[(bt + 1) & 1]);
+#pragma unroll
+                for (int dd = 0; dd < NBT; ++dd)
+#pragma unroll
+                    for (int ht = 0; ht < kHalf / 16; ++ht)
+                        o[NBT * bt + dd][ht] = mfma_bf16(vf[bt & 1][dd], pf[ht], o[NBT * bt + dd][ht]);
+            }
             issue_fence();
-        }
-    };
+        };
 
-    // The loop: chunk c lives in tile c % 3 and is staged in registers two
-    // chunks ahead (stA / stB by parity).  At the top of iteration c (after its
-    // barrier) chunk c is in LDS, P and alpha of chunk c-1 are written, and
-    // tile (c+1) % 3 -- last read by PV(c-2) -- is free: the staged chunk c+1
-    // is stored into it and chunk c+3 is loaded into the registers it held.
-    // QK(c) runs, then PV(c-1) (the matrix core busy while the softmax of
-    // chunk c follows), then softmax(c).
-    auto step = [&](int c, Stage& st_next) __attribute__((always_inline)) {
-        sync_lds();
-        // O is still zero after chunk 0, so its factors need not be applied
-        const bool resc = c > 1 && rescale_chunk[(c - 1) & 1] == c - 1;
-        if (c + 1 < nchunks) {
-            store_chunk((c + 1) % kRing, st_next);
-            if (c + 3 < nchunks) {
-                load_chunk(rows_next, st_next);
-                if (c + 4 < nchunks) read_rows(c + 4, rows_next);
+        pipeline(std::true_type{}, [&]() __attribute__((always_inline)) {},
+                 [&]() __attribute__((always_inline)) {},
+                 [&](int c) __attribute__((always_inline)) {
+                     // O is still zero after chunk 0, so its factors need not be applied
+                     const bool resc = c > 1 && rescale_chunk[(c - 1) & 1] == c - 1;
+                     pv(tile[(c - 1) % kRing], c - 1, resc);
+                 },
+                 [&]() __attribute__((always_inline)) {
+                     const int c = nchunks - 1;
+                     pv(tile[c % kRing], c, c > 0 && rescale_chunk[c & 1] == c);
+                 });
+
+        // normalized bf16 rows into LDS (the tiles are free now)
+        __syncthreads();  // l and m are in LDS
+        constexpr int kORow = kDv * 2 + 16;  // padded LDS row of one head
+        uint8_t* obuf = &tile[0][0];
+#pragma unroll
+        for (int ht = 0; ht < kHalf / 16; ++ht) {
+            const float lsum = l_s[16 * ht + j];
+            const float inv_l = lsum > 0.f ? 1.f / lsum : 0.f;
+            uint8_t* orow = obuf + (16 * ht + j) * kORow + 2 * (pw * kDvPerPv + 4 * g);
+#pragma unroll
+            for (int dt = 0; dt < kDvPerPv / 16; ++dt) {
+                const f32x4 v = o[dt][ht];
+                *reinterpret_cast<uint2*>(orow + 32 * dt) =
+                    make_uint2(pack_bf16x2(v[0] * inv_l, v[1] * inv_l), pack_bf16x2(v[2] * inv_l, v[3] * inv_l));
             }
         }
-        const auto sc = qk(tile[c % kRing]);
-        pv(tile[(c - 1) % kRing], c - 1, resc);
-        softmax(sc.v, c);
-    };
-    if (nchunks > 0) {
-        read_rows(0, rows_next);
-        load_chunk(rows_next, stA);
-        if (nchunks > 1) {
-            read_rows(1, rows_next);
-            load_chunk(rows_next, stB);
-        }
-        load_q();  // in flight with the first gathers
-        if (nchunks > 2) read_rows(2, rows_next);
-        store_chunk(0, stA);
-        if (nchunks > 2) {
-            load_chunk(rows_next, stA);
-            if (nchunks > 3) read_rows(3, rows_next);
-        }
-        sync_lds();
-        if (nchunks > 1) {
-            store_chunk(1, stB);
-            if (nchunks > 3) {
-                load_chunk(rows_next, stB);
-                if (nchunks > 4) read_rows(4, rows_next);
-            }
-        }
-        {
-            const auto sc = qk(tile[0]);
-            softmax(sc.v, 0);
-        }
-        int c = 1;
-        for (; c + 1 < nchunks; c += 2) {
-            step(c, stA);      // stores chunk c+1 (even), loads c+3 (even)
-            step(c + 1, stB);  // stores chunk c+2 (odd), loads c+4 (odd)
-        }
-        if (c < nchunks) step(c, stA);
-        sync_lds();
-        c = nchunks - 1;
-        pv(tile[c % kRing], c, c > 0 && rescale_chunk[c & 1] == c);
+        __syncthreads();  // the results are in LDS
     }
 
-    // 4. results: the normalized bf16 rows pass through LDS (the tiles are
-    //    free now) so that every store instruction writes one contiguous 1 KB
-    //    head row: O[row][hb + h][:] (or the split's partial).
-    if (g == 0) {
-        l_s[hl0 + j] = l_run;
-        m_s[hl0 + j] = m_run;
-    }
-    __syncthreads();
-    constexpr int kORow = kDv * 2 + 16;  // padded LDS row of one head
-    uint8_t* obuf = &tile[0][0];
-#pragma unroll
-    for (int ht = 0; ht < kHalf / 16; ++ht) {
-        const float lsum = l_s[16 * ht + j];
-        const float inv_l = lsum > 0.f ? 1.f / lsum : 0.f;
-        uint8_t* orow = obuf + (16 * ht + j) * kORow + 2 * (wave * kDvPerWave + 4 * g);
-#pragma unroll
-        for (int dt = 0; dt < kDvPerWave / 16; ++dt) {
-            const f32x4 v = o[dt][ht];
-            *reinterpret_cast<uint2*>(orow + 32 * dt) =
-                make_uint2(pack_bf16x2(v[0] * inv_l, v[1] * inv_l), pack_bf16x2(v[2] * inv_l, v[3] * inv_l));
-        }
-    }
-    __syncthreads();
+    // 4. results: every store instruction writes one contiguous 1 KB head row,
+    //    O[row][hb + h][:] (or the split's partial).
+    constexpr int kORow = kDv * 2 + 16;
+    const uint8_t* obuf = &tile[0][0];
     const int64_t part = (int64_t)row * splits + split;
     uint16_t* dst = splits == 1 ? out + ((int64_t)row * kH + hb) * kDv : ws_o + (part * kH + hb) * kDv;
 #pragma unroll
