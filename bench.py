@@ -63,7 +63,7 @@ def source_hash(files):
 
 
 # kernels of each stage, by name, as rocprofv3 reports them
-STAGE_KERNELS = {"indexer": ("indexer_",), "topk": ("topk_kernel",), "attention": ("sfa_",)}
+STAGE_KERNELS = {"indexer": ("indexer_",), "topk": ("topk_",), "attention": ("sfa_",)}
 COPY_KERNEL = "neg_kernel"  # the plain copy used to calibrate the byte counters
 
 KERNEL_SOURCES = {
@@ -278,7 +278,7 @@ def main():
         ach = nbytes / dur_s / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS}
     roof["traffic"] = measured_traffic(dom, args.workload)
-    roof["kernel"] = {"indexer": "indexer scoring (indexer_*_kernel)", "topk": "top-k (topk_kernel)",
+    roof["kernel"] = {"indexer": "indexer scoring (indexer_*_kernel)", "topk": "top-k (topk_reg_kernel or topk_kernel)",
                       "attention": "sparse attention (sfa_mla_kernel, plus sfa_combine_kernel when split)"}[dom]
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = nflops

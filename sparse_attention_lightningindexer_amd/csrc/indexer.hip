@@ -121,10 +121,11 @@ __device__ __forceinline__ float head_weighted_relu_sum(const f32x4 (&acc)[4], c
 // Decode: a sequence's n_q <= NQ rows share every K tile.  Each wave owns TPW
 // consecutive 64-position tiles of one sequence; their K fragments come
 // straight from HBM into registers (no reuse across waves), two tiles in
-// flight while the previous one is scored.  grid (ceil(tiles / (4*TPW)),
-// batch), block 256.
-template <class T, int NQ, int TPW>
-__global__ __launch_bounds__(256) void indexer_decode_kernel(
+// flight while the previous one is scored; the workgroup's NW waves share the
+// sequence's queries through LDS.  grid (ceil(tiles / (NW*TPW)), batch),
+// block 64*NW.
+template <class T, int NQ, int TPW, int NW>
+__global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kpool, const float* __restrict__ kscale,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
@@ -134,8 +135,8 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, j = lane & 15;
     const int Lb = clamp_len(seq_lens, b, max_seq_len);
-    if ((int)blockIdx.x * 4 * TPW * kBlock >= Lb) return;  // block-uniform
-    const int tile0 = (blockIdx.x * 4 + wave) * TPW;
+    if ((int)blockIdx.x * NW * TPW * kBlock >= Lb) return;  // block-uniform
+    const int tile0 = (blockIdx.x * NW + wave) * TPW;
 
     // the sequence's query rows, staged once per workgroup (padded rows keep
     // the 16-row fragment reads conflict free)
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t q_s[NQ * kIdxHeads * QROW];
     {
         constexpr int UNITS = NQ * kIdxHeads * T::ROW / 16;
-        for (int u = threadIdx.x; u < UNITS; u += 256) {
+        for (int u = threadIdx.x; u < UNITS; u += 64 * NW) {
             const int hr = u / (T::ROW / 16), c = u % (T::ROW / 16);  // head row (qi*64 + h), unit
             const int qi = hr / kIdxHeads;
             const int64_t rr = (int64_t)b * n_q + (qi < n_q ? qi : 0);
@@ -361,18 +362,19 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
     }
     const bool fp8 = a.dtype == 2;
     if (a.n_q <= 2) {
-        constexpr int TPW = 4;   // tiles per wave
+        // one row: 8 waves x 2 tiles (both in flight, two waves per SIMD); two
+        // rows need more registers: 4 waves x 4 tiles, two in flight
         const int tiles = (a.max_seq_len + kBlock - 1) / kBlock;
-        dim3 grid((tiles + 4 * TPW - 1) / (4 * TPW), a.batch);
-#define DSA_DEC(T, NQ)                                                                          \
-    hipLaunchKernelGGL((indexer_decode_kernel<T, NQ, TPW>), grid, dim3(256), 0, st,             \
-                       (const uint8_t*)a.q, a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale,  \
-                       a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len,  \
+#define DSA_DEC(T, NQ, TPW, NW)                                                                  \
+    hipLaunchKernelGGL((indexer_decode_kernel<T, NQ, TPW, NW>),                                  \
+                       dim3((tiles + NW * TPW - 1) / (NW * TPW), a.batch), dim3(64 * NW), 0, st, \
+                       (const uint8_t*)a.q, a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale,   \
+                       a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len,   \
                        a.scores, a.ld)
         if (fp8) {
-            if (a.n_q == 1) DSA_DEC(IdxFp8, 1); else DSA_DEC(IdxFp8, 2);
+            if (a.n_q == 1) DSA_DEC(IdxFp8, 1, 2, 8); else DSA_DEC(IdxFp8, 2, 4, 4);
         } else {
-            if (a.n_q == 1) DSA_DEC(IdxBf16, 1); else DSA_DEC(IdxBf16, 2);
+            if (a.n_q == 1) DSA_DEC(IdxBf16, 1, 2, 8); else DSA_DEC(IdxBf16, 2, 4, 4);
         }
 #undef DSA_DEC
         return hipGetLastError();
