@@ -168,22 +168,21 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch, const dsa_indexer_args* id
 }
 
 size_t dsa_topk_workspace_bytes(const dsa_batch* batch, int32_t top_k) {
-    (void)batch;
-    (void)top_k;
-    return 0;
+    if (check_batch(batch) != DSA_OK || top_k < 1 || top_k > kMaxTopK) return 0;
+    return dsa::topk_ws_bytes(batch->batch * batch->n_q, batch->max_seq_len, top_k);
 }
 
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores, int32_t top_k,
                     int32_t* indices, void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     dsa_status s = check_batch(batch);
     if (s != DSA_OK) return s;
     if (top_k < 1 || top_k > kMaxTopK) return DSA_ERR_SHAPE;
     if (batch->batch > 0 && (scores == nullptr || indices == nullptr)) return DSA_ERR_NULL;
     if (ld_scores < batch->max_seq_len) return DSA_ERR_SHAPE;
+    const size_t need = dsa::topk_ws_bytes(batch->batch * batch->n_q, batch->max_seq_len, top_k);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return DSA_ERR_WORKSPACE;
     dsa::TopkLaunch L{scores, ld_scores, batch->seq_lens, batch->batch, batch->n_q, batch->max_seq_len, top_k,
-                      indices};
+                      indices, (int32_t*)ws};
     return hip_status(dsa::launch_topk(L, (hipStream_t)stream));
 }
 
@@ -210,7 +209,8 @@ size_t dsa_forward_workspace_bytes(const dsa_batch* batch, const dsa_indexer_arg
     if (check_batch(batch) != DSA_OK || idx == nullptr || attn == nullptr || top_k < 1 || top_k > kMaxTopK) return 0;
     const size_t rows = (size_t)batch->batch * batch->n_q;
     return align_up(sizeof(float) * rows * (size_t)forward_ld(batch)) + align_up(sizeof(int32_t) * rows * top_k) +
-           align_up(attn_ws(batch, attn, top_k));
+           align_up(attn_ws(batch, attn, top_k)) +
+           align_up(dsa::topk_ws_bytes((int)rows, batch->max_seq_len, top_k));
 }
 
 dsa_status dsa_forward(const dsa_batch* batch, const dsa_indexer_args* idx, const dsa_attn_args* attn,
@@ -230,11 +230,14 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_indexer_args* idx, cons
     int32_t* idx_ws = (int32_t*)p;
     p += align_up(sizeof(int32_t) * rows * top_k);
     float* attn_ws_p = (float*)p;
+    p += align_up(attn_ws(batch, attn, top_k));
+    int32_t* topk_ws = (int32_t*)p;
     int32_t* indices = indices_out != nullptr ? indices_out : idx_ws;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = dsa::launch_indexer(indexer_launch(batch, idx, scores, ld), st);
     if (e != hipSuccess) return DSA_ERR_HIP;
-    dsa::TopkLaunch T{scores, ld, batch->seq_lens, batch->batch, batch->n_q, batch->max_seq_len, top_k, indices};
+    dsa::TopkLaunch T{scores, ld, batch->seq_lens, batch->batch, batch->n_q, batch->max_seq_len, top_k, indices,
+                      topk_ws};
     if ((e = dsa::launch_topk(T, st)) != hipSuccess) return DSA_ERR_HIP;
     return hip_status(dsa::launch_sparse_attn(attn_launch(batch, attn, indices, top_k, attn_ws_p), st));
 }

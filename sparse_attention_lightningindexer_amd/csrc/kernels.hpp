@@ -33,6 +33,7 @@ struct TopkLaunch {
     const int32_t* seq_lens;
     int batch, n_q, max_seq_len, top_k;
     int32_t* indices;
+    int32_t* ws;               // segment candidates for long rows, topk_ws_bytes
 };
 
 struct AttnLaunch {
@@ -59,6 +60,7 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t st);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st);
 
 int attn_splits(int rows, int top_k, int Dqk);
+size_t topk_ws_bytes(int rows, int max_seq_len, int top_k);
 size_t attn_ws_bytes(int rows, int top_k, int Dqk, int H, int Dv);
 
 }  // namespace dsa

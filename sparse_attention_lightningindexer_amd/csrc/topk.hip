@@ -124,61 +124,39 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     }
 }
 
-// Register-resident variant for rows up to 1024 * KPT positions: thread t holds
-// the keys of positions KPT*t .. KPT*t + KPT - 1, so the keys are read from
-// memory once.  The MSB-first radix select uses digits of 12, 10 and 10 bits
-// (one LDS histogram per pass, bins owned by threads for the suffix scan), and
-// the ordered output comes from one block scan of the per-thread counts.
-template <int KPT>
-__global__ __launch_bounds__(1024) void topk_reg_kernel(const float* __restrict__ scores, int64_t ld,
-                                                        const int32_t* __restrict__ seq_lens, int n_q,
-                                                        int max_seq_len, int rows, int top_k, bool vec,
-                                                        int32_t* __restrict__ indices) {
-    constexpr int NT = 1024, NW = NT / kWave;
-    __shared__ uint32_t hist[4096];
-    __shared__ __attribute__((aligned(16))) uint32_t wsum[NW];
-    __shared__ uint32_t cut_digit, cut_above;
-    // sum of the per-wave totals of the waves w with pick(w)
-    auto wsum_where = [&](auto pick) -> uint32_t {
+// Register-resident selection by one 1024-thread workgroup over up to
+// 1024 * KPT slots: thread t holds the keys of slots KPT*t .. KPT*t + KPT - 1
+// (bit q of `valid` says whether slot KPT*t + q takes part), so the keys are
+// read from memory once.  The MSB-first radix select uses digits of 12, 10 and
+// 10 bits (one LDS histogram per pass, bins owned by threads for the suffix
+// scan); the k-th largest key T and the number of ties to keep follow, and one
+// block scan of the per-thread counts gives every kept slot its output place,
+// lowest slot first among equal keys.  emit(place, q) writes kept slot
+// KPT*t + q.  Exactly `top_k` slots are kept (callers guarantee that at least
+// top_k are valid).
+constexpr int kSelThreads = 1024;
+struct SelectShared {
+    uint32_t hist[4096];
+    uint32_t wsum[kSelThreads / 64] __attribute__((aligned(16)));
+    uint32_t cut_digit, cut_above;
+};
+
+template <int KPT, class Emit>
+__device__ __forceinline__ void block_select(SelectShared& sh, const uint32_t (&key)[KPT], uint32_t valid,
+                                             int top_k, Emit&& emit) {
+    constexpr int NT = kSelThreads, NW = NT / kWave;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto wsum_where = [&](auto pick) -> uint32_t {  // sum of the per-wave totals of the waves w with pick(w)
         uint32_t t = 0u;
 #pragma unroll
         for (int q = 0; q < NW / 4; ++q) {
-            const uint4 v = reinterpret_cast<const uint4*>(wsum)[q];
+            const uint4 v = reinterpret_cast<const uint4*>(sh.wsum)[q];
             t += (pick(4 * q) ? v.x : 0u) + (pick(4 * q + 1) ? v.y : 0u) + (pick(4 * q + 2) ? v.z : 0u) +
                  (pick(4 * q + 3) ? v.w : 0u);
         }
         return t;
     };
-
-    const int r = rows - 1 - (int)blockIdx.x;
-    const int b = r / n_q, i0 = r % n_q;
-    const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, i0);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int32_t* out = indices + (int64_t)r * top_k;
-    const float* row = scores + (int64_t)r * ld;
-
-    if (L <= top_k) {  // keep the whole history
-        for (int t = tid; t < top_k; t += NT) out[t] = t < L ? t : -1;
-        return;
-    }
-
-    const int base = KPT * tid;
-    const int nv = min(max(L - base, 0), KPT);  // valid keys of this thread (a prefix)
-    uint32_t key[KPT];
-    if (vec && nv == KPT) {
-#pragma unroll
-        for (int q = 0; q < KPT / 4; ++q) {
-            const float4 v = *reinterpret_cast<const float4*>(row + base + 4 * q);
-            key[4 * q] = score_key(v.x);
-            key[4 * q + 1] = score_key(v.y);
-            key[4 * q + 2] = score_key(v.z);
-            key[4 * q + 3] = score_key(v.w);
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < KPT; ++q) key[q] = q < nv ? score_key(row[base + q]) : 0u;
-    }
-    for (int t = tid; t < 4096; t += NT) hist[t] = 0u;
+    for (int t = tid; t < 4096; t += NT) sh.hist[t] = 0u;
     __syncthreads();
 
     uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)top_k;
@@ -186,20 +164,20 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const float* __restrict_
         const uint32_t nb = 1u << bits, dm = nb - 1u;
 #pragma unroll
         for (int q = 0; q < KPT; ++q)
-            if (q < nv && (key[q] & mask) == prefix) atomicAdd(&hist[(key[q] >> shift) & dm], 1u);
+            if (((valid >> q) & 1u) && (key[q] & mask) == prefix) atomicAdd(&sh.hist[(key[q] >> shift) & dm], 1u);
         __syncthreads();
         // thread t owns bins [per*t, per*t + per); its counts are read, cleared
         // for the next pass, and scanned from the top digit down.
         const int per = (int)nb / NT;  // 4 or 1
         uint32_t cnt[4] = {0u, 0u, 0u, 0u}, own = 0u;
         for (int k = 0; k < per; ++k) {
-            cnt[k] = hist[per * tid + k];
-            hist[per * tid + k] = 0u;
+            cnt[k] = sh.hist[per * tid + k];
+            sh.hist[per * tid + k] = 0u;
             own += cnt[k];
         }
         const uint32_t P = wave_scan_incl(own);                    // lanes <= this one
         const uint32_t wtot = __builtin_amdgcn_readlane(P, kWave - 1);
-        if (lane == 0) wsum[wave] = wtot;
+        if (lane == 0) sh.wsum[wave] = wtot;
         __syncthreads();
         // keys in higher bins: later lanes of this wave, then later waves
         const uint32_t above = (wtot - P) + wsum_where([&](int w) { return w > wave; });
@@ -208,17 +186,17 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const float* __restrict_
             uint32_t sfx = above;
             for (int k = per - 1; k >= 0; --k) {
                 if (sfx + cnt[k] >= krem) {
-                    cut_digit = (uint32_t)(per * tid + k);
-                    cut_above = sfx;
+                    sh.cut_digit = (uint32_t)(per * tid + k);
+                    sh.cut_above = sfx;
                     break;
                 }
                 sfx += cnt[k];
             }
         }
         __syncthreads();
-        prefix |= cut_digit << shift;
+        prefix |= sh.cut_digit << shift;
         mask |= dm << shift;
-        krem -= cut_above;
+        krem -= sh.cut_above;
     };
     pass(20, 12);
     pass(10, 10);
@@ -229,44 +207,175 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const float* __restrict_
     uint32_t gt = 0u, eq = 0u;
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
-        gt += (q < nv && key[q] > T) ? 1u : 0u;
-        eq += (q < nv && key[q] == T) ? 1u : 0u;
+        const bool v = (valid >> q) & 1u;
+        gt += (v && key[q] > T) ? 1u : 0u;
+        eq += (v && key[q] == T) ? 1u : 0u;
     }
     const uint32_t packed = (gt << 16) | eq;  // both totals stay below 2^16
     const uint32_t incl = wave_scan_incl(packed);
-    if (lane == kWave - 1) wsum[wave] = incl;
+    if (lane == kWave - 1) sh.wsum[wave] = incl;
     __syncthreads();
     const uint32_t excl = (incl - packed) + wsum_where([&](int w) { return w < wave; });
     const uint32_t gt_before = excl >> 16, eq_before = excl & 0xffffu;
-    int slot = (int)(gt_before + min(eq_before, krem));
+    int place = (int)(gt_before + min(eq_before, krem));
     uint32_t eq_seen = eq_before;
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
-        if (q < nv) {
+        if ((valid >> q) & 1u) {
             const bool is_eq = key[q] == T;
             const bool sel = key[q] > T || (is_eq && eq_seen < krem);
             eq_seen += is_eq ? 1u : 0u;
-            if (sel) out[slot++] = base + q;
+            if (sel) emit(place++, q);
         }
     }
+}
+
+// Keys of `n` consecutive scores starting at row[base] (n <= KPT), vector
+// loads when the whole run is present and aligned.
+template <int KPT>
+__device__ __forceinline__ void load_keys(const float* row, int base, int n, bool vec, uint32_t (&key)[KPT]) {
+    if (vec && n == KPT) {
+#pragma unroll
+        for (int q = 0; q < KPT / 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(row + base + 4 * q);
+            key[4 * q] = score_key(v.x);
+            key[4 * q + 1] = score_key(v.y);
+            key[4 * q + 2] = score_key(v.z);
+            key[4 * q + 3] = score_key(v.w);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < KPT; ++q) key[q] = q < n ? score_key(row[base + q]) : 0u;
+    }
+}
+
+__device__ __forceinline__ uint32_t prefix_mask(int n) { return n >= 32 ? 0xffffffffu : ((1u << max(n, 0)) - 1u); }
+
+// Rows up to 1024 * KPT positions, one workgroup per row (rows longest first).
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void topk_reg_kernel(const float* __restrict__ scores, int64_t ld,
+                                                               const int32_t* __restrict__ seq_lens, int n_q,
+                                                               int max_seq_len, int rows, int top_k, bool vec,
+                                                               int32_t* __restrict__ indices) {
+    __shared__ SelectShared sh;
+    const int r = rows - 1 - (int)blockIdx.x;
+    const int b = r / n_q, i0 = r % n_q;
+    const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, i0);
+    const int tid = threadIdx.x;
+    int32_t* out = indices + (int64_t)r * top_k;
+    if (L <= top_k) {  // keep the whole history
+        for (int t = tid; t < top_k; t += kSelThreads) out[t] = t < L ? t : -1;
+        return;
+    }
+    const int base = KPT * tid;
+    const int nv = min(max(L - base, 0), KPT);  // valid keys of this thread (a prefix)
+    uint32_t key[KPT];
+    load_keys<KPT>(scores + (int64_t)r * ld, base, nv, vec, key);
+    block_select<KPT>(sh, key, prefix_mask(nv), top_k, [&](int place, int q) { out[place] = base + q; });
+}
+
+// Rows longer than the register-resident kernel takes: stage 1 keeps the top_k
+// of every 16384-position segment (all of a shorter segment) as ascending
+// positions in cand[row][segment][top_k] (-1 padded); the row's top_k is
+// contained in the union.  Stage 2 selects from those candidates, which are
+// in ascending position order, so the lowest-position rule for equal scores
+// carries over.  grid (segments, rows) and (rows).
+constexpr int kSegLen = kSelThreads * 16;
+
+__global__ __launch_bounds__(kSelThreads) void topk_segment_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                   const int32_t* __restrict__ seq_lens, int n_q,
+                                                                   int max_seq_len, int rows, int top_k, bool vec,
+                                                                   int nseg, int32_t* __restrict__ cand) {
+    __shared__ SelectShared sh;
+    const int seg = blockIdx.x, r = rows - 1 - (int)blockIdx.y;
+    const int b = r / n_q, i0 = r % n_q;
+    const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, i0);
+    const int tid = threadIdx.x;
+    if (L <= top_k) return;  // stage 2 writes such rows itself
+    int32_t* out = cand + ((int64_t)r * nseg + seg) * top_k;
+    const int s0 = seg * kSegLen;
+    const int Ls = min(max(L - s0, 0), kSegLen);  // positions of this segment in the history
+    if (Ls <= top_k) {
+        for (int t = tid; t < top_k; t += kSelThreads) out[t] = t < Ls ? s0 + t : -1;
+        return;
+    }
+    const int base = 16 * tid;
+    const int nv = min(max(Ls - base, 0), 16);
+    uint32_t key[16];
+    load_keys<16>(scores + (int64_t)r * ld + s0, base, nv, vec, key);
+    block_select<16>(sh, key, prefix_mask(nv), top_k, [&](int place, int q) { out[place] = s0 + base + q; });
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                 const int32_t* __restrict__ seq_lens, int n_q,
+                                                                 int max_seq_len, int rows, int top_k, int nseg,
+                                                                 const int32_t* __restrict__ cand,
+                                                                 int32_t* __restrict__ indices) {
+    __shared__ SelectShared sh;
+    const int r = rows - 1 - (int)blockIdx.x;
+    const int b = r / n_q, i0 = r % n_q;
+    const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, i0);
+    const int tid = threadIdx.x;
+    int32_t* out = indices + (int64_t)r * top_k;
+    if (L <= top_k) {
+        for (int t = tid; t < top_k; t += kSelThreads) out[t] = t < L ? t : -1;
+        return;
+    }
+    const int n = nseg * top_k;  // candidate slots of the row
+    const int32_t* cr = cand + (int64_t)r * n;
+    const float* row = scores + (int64_t)r * ld;
+    const int base = KPT * tid;
+    int pos[KPT];
+    uint32_t key[KPT], valid = 0u;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) pos[q] = base + q < n ? cr[base + q] : -1;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+        key[q] = score_key(row[pos[q] < 0 ? 0 : pos[q]]);
+        valid |= (pos[q] >= 0 ? 1u : 0u) << q;
+    }
+    block_select<KPT>(sh, key, valid, top_k, [&](int place, int q) { out[place] = pos[q]; });
+}
+
+int topk_segments(int max_seq_len) { return (max_seq_len + kSegLen - 1) / kSegLen; }
+
+size_t topk_ws_bytes(int rows, int max_seq_len, int top_k) {
+    if (max_seq_len <= 32 * 1024) return 0;
+    const int64_t n = (int64_t)topk_segments(max_seq_len) * top_k;
+    if (n > 32 * 1024) return 0;  // beyond the merge kernel: the global-memory kernel, no workspace
+    return sizeof(int32_t) * (size_t)rows * (size_t)n;
 }
 
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
     const int rows = a.batch * a.n_q;
     if (rows == 0) return hipSuccess;
     const bool vec = (a.ld % 4) == 0 && ((uintptr_t)a.scores % 16) == 0;
-    if (a.max_seq_len <= 8 * 1024)
-        hipLaunchKernelGGL((topk_reg_kernel<8>), dim3(rows), dim3(1024), 0, st, a.scores, a.ld, a.seq_lens, a.n_q,
-                           a.max_seq_len, rows, a.top_k, vec, a.indices);
-    else if (a.max_seq_len <= 16 * 1024)
-        hipLaunchKernelGGL((topk_reg_kernel<16>), dim3(rows), dim3(1024), 0, st, a.scores, a.ld, a.seq_lens, a.n_q,
-                           a.max_seq_len, rows, a.top_k, vec, a.indices);
-    else if (a.max_seq_len <= 32 * 1024)
-        hipLaunchKernelGGL((topk_reg_kernel<32>), dim3(rows), dim3(1024), 0, st, a.scores, a.ld, a.seq_lens, a.n_q,
-                           a.max_seq_len, rows, a.top_k, vec, a.indices);
-    else
+#define DSA_REG(K)                                                                                        \
+    hipLaunchKernelGGL((topk_reg_kernel<K>), dim3(rows), dim3(kSelThreads), 0, st, a.scores, a.ld, a.seq_lens, \
+                       a.n_q, a.max_seq_len, rows, a.top_k, vec, a.indices)
+    if (a.max_seq_len <= 8 * 1024) DSA_REG(8);
+    else if (a.max_seq_len <= 16 * 1024) DSA_REG(16);
+    else if (a.max_seq_len <= 32 * 1024) DSA_REG(32);
+#undef DSA_REG
+    else if (topk_ws_bytes(rows, a.max_seq_len, a.top_k) > 0) {
+        const int nseg = topk_segments(a.max_seq_len);
+        hipLaunchKernelGGL(topk_segment_kernel, dim3(nseg, rows), dim3(kSelThreads), 0, st, a.scores, a.ld,
+                           a.seq_lens, a.n_q, a.max_seq_len, rows, a.top_k, vec, nseg, a.ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int n = nseg * a.top_k;
+#define DSA_MERGE(K)                                                                                         \
+    hipLaunchKernelGGL((topk_merge_kernel<K>), dim3(rows), dim3(kSelThreads), 0, st, a.scores, a.ld, a.seq_lens, \
+                       a.n_q, a.max_seq_len, rows, a.top_k, nseg, a.ws, a.indices)
+        if (n <= 8 * 1024) DSA_MERGE(8);
+        else if (n <= 16 * 1024) DSA_MERGE(16);
+        else DSA_MERGE(32);
+#undef DSA_MERGE
+    } else {
         hipLaunchKernelGGL((topk_kernel<1024, false>), dim3(rows), dim3(1024), 0, st, a.scores, a.ld,
                            a.seq_lens, a.n_q, a.max_seq_len, rows, a.top_k, a.indices);
+    }
     return hipGetLastError();
 }
 
