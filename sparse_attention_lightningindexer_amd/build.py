@@ -19,10 +19,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
-# Per-source extras.  The attention kernel rescales its accumulators with
-# vector ALU instructions, so its matrix-core results stay in ordinary VGPRs
-# (otherwise they are copied between register files every chunk).
-EXTRA = {"sfa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra hipcc flags (none at present).
+EXTRA = {}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -18,9 +18,10 @@
 //      the MFMA operand reads are bank-conflict free).  An MXFP8 cache is
 //      dequantized (e4m3 * 2^(e8m0-127), exact in bf16) on the way in;
 //   2. S^T = K . Q^T on MFMA with Q held in registers for the whole kernel;
-//   3. online softmax in the log2 domain, per head, in registers; the
-//      running maximum is only moved when it grows by more than 2^8, which
-//      changes rounding only (numerator and denominator share it);
+//   3. softmax in the log2 domain, per head, in registers, relative to a
+//      fixed reference (the first chunk's maximum; an exact second pass if a
+//      later logit exceeds it by more than 2^32), so the accumulators are
+//      never rescaled;
 //   4. O^T += V^T . P^T on MFMA: P is laid out in LDS as the B operand, and
 //      V^T comes from LDS with the transposing read ds_read_b64_tr_b16;
 //   5. the row's result (or the split's normalized partial and its LSE) is
@@ -37,7 +38,7 @@ constexpr int kRowB = kDqk * 2;        // bytes per bf16 latent row
 constexpr int kTileB = kCh * kRowB;    // 36864 bytes per chunk
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescale = 8.0f;       // move the running max when it grows by > 2^8
+constexpr float kSlack = 32.0f;        // probabilities may exceed 1 by up to 2^32 (log2 units)
 
 // LDS byte offset of 16-byte unit u of tile row `row`: the low three unit bits
 // are XORed with bits 1..3 of the row.  With the 1152-byte row stride this
@@ -80,14 +81,14 @@ __device__ __forceinline__ void dequant_unit(i32x4 codes, float scale, i32x4& lo
 //   QK   waves 0, 1 own heads 32w .. 32w+31 of the half over all 32 positions:
 //        S^T = K . Q^T with Q^T resident in registers, each K fragment read
 //        from LDS feeding two MFMAs; the row maxima and the softmax of the
-//        chunk are local to the wave, which writes bf16 P[head][pos] and the
-//        rescale factors to LDS;
+//        chunk are local to the wave, which writes bf16 P[head][pos] to LDS;
 //   PV   waves 2, 3 own value channels 256(w-2) .. +255 for all 64 heads:
 //        O^T[d][h] += V^T . P^T, each V^T fragment (transposing LDS read)
 //        feeding 4 MFMAs and each P^T fragment 16.
 // QK(c) and PV(c-1) run at the same time on different SIMDs; one barrier per
-// chunk hands P(c) over.  Latent rows are gathered through registers by the
-// two PV waves (loaded one iteration before they are written to LDS).
+// chunk hands P(c) over.  Latent rows are gathered through registers, the
+// latent part by the PV waves and the rope part by the QK waves (loaded two
+// chunks ahead, written to LDS one chunk ahead).
 // LDS (one workgroup per CU): 3 x 36 KiB tiles + P 10 KiB + slot list 8 KiB.
 constexpr int kWaves = 4, kThreads = kWaves * kWave;
 constexpr int kHalf = kH / 2;                   // heads per workgroup
@@ -114,9 +115,8 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     float* __restrict__ lse, uint16_t* __restrict__ ws_o, float* __restrict__ ws_lse) {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kRing][kTileB];
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][kHalf * kPRow];  // P[head][pos] bf16, by chunk parity
-    __shared__ float alpha_s[2][kHalf];  // rescale factor per head, by chunk parity
     __shared__ float l_s[kHalf], m_s[kHalf];
-    __shared__ int rescale_chunk[2];     // the chunk (by parity) whose factors are not all 1
+    __shared__ int overflow;             // some logit exceeded its reference by more than 2^kSlack
     __shared__ __attribute__((aligned(16))) int32_t prow[kAttnMaxSplitSlots];
     __shared__ int wave_cnt[kWaves];
 
@@ -180,59 +180,61 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     const int nchunks = (n_valid + kCh - 1) / kCh;
     // pad the last chunk with a valid row, so every chunk row names real data
     if (tid < nchunks * kCh - n_valid) prow[n_valid + tid] = prow[0];
-    if (tid < 2) rescale_chunk[tid] = -1;
+    if (tid == 0) overflow = 0;
     __syncthreads();
 
-    // 1. Staging, by the two PV waves (w = 2, 3; sw = w - 2).  bf16: wave sw
-    //    loads chunk rows 16sw .. 16sw+15 whole -- 64 lanes x 16 bytes cover a
-    //    row's 512 latent channels, from a row base held in scalar registers --
-    //    and each of its lanes two rope units (unit 64 + U%8 of row U/8 for
-    //    U = 64sw + lane + 128k).  MXFP8: unit U = 128k + 64sw + lane of the
-    //    chunk's 32 rows x 36 units (row U/36, 16 codes U%36) with its E8M0
-    //    scale byte, dequantized (exact) to two bf16 units when stored.  Rows
-    //    are stored at their XOR-swizzled places.
-    constexpr int kStRows = kCh / 2;                 // 16 rows per staging wave
+    // 1. Staging.  bf16: PV wave sw = w - 2 loads the latent part of chunk
+    //    rows 16sw .. 16sw+15 -- 64 lanes x 16 bytes cover a row's 512 latent
+    //    channels, from a row base held in scalar registers -- and QK wave w
+    //    the rope units 64 + U%8 of rows U/8 for U = 64w + lane + 128k.
+    //    MXFP8 (PV waves only): unit U = 128i + 64sw + lane of the chunk's 32
+    //    rows x 36 units (row U/36, 16 codes U%36) with its E8M0 scale byte,
+    //    dequantized (exact) to two bf16 units when stored.  Rows are stored
+    //    at their XOR-swizzled places.  Role 0 = QK waves, 1 = PV waves.
+    constexpr int kStRows = kCh / 2;                         // 16 latent rows per PV wave
     constexpr int kMxPer = kCh * kMxUnitsRow / (2 * kWave);  // 9 MXFP8 units per lane
-    constexpr int kStN = MX ? kMxPer : kStRows + 2;  // staged 16-byte units per lane
-    const int sw = wave - 2;
+    const int sw = wave & 1;  // index of the wave within its role
     const int srow0 = kStRows * sw;
     struct Stage {
-        i32x4 v[kStN];
+        i32x4 v[MX ? kMxPer : kStRows];
         uint32_t sc[MX ? kMxPer : 1];
     };
     // Pool rows of a chunk's staged units, read from the slot list one chunk
     // before their loads are issued (the LDS latency stays off the issue path).
     struct Rows {
-        int v[kStN];
+        int v[MX ? kMxPer : kStRows];
     };
-    auto tail_unit = [&](int k) -> int { return kWave * sw + lane + 2 * kWave * k; };  // rope unit index
-    auto read_rows = [&](int c, Rows& R) __attribute__((always_inline)) {
+    auto rope_unit = [&](int k) -> int { return kWave * sw + lane + 2 * kWave * k; };
+    auto read_rows = [&](auto role_tag, int c, Rows& R) __attribute__((always_inline)) {
+        constexpr int ROLE = decltype(role_tag)::value;
         const int32_t* pc = prow + c * kCh;
-        if constexpr (!MX) {
+        if constexpr (!MX && ROLE == 1) {
 #pragma unroll
             for (int q4 = 0; q4 < kStRows / 4; ++q4) {
                 const int4 a = *reinterpret_cast<const int4*>(pc + srow0 + 4 * q4);
                 R.v[4 * q4] = a.x; R.v[4 * q4 + 1] = a.y; R.v[4 * q4 + 2] = a.z; R.v[4 * q4 + 3] = a.w;
             }
+        } else if constexpr (!MX && ROLE == 0) {
 #pragma unroll
-            for (int k = 0; k < 2; ++k) R.v[kStRows + k] = pc[tail_unit(k) >> 3];
-        } else {
+            for (int k = 0; k < 2; ++k) R.v[k] = pc[rope_unit(k) >> 3];
+        } else if constexpr (MX && ROLE == 1) {
 #pragma unroll
             for (int i = 0; i < kMxPer; ++i) R.v[i] = pc[opaque(2 * kWave * i + kWave * sw + lane) / kMxUnitsRow];
         }
     };
-    auto load_chunk = [&](const Rows& R, Stage& st) __attribute__((always_inline)) {
-        if constexpr (!MX) {
+    auto load_chunk = [&](auto role_tag, const Rows& R, Stage& st) __attribute__((always_inline)) {
+        constexpr int ROLE = decltype(role_tag)::value;
+        if constexpr (!MX && ROLE == 1) {
 #pragma unroll
             for (int i = 0; i < kStRows; ++i) {
                 const uint8_t* rowp = kv + (int64_t)__builtin_amdgcn_readfirstlane(R.v[i]) * kRowB;
                 st.v[i] = *reinterpret_cast<const i32x4*>(rowp + lane * 16);
             }
+        } else if constexpr (!MX && ROLE == 0) {
 #pragma unroll
             for (int k = 0; k < 2; ++k)
-                st.v[kStRows + k] = *reinterpret_cast<const i32x4*>(kv + (int64_t)R.v[kStRows + k] * kRowB +
-                                                                    16 * (64 + (tail_unit(k) & 7)));
-        } else {
+                st.v[k] = *reinterpret_cast<const i32x4*>(kv + (int64_t)R.v[k] * kRowB + 16 * (64 + (rope_unit(k) & 7)));
+        } else if constexpr (MX && ROLE == 1) {
 #pragma unroll
             for (int i = 0; i < kMxPer; ++i) {
                 const int U = opaque(2 * kWave * i + kWave * sw + lane);
@@ -243,19 +245,21 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
             }
         }
     };
-    auto store_chunk = [&](int slot, const Stage& st) __attribute__((always_inline)) {
+    auto store_chunk = [&](auto role_tag, int slot, const Stage& st) __attribute__((always_inline)) {
+        constexpr int ROLE = decltype(role_tag)::value;
         uint8_t* T = tile[slot];
-        if constexpr (!MX) {
+        if constexpr (!MX && ROLE == 1) {
             uint8_t* Tw = T + srow0 * kRowB;
 #pragma unroll
             for (int i = 0; i < kStRows; ++i)
                 *reinterpret_cast<i32x4*>(Tw + i * kRowB + ((lane ^ row_swz(srow0 + i)) << 4)) = st.v[i];
+        } else if constexpr (!MX && ROLE == 0) {
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                const int U = tail_unit(k);
-                *reinterpret_cast<i32x4*>(T + lds_unit(U >> 3, 64 + (U & 7))) = st.v[kStRows + k];
+                const int U = rope_unit(k);
+                *reinterpret_cast<i32x4*>(T + lds_unit(U >> 3, 64 + (U & 7))) = st.v[k];
             }
-        } else {
+        } else if constexpr (MX && ROLE == 1) {
 #pragma unroll
             for (int i = 0; i < kMxPer; ++i) {
                 const int U = opaque(2 * kWave * i + kWave * sw + lane);
@@ -268,62 +272,78 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         }
     };
 
-    // The chunk pipeline, common to both roles: chunk c lives in tile c % 3.
-    // At the top of iteration c (after its barrier) chunk c is in LDS, P and
-    // alpha of chunk c-1 are written, and tile (c+1) % 3 -- last read by
-    // PV(c-2) -- is free: the staged chunk c+1 is stored into it and chunk c+2
-    // is loaded into the registers it held.  `first` runs for chunk 0, `work(c)` in iteration c
+    // The chunk pipeline, common to both roles: chunk c lives in tile c % 3
+    // and is staged in registers two chunks ahead (stA / stB by parity).  At
+    // the top of iteration c (after its barrier) chunk c is in LDS, P of chunk
+    // c-1 is written, and tile (c+1) % 3 -- last read by PV(c-2) -- is free:
+    // the staged chunk c+1 is stored into it and chunk c+3 is loaded into the
+    // registers it held.  `first` runs for chunk 0, `work(c)` in iteration c
     // >= 1, `last` after the final barrier.  Both roles execute the same
-    // barriers.
-    // One chunk is staged in registers ahead of its store: chunk c+1 is
-    // loaded in iteration c-1 and stored in iteration c.
-    auto pipeline = [&](auto stage_tag, auto&& after_first_loads, auto&& first, auto&& work, auto&& last)
+    // barriers; only the PV waves stage.
+    auto pipeline = [&](auto role, auto&& after_first_loads, auto&& first, auto&& work, auto&& last)
                         __attribute__((always_inline)) {
-        constexpr bool STAGE = decltype(stage_tag)::value;
+        constexpr bool STAGE = decltype(role)::value == 1 || !MX;  // the QK waves stage nothing for MXFP8
         if (nchunks == 0) return;
-        Stage st;
+        Stage stA, stB;
         Rows rows_next;
         if constexpr (STAGE) {
-            read_rows(0, rows_next);
-            load_chunk(rows_next, st);
-            if (nchunks > 1) read_rows(1, rows_next);
+            read_rows(role, 0, rows_next);
+            load_chunk(role, rows_next, stA);
+            if (nchunks > 1) {
+                read_rows(role, 1, rows_next);
+                load_chunk(role, rows_next, stB);
+            }
         }
         after_first_loads();
         if constexpr (STAGE) {
-            store_chunk(0, st);
-            if (nchunks > 1) {
-                load_chunk(rows_next, st);
-                if (nchunks > 2) read_rows(2, rows_next);
+            if (nchunks > 2) read_rows(role, 2, rows_next);
+            store_chunk(role, 0, stA);
+            if (nchunks > 2) {
+                load_chunk(role, rows_next, stA);
+                if (nchunks > 3) read_rows(role, 3, rows_next);
             }
         }
         sync_lds();
         if constexpr (STAGE) {
             if (nchunks > 1) {
-                store_chunk(1, st);
-                if (nchunks > 2) {
-                    load_chunk(rows_next, st);
-                    if (nchunks > 3) read_rows(3, rows_next);
+                store_chunk(role, 1, stB);
+                if (nchunks > 3) {
+                    load_chunk(role, rows_next, stB);
+                    if (nchunks > 4) read_rows(role, 4, rows_next);
                 }
             }
         }
         first();
-        for (int c = 1; c < nchunks; ++c) {
+        auto step = [&](int c, Stage& st_next) __attribute__((always_inline)) {
             sync_lds();
             if constexpr (STAGE) {
                 if (c + 1 < nchunks) {
-                    store_chunk((c + 1) % kRing, st);
-                    if (c + 2 < nchunks) {
-                        load_chunk(rows_next, st);
-                        if (c + 3 < nchunks) read_rows(c + 3, rows_next);
+                    store_chunk(role, (c + 1) % kRing, st_next);
+                    if (c + 3 < nchunks) {
+                        load_chunk(role, rows_next, st_next);
+                        if (c + 4 < nchunks) read_rows(role, c + 4, rows_next);
                     }
                 }
             }
             work(c);
+        };
+        int c = 1;
+        for (; c + 1 < nchunks; c += 2) {
+            step(c, stA);      // stores chunk c+1 (even), loads c+3 (even)
+            step(c + 1, stB);  // stores chunk c+2 (odd), loads c+4 (odd)
         }
+        if (c < nchunks) step(c, stA);
         sync_lds();
         last();
     };
 
+    // Softmax without rescaling.  Each head's probabilities are taken
+    // relative to a reference: the first chunk's maximum.  The accumulators
+    // never need rescaling as long as no later logit exceeds the reference by
+    // more than 2^kSlack (probabilities, O and l stay far from fp32 and bf16
+    // overflow); if one does, the whole work item is computed again with the
+    // exact maximum, observed on the way, as the reference.  The result is the
+    // same softmax either way (reference and denominator cancel).
     if (wave < 2) {
         // ---------------------------------------------------------- QK role
         // heads hl0 .. hl0+31 of the half.  qf[ht][ks] holds
@@ -339,8 +359,10 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                     qf[ht][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
             }
         };
-        // softmax state of heads hl0 + 16ht + j (identical in the four lane groups)
-        float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+        // per head hl0 + 16ht + j (identical in the four lane groups): the
+        // reference, the largest scaled logit seen, and the denominator
+        float m_ref[2] = {-INFINITY, -INFINITY}, m_obs[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+        bool exact = false;  // the reference is the exact maximum (second pass)
 
         // S for 32 heads x 32 positions: lane holds S[head hl0 + 16ht + j][pos
         // 16pt + 4g + i] in s[ht][pt][i].  K fragment (pt, ks): row 16pt + j,
@@ -387,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         // Positions past the valid ones are -inf; exp2 of -inf is 0.
         auto softmax = [&](const S4& s, int c) __attribute__((always_inline)) {
             const int lim = n_valid - c * kCh - 4 * g;  // position 16pt + 4g + i is valid iff 16pt + i < lim
-            bool rescale = false;
+            bool over = false;
 #pragma unroll
             for (int ht = 0; ht < 2; ++ht) {
                 float sm[2][4];
@@ -400,13 +422,10 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                         cmax = fmaxf(cmax, sm[pt][i]);
                     }
                 cmax = max_over_groups(cmax) * scale_log2;  // scale_log2 > 0
-                float alpha = 1.f;
-                if (cmax > m_run[ht] + kRescale) {  // also the first finite maximum (m_run = -inf)
-                    alpha = __builtin_amdgcn_exp2f(m_run[ht] - cmax);  // 0 when m_run = -inf
-                    m_run[ht] = cmax;
-                }
-                rescale |= alpha != 1.f;
-                const float mneg = m_run[ht] == -INFINITY ? 0.f : -m_run[ht];
+                if (!exact && c == 0) m_ref[ht] = cmax;
+                m_obs[ht] = fmaxf(m_obs[ht], cmax);
+                over |= cmax > m_ref[ht] + kSlack;          // also a reference of -inf
+                const float mneg = m_ref[ht] == -INFINITY ? 0.f : -m_ref[ht];
                 float psum = 0.f;
                 const int hl = hl0 + 16 * ht + j;
 #pragma unroll
@@ -420,21 +439,31 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                     *reinterpret_cast<uint2*>(pbuf[c & 1] + hl * kPRow + 2 * (16 * pt + 4 * g)) =
                         make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
                 }
-                l_run[ht] = l_run[ht] * alpha + sum_over_groups(psum);
-                if (g == 0) alpha_s[c & 1][hl] = alpha;
+                l_run[ht] += sum_over_groups(psum);
             }
-            if (ballot(rescale) != 0ull && lane == 0) rescale_chunk[c & 1] = c;  // every writer stores c
+            if (ballot(over) != 0ull && lane == 0) overflow = 1;
         };
 
-        pipeline(std::false_type{}, [&]() __attribute__((always_inline)) { load_q(); },
-                 [&]() __attribute__((always_inline)) { softmax(qk(tile[0]), 0); },
-                 [&](int c) __attribute__((always_inline)) { softmax(qk(tile[c % kRing]), c); },
-                 [&]() __attribute__((always_inline)) {});
+        for (;;) {
+            pipeline(std::integral_constant<int, 0>{}, [&]() __attribute__((always_inline)) { load_q(); },
+                     [&]() __attribute__((always_inline)) { softmax(qk(tile[0]), 0); },
+                     [&](int c) __attribute__((always_inline)) { softmax(qk(tile[c % kRing]), c); },
+                     [&]() __attribute__((always_inline)) {});
+            if (overflow == 0) break;  // read by every wave after the pipeline's last barrier
+            __syncthreads();           // every wave has read the flag
+            if (tid == 0) overflow = 0;
+            exact = true;
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht) {
+                m_ref[ht] = m_obs[ht];
+                l_run[ht] = 0.f;
+            }
+        }
         if (g == 0) {
 #pragma unroll
             for (int ht = 0; ht < 2; ++ht) {
                 l_s[hl0 + 16 * ht + j] = l_run[ht];
-                m_s[hl0 + 16 * ht + j] = m_run[ht];
+                m_s[hl0 + 16 * ht + j] = m_ref[ht];
             }
         }
         __syncthreads();  // l and m are in LDS
@@ -456,17 +485,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         // 16ht + j][pos 8g .. 8g+7].  Channel 256pw + 16dt + 4(j%4) is unit
         // 32pw + 2dt + (j%4)/2, byte 8((j%4)&1); d-tiles 4 apart differ by one
         // 128-byte step, so four bases per row and immediates cover all 16.
-        auto pv = [&](const uint8_t* T, int c, bool rescale) __attribute__((always_inline)) {
-            if (rescale) {  // workgroup-uniform
-#pragma unroll
-                for (int ht = 0; ht < kHalf / 16; ++ht) {
-                    const float al = alpha_s[c & 1][16 * ht + j];
-#pragma unroll
-                    for (int dt = 0; dt < kDvPerPv / 16; ++dt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) o[dt][ht][i] *= al;
-                }
-            }
+        auto pv = [&](const uint8_t* T, int c) __attribute__((always_inline)) {
             bf16x8 pf[kHalf / 16];
 #pragma unroll
             for (int ht = 0; ht < kHalf / 16; ++ht)
@@ -477,12 +496,15 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                 const int unit = 32 * pw + 2 * dd + (q4 >> 1);
                 return T + r_ * kRowB + ((unit ^ row_swz(r_)) << 4) + 8 * (q4 & 1);
             };
-            constexpr int NBT = 4;  // d-tiles per batch
+            constexpr int NBT = 2;  // d-tiles per batch
             auto read_v = [&](int bt, bf16x8 (&vf)[NBT]) __attribute__((always_inline)) {
 #pragma unroll
                 for (int dd = 0; dd < NBT; ++dd) {
-                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS v4i16*)(vaddr(r0, dd) + 128 * bt));
-                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS v4i16*)(vaddr(r1, dd) + 128 * bt));
+                    const int dt = NBT * bt + dd;  // bases for dt % 4, one 128-byte step per 4 d-tiles
+                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (DSA_LDS v4i16*)(vaddr(r0, dt & 3) + 128 * (dt >> 2)));
+                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (DSA_LDS v4i16*)(vaddr(r1, dt & 3) + 128 * (dt >> 2)));
                     const v4i16 both[2] = {lo, hi};
                     vf[dd] = *reinterpret_cast<const bf16x8*>(both);
                 }
@@ -502,17 +524,18 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
             issue_fence();
         };
 
-        pipeline(std::true_type{}, [&]() __attribute__((always_inline)) {},
-                 [&]() __attribute__((always_inline)) {},
-                 [&](int c) __attribute__((always_inline)) {
-                     // O is still zero after chunk 0, so its factors need not be applied
-                     const bool resc = c > 1 && rescale_chunk[(c - 1) & 1] == c - 1;
-                     pv(tile[(c - 1) % kRing], c - 1, resc);
-                 },
-                 [&]() __attribute__((always_inline)) {
-                     const int c = nchunks - 1;
-                     pv(tile[c % kRing], c, c > 0 && rescale_chunk[c & 1] == c);
-                 });
+        for (;;) {
+            pipeline(std::integral_constant<int, 1>{}, [&]() __attribute__((always_inline)) {},
+                     [&]() __attribute__((always_inline)) {},
+                     [&](int c) __attribute__((always_inline)) { pv(tile[(c - 1) % kRing], c - 1); },
+                     [&]() __attribute__((always_inline)) { pv(tile[(nchunks - 1) % kRing], nchunks - 1); });
+            if (overflow == 0) break;
+            __syncthreads();  // every wave has read the flag; the work item is computed again
+#pragma unroll
+            for (int dt = 0; dt < kDvPerPv / 16; ++dt)
+#pragma unroll
+                for (int ht = 0; ht < kHalf / 16; ++ht) o[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 
         // normalized bf16 rows into LDS (the tiles are free now)
         __syncthreads();  // l and m are in LDS
