@@ -85,16 +85,20 @@ __device__ __forceinline__ void dequant_unit(i32x4 codes, float scale, i32x4& lo
 //   PV   waves 2, 3 own value channels 256(w-2) .. +255 for all 64 heads:
 //        O^T[d][h] += V^T . P^T, each V^T fragment (transposing LDS read)
 //        feeding 4 MFMAs and each P^T fragment 16.
-// QK(c) and PV(c-1) run at the same time on different SIMDs; one barrier per
-// chunk hands P(c) over.  Latent rows are gathered through registers, the
-// latent part by the PV waves and the rope part by the QK waves (loaded two
-// chunks ahead, written to LDS one chunk ahead).
-// LDS (one workgroup per CU): 3 x 36 KiB tiles + P 10 KiB + slot list 8 KiB.
+// The QK waves run one chunk ahead: in iteration c they issue the MFMAs of
+// QK(c) together with the softmax of chunk c-1 (independent work, so the
+// matrix core and the vector ALU overlap), while the PV waves compute
+// PV(c-2).  One barrier per chunk hands P over.  Latent rows are gathered
+// through registers by the PV waves (loaded two chunks ahead of their store,
+// stored one chunk ahead of their QK); each PV wave keeps the pool rows of its
+// 16 chunk rows for every chunk in registers (row r in register r, chunk c in
+// lane c).  LDS (one workgroup per CU): 4 x 36 KiB tiles + P 10 KiB; the slot
+// list of the compaction lives in the fourth tile until the gathers start.
 constexpr int kWaves = 4, kThreads = kWaves * kWave;
 constexpr int kHalf = kH / 2;                   // heads per workgroup
 constexpr int kQkHeads = kHalf / 2;             // 32 heads per QK wave
 constexpr int kDvPerPv = kDv / 2;               // 256 value channels = 16 D-tiles per PV wave
-constexpr int kRing = 3;                        // bf16 tiles resident in LDS
+constexpr int kRing = 4;                        // bf16 tiles resident in LDS
 constexpr int kPRow = kCh * 2 + 16;             // bytes per head row of P (64 + 16 pad)
 constexpr int kMxUnitsRow = kDqk / 16;          // 36 16-code units per MXFP8 row
 
@@ -117,8 +121,9 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][kHalf * kPRow];  // P[head][pos] bf16, by chunk parity
     __shared__ float l_s[kHalf], m_s[kHalf];
     __shared__ int overflow;             // some logit exceeded its reference by more than 2^kSlack
-    __shared__ __attribute__((aligned(16))) int32_t prow[kAttnMaxSplitSlots];
     __shared__ int wave_cnt[kWaves];
+    int32_t* const prow = reinterpret_cast<int32_t*>(&tile[kRing - 1][0]);  // slot list (prologue only)
+    static_assert(kAttnMaxSplitSlots * 4 <= kTileB, "slot list fits in one tile");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -183,158 +188,135 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     if (tid == 0) overflow = 0;
     __syncthreads();
 
-    // 1. Staging.  bf16: PV wave sw = w - 2 loads the latent part of chunk
-    //    rows 16sw .. 16sw+15 -- 64 lanes x 16 bytes cover a row's 512 latent
-    //    channels, from a row base held in scalar registers -- and QK wave w
-    //    the rope units 64 + U%8 of rows U/8 for U = 64w + lane + 128k.
-    //    MXFP8 (PV waves only): unit U = 128i + 64sw + lane of the chunk's 32
-    //    rows x 36 units (row U/36, 16 codes U%36) with its E8M0 scale byte,
-    //    dequantized (exact) to two bf16 units when stored.  Rows are stored
-    //    at their XOR-swizzled places.  Role 0 = QK waves, 1 = PV waves.
-    constexpr int kStRows = kCh / 2;                         // 16 latent rows per PV wave
-    constexpr int kMxPer = kCh * kMxUnitsRow / (2 * kWave);  // 9 MXFP8 units per lane
+    // 1. Staging, by the PV waves (sw = w - 2 owns chunk rows 16sw .. 16sw+15).
+    //    bf16: each row's 512 latent channels are one 64-lane x 16-byte load
+    //    from a row base in scalar registers; the rope units 64 + lane%8 of
+    //    rows 16sw + lane/8 + 8k (k = 0, 1) follow as two loads.  MXFP8: unit
+    //    U = 64i + lane of the wave's 16 rows x 36 units (row U/36, 16 codes
+    //    U%36) with its E8M0 scale byte, dequantized (exact) to two bf16 units
+    //    when stored.  Rows are stored at their XOR-swizzled places.
+    constexpr int kStRows = kCh / 2;                           // 16 rows per PV wave
+    constexpr int kMxPer = kStRows * kMxUnitsRow / kWave;      // 9 MXFP8 units per lane
+    constexpr int kStN = MX ? kMxPer : kStRows + 2;
     const int sw = wave & 1;  // index of the wave within its role
     const int srow0 = kStRows * sw;
     struct Stage {
-        i32x4 v[MX ? kMxPer : kStRows];
+        i32x4 v[kStN];
         uint32_t sc[MX ? kMxPer : 1];
     };
-    // Pool rows of a chunk's staged units, read from the slot list one chunk
-    // before their loads are issued (the LDS latency stays off the issue path).
-    struct Rows {
-        int v[MX ? kMxPer : kStRows];
+    int vid[kStRows];  // pool row of chunk row srow0 + r of chunk c, in lane c
+    auto load_row_ids = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < kStRows; ++r) vid[r] = lane < nchunks ? prow[lane * kCh + srow0 + r] : 0;
     };
-    auto rope_unit = [&](int k) -> int { return kWave * sw + lane + 2 * kWave * k; };
-    auto read_rows = [&](auto role_tag, int c, Rows& R) __attribute__((always_inline)) {
-        constexpr int ROLE = decltype(role_tag)::value;
-        const int32_t* pc = prow + c * kCh;
-        if constexpr (!MX && ROLE == 1) {
-#pragma unroll
-            for (int q4 = 0; q4 < kStRows / 4; ++q4) {
-                const int4 a = *reinterpret_cast<const int4*>(pc + srow0 + 4 * q4);
-                R.v[4 * q4] = a.x; R.v[4 * q4 + 1] = a.y; R.v[4 * q4 + 2] = a.z; R.v[4 * q4 + 3] = a.w;
-            }
-        } else if constexpr (!MX && ROLE == 0) {
-#pragma unroll
-            for (int k = 0; k < 2; ++k) R.v[k] = pc[rope_unit(k) >> 3];
-        } else if constexpr (MX && ROLE == 1) {
-#pragma unroll
-            for (int i = 0; i < kMxPer; ++i) R.v[i] = pc[opaque(2 * kWave * i + kWave * sw + lane) / kMxUnitsRow];
-        }
+    // pool row of chunk row srow0 + r of chunk c (wave-uniform)
+    auto sid = [&](int c, int r) __attribute__((always_inline)) -> int {
+        return __builtin_amdgcn_readlane(vid[r], c);
     };
-    auto load_chunk = [&](auto role_tag, const Rows& R, Stage& st) __attribute__((always_inline)) {
-        constexpr int ROLE = decltype(role_tag)::value;
-        if constexpr (!MX && ROLE == 1) {
+    auto load_chunk = [&](int c, Stage& st) __attribute__((always_inline)) {
+        if constexpr (!MX) {
+            int rid[kStRows];
 #pragma unroll
-            for (int i = 0; i < kStRows; ++i) {
-                const uint8_t* rowp = kv + (int64_t)__builtin_amdgcn_readfirstlane(R.v[i]) * kRowB;
-                st.v[i] = *reinterpret_cast<const i32x4*>(rowp + lane * 16);
-            }
-        } else if constexpr (!MX && ROLE == 0) {
+            for (int r = 0; r < kStRows; ++r) rid[r] = sid(c, r);
 #pragma unroll
-            for (int k = 0; k < 2; ++k)
-                st.v[k] = *reinterpret_cast<const i32x4*>(kv + (int64_t)R.v[k] * kRowB + 16 * (64 + (rope_unit(k) & 7)));
-        } else if constexpr (MX && ROLE == 1) {
-#pragma unroll
-            for (int i = 0; i < kMxPer; ++i) {
-                const int U = opaque(2 * kWave * i + kWave * sw + lane);
-                const int u = U % kMxUnitsRow;
-                const int64_t pr = R.v[i];
-                st.v[i] = *reinterpret_cast<const i32x4*>(kv + pr * kDqk + u * 16);
-                st.sc[i] = kvscale[pr * (kDqk / 32) + (u >> 1)];
-            }
-        }
-    };
-    auto store_chunk = [&](auto role_tag, int slot, const Stage& st) __attribute__((always_inline)) {
-        constexpr int ROLE = decltype(role_tag)::value;
-        uint8_t* T = tile[slot];
-        if constexpr (!MX && ROLE == 1) {
-            uint8_t* Tw = T + srow0 * kRowB;
-#pragma unroll
-            for (int i = 0; i < kStRows; ++i)
-                *reinterpret_cast<i32x4*>(Tw + i * kRowB + ((lane ^ row_swz(srow0 + i)) << 4)) = st.v[i];
-        } else if constexpr (!MX && ROLE == 0) {
+            for (int r = 0; r < kStRows; ++r)
+                st.v[r] = *reinterpret_cast<const i32x4*>(kv + (int64_t)rid[r] * kRowB + lane * 16);
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                const int U = rope_unit(k);
-                *reinterpret_cast<i32x4*>(T + lds_unit(U >> 3, 64 + (U & 7))) = st.v[k];
+                int id = rid[8 * k];
+#pragma unroll
+                for (int m = 1; m < 8; ++m) id = (lane >> 3) == m ? rid[8 * k + m] : id;
+                st.v[kStRows + k] = *reinterpret_cast<const i32x4*>(kv + (int64_t)id * kRowB + 16 * (64 + (lane & 7)));
             }
-        } else if constexpr (MX && ROLE == 1) {
+        } else {
 #pragma unroll
             for (int i = 0; i < kMxPer; ++i) {
-                const int U = opaque(2 * kWave * i + kWave * sw + lane);
-                const int r_ = U / kMxUnitsRow, u = U % kMxUnitsRow;
+                const int U = kWave * i + lane;
+                const int r = U / kMxUnitsRow, u = U - r * kMxUnitsRow;
+                constexpr int dummy = 0;
+                (void)dummy;
+                const int r0 = (kWave * i) / kMxUnitsRow;  // the instruction's rows are r0 .. r0+2
+                int id = sid(c, r0);
+                if (r0 + 1 < kStRows) id = r == r0 + 1 ? sid(c, r0 + 1) : id;
+                if (r0 + 2 < kStRows) id = r == r0 + 2 ? sid(c, r0 + 2) : id;
+                st.v[i] = *reinterpret_cast<const i32x4*>(kv + (int64_t)id * kDqk + u * 16);
+                st.sc[i] = kvscale[(int64_t)id * (kDqk / 32) + (u >> 1)];
+            }
+        }
+    };
+    auto store_chunk = [&](int slot, const Stage& st) __attribute__((always_inline)) {
+        uint8_t* T = tile[slot];
+        if constexpr (!MX) {
+            uint8_t* Tw = T + srow0 * kRowB;
+#pragma unroll
+            for (int r = 0; r < kStRows; ++r)
+                *reinterpret_cast<i32x4*>(Tw + r * kRowB + ((lane ^ row_swz(srow0 + r)) << 4)) = st.v[r];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int row = srow0 + (lane >> 3) + 8 * k;
+                *reinterpret_cast<i32x4*>(T + lds_unit(row, 64 + (lane & 7))) = st.v[kStRows + k];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kMxPer; ++i) {
+                const int U = kWave * i + lane;
+                const int r = U / kMxUnitsRow, u = U - r * kMxUnitsRow;
                 i32x4 lo, hi;
                 dequant_unit(st.v[i], e8m0_to_f32(st.sc[i]), lo, hi);
-                *reinterpret_cast<i32x4*>(T + lds_unit(r_, 2 * u)) = lo;
-                *reinterpret_cast<i32x4*>(T + lds_unit(r_, 2 * u + 1)) = hi;
+                *reinterpret_cast<i32x4*>(T + lds_unit(srow0 + r, 2 * u)) = lo;
+                *reinterpret_cast<i32x4*>(T + lds_unit(srow0 + r, 2 * u + 1)) = hi;
             }
         }
     };
 
-    // The chunk pipeline, common to both roles: chunk c lives in tile c % 3
-    // and is staged in registers two chunks ahead (stA / stB by parity).  At
-    // the top of iteration c (after its barrier) chunk c is in LDS, P of chunk
-    // c-1 is written, and tile (c+1) % 3 -- last read by PV(c-2) -- is free:
-    // the staged chunk c+1 is stored into it and chunk c+3 is loaded into the
-    // registers it held.  `first` runs for chunk 0, `work(c)` in iteration c
-    // >= 1, `last` after the final barrier.  Both roles execute the same
-    // barriers; only the PV waves stage.
-    auto pipeline = [&](auto role, auto&& after_first_loads, auto&& first, auto&& work, auto&& last)
-                        __attribute__((always_inline)) {
-        constexpr bool STAGE = decltype(role)::value == 1 || !MX;  // the QK waves stage nothing for MXFP8
+    // The chunk pipeline: chunk c lives in tile c % 4.  Chunk k is loaded into
+    // registers in iteration k-3 and stored into its tile in iteration k-1
+    // (tile k % 4 was last read by PV(k-4) in iteration k-2).  Iteration c
+    // (after its barrier): chunk c is in LDS and P(c-2) is written; the QK
+    // waves run QK(c) with softmax(c-1), the PV waves stage and run PV(c-2).
+    // Both roles execute the same nchunks + 2 barriers.
+    auto pv_pipeline = [&](auto&& pv_chunk) __attribute__((always_inline)) {
         if (nchunks == 0) return;
-        Stage stA, stB;
-        Rows rows_next;
-        if constexpr (STAGE) {
-            read_rows(role, 0, rows_next);
-            load_chunk(role, rows_next, stA);
-            if (nchunks > 1) {
-                read_rows(role, 1, rows_next);
-                load_chunk(role, rows_next, stB);
-            }
+        Stage stA, stB;  // chunk k is staged in stA (k even) or stB (k odd)
+        load_chunk(0, stA);
+        if (nchunks > 1) load_chunk(1, stB);
+        store_chunk(0, stA);
+        if (nchunks > 2) load_chunk(2, stA);
+        sync_lds();  // barrier 0
+        if (nchunks > 1) {
+            store_chunk(1, stB);
+            if (nchunks > 3) load_chunk(3, stB);
         }
-        after_first_loads();
-        if constexpr (STAGE) {
-            if (nchunks > 2) read_rows(role, 2, rows_next);
-            store_chunk(role, 0, stA);
-            if (nchunks > 2) {
-                load_chunk(role, rows_next, stA);
-                if (nchunks > 3) read_rows(role, 3, rows_next);
-            }
-        }
-        sync_lds();
-        if constexpr (STAGE) {
-            if (nchunks > 1) {
-                store_chunk(role, 1, stB);
-                if (nchunks > 3) {
-                    load_chunk(role, rows_next, stB);
-                    if (nchunks > 4) read_rows(role, 4, rows_next);
-                }
-            }
-        }
-        first();
         auto step = [&](int c, Stage& st_next) __attribute__((always_inline)) {
-            sync_lds();
-            if constexpr (STAGE) {
-                if (c + 1 < nchunks) {
-                    store_chunk(role, (c + 1) % kRing, st_next);
-                    if (c + 3 < nchunks) {
-                        load_chunk(role, rows_next, st_next);
-                        if (c + 4 < nchunks) read_rows(role, c + 4, rows_next);
-                    }
-                }
+            sync_lds();  // barrier c
+            if (c + 1 < nchunks) {
+                store_chunk((c + 1) % kRing, st_next);
+                if (c + 3 < nchunks) load_chunk(c + 3, st_next);
             }
-            work(c);
+            if (c >= 2) pv_chunk(c - 2);
         };
         int c = 1;
-        for (; c + 1 < nchunks; c += 2) {
-            step(c, stA);      // stores chunk c+1 (even), loads c+3 (even)
-            step(c + 1, stB);  // stores chunk c+2 (odd), loads c+4 (odd)
+        for (; c + 1 <= nchunks; c += 2) {
+            step(c, stA);                    // stores chunk c+1 (even), loads c+3 (even)
+            if (c + 1 <= nchunks) step(c + 1, stB);
         }
-        if (c < nchunks) step(c, stA);
-        sync_lds();
-        last();
+        if (c <= nchunks) step(c, stA);
+        sync_lds();  // barrier nchunks + 1
+        pv_chunk(nchunks - 1);
+    };
+    auto qk_pipeline = [&](auto&& first_loads, auto&& qk_chunk, auto&& qk_and_softmax, auto&& softmax_only)
+                           __attribute__((always_inline)) {
+        if (nchunks == 0) return;
+        first_loads();
+        sync_lds();  // barrier 0
+        qk_chunk(0);
+        for (int c = 1; c < nchunks; ++c) {
+            sync_lds();  // barrier c
+            qk_and_softmax(c);
+        }
+        sync_lds();  // barrier nchunks
+        softmax_only(nchunks - 1);
+        sync_lds();  // barrier nchunks + 1
     };
 
     // Softmax without rescaling.  Each head's probabilities are taken
@@ -393,7 +375,6 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
             read_batch(0, ka[0]);
 #pragma unroll
             for (int bt = 0; bt < NBATCH; ++bt) {
-                issue_fence();
                 if (bt + 1 < NBATCH) read_batch(bt + 1, ka[(bt + 1) & 1]);
 #pragma unroll
                 for (int kk = 0; kk < NB; ++kk) {
@@ -402,7 +383,6 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                     for (int ht = 0; ht < 2; ++ht) s.v[ht][pt] = mfma_bf16(ka[bt & 1][kk], qf[ht][ks], s.v[ht][pt]);
                 }
             }
-            issue_fence();
             return s;
         };
         // softmax of the chunk for heads hl0 + 16ht + j, local to the wave.
@@ -445,10 +425,15 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         };
 
         for (;;) {
-            pipeline(std::integral_constant<int, 0>{}, [&]() __attribute__((always_inline)) { load_q(); },
-                     [&]() __attribute__((always_inline)) { softmax(qk(tile[0]), 0); },
-                     [&](int c) __attribute__((always_inline)) { softmax(qk(tile[c % kRing]), c); },
-                     [&]() __attribute__((always_inline)) {});
+            S4 s_prev;  // S of the previous chunk, its softmax pending
+            qk_pipeline([&]() __attribute__((always_inline)) { load_q(); },
+                        [&](int c) __attribute__((always_inline)) { s_prev = qk(tile[c % kRing]); },
+                        [&](int c) __attribute__((always_inline)) {
+                            const S4 s_cur = qk(tile[c % kRing]);  // independent of the softmax below
+                            softmax(s_prev, c - 1);
+                            s_prev = s_cur;
+                        },
+                        [&](int c) __attribute__((always_inline)) { softmax(s_prev, c); });
             if (overflow == 0) break;  // read by every wave after the pipeline's last barrier
             __syncthreads();           // every wave has read the flag
             if (tid == 0) overflow = 0;
@@ -524,11 +509,9 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
             issue_fence();
         };
 
+        load_row_ids();
         for (;;) {
-            pipeline(std::integral_constant<int, 1>{}, [&]() __attribute__((always_inline)) {},
-                     [&]() __attribute__((always_inline)) {},
-                     [&](int c) __attribute__((always_inline)) { pv(tile[(c - 1) % kRing], c - 1); },
-                     [&]() __attribute__((always_inline)) { pv(tile[(nchunks - 1) % kRing], nchunks - 1); });
+            pv_pipeline([&](int c) __attribute__((always_inline)) { pv(tile[c % kRing], c); });
             if (overflow == 0) break;
             __syncthreads();  // every wave has read the flag; the work item is computed again
 #pragma unroll
