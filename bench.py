@@ -242,29 +242,37 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)",
           file=sys.stderr, flush=True)
 
-    # per-stage durations: the same kernels through the three unfused calls,
-    # HIP events recorded on the launch stream between them
+    # per-stage durations: the same kernels through the three unfused calls.
+    # Each stage runs K times back to back (input sets rotating) between two
+    # HIP events on the launch stream, so an event's own cost is spread over K
+    # launches.  Before each loop the GPU spins (~0.25 ms per launch) so that
+    # the host has queued every call before the first one runs.
     acc = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * args.steps)]
     scores = [torch.empty((s[0].rows, max(1, s[0].max_seq_len)), dtype=torch.float32, device="cuda")
               for s in sets]
     attn_ws = [torch.empty(max(1, B.dsa_sparse_attn_workspace_bytes(s[1])), dtype=torch.uint8, device="cuda")
                for s in sets]
-    for i in range(args.steps):
-        _, dev, _, idx = sets[i % nsets]
-        sc = scores[i % nsets]
-        ev[4 * i].record(stream)
-        B.dsa_indexer_scores(dev, sc, stream=stream)
-        ev[4 * i + 1].record(stream)
-        B.dsa_topk(dev, sc, indices=idx, stream=stream)
-        ev[4 * i + 2].record(stream)
-        B.dsa_sparse_attn(dev, idx, ws=attn_ws[i % nsets], stream=stream)
-        ev[4 * i + 3].record(stream)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        acc["indexer"] += ev[4 * i].elapsed_time(ev[4 * i + 1])
-        acc["topk"] += ev[4 * i + 1].elapsed_time(ev[4 * i + 2])
-        acc["attention"] += ev[4 * i + 2].elapsed_time(ev[4 * i + 3])
+    for i in range(nsets):  # every set's scores and indices, for the loops below
+        _, dev, _, idx = sets[i]
+        B.dsa_indexer_scores(dev, scores[i], stream=stream)
+        B.dsa_topk(dev, scores[i], indices=idx, stream=stream)
+    calls = {
+        "indexer": lambda i: B.dsa_indexer_scores(sets[i % nsets][1], scores[i % nsets], stream=stream),
+        "topk": lambda i: B.dsa_topk(sets[i % nsets][1], scores[i % nsets], indices=sets[i % nsets][3],
+                                     stream=stream),
+        "attention": lambda i: B.dsa_sparse_attn(sets[i % nsets][1], sets[i % nsets][3], ws=attn_ws[i % nsets],
+                                                 stream=stream),
+    }
+    for name, call in calls.items():
+        torch.cuda.synchronize()
+        torch.cuda._sleep(600_000 * args.steps)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for i in range(args.steps):
+            call(i)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        acc[name] = s0.elapsed_time(s1)
     stage_us = {k: v / args.steps * 1e3 for k, v in acc.items()}
     algo = algorithmic(wl0)
     dom = max(stage_us, key=stage_us.get)

@@ -14,7 +14,7 @@
 //   0. the split's index slots are validated (0 <= s < L_r, block present)
 //      and compacted in order into LDS as pool-row numbers;
 //   1. per chunk of 32 positions the latent rows are gathered through
-//      registers into a 3-tile LDS ring (16-byte units XOR-swizzled by row so
+//      registers into a 4-tile LDS ring (16-byte units XOR-swizzled by row so
 //      the MFMA operand reads are bank-conflict free).  An MXFP8 cache is
 //      dequantized (e4m3 * 2^(e8m0-127), exact in bf16) on the way in;
 //   2. S^T = K . Q^T on MFMA with Q held in registers for the whole kernel;

@@ -7,11 +7,18 @@
 // is ascending, padded with -1.
 //
 // Method: scores map to order-preserving 32-bit keys (-0.0 folded into
-// +0.0); an MSB-first radix select with 8-bit digits and LDS histograms
-// finds the k-th largest key T and how many keys equal to T are needed;
-// one ordered pass then keeps every key > T and the first needed keys == T,
-// using wave ballots for the in-order ranks.  One workgroup per row; rows are
-// visited longest-first when the grid is larger than the GPU.
+// +0.0); an MSB-first radix select with LDS histograms finds the k-th
+// largest key T and how many keys equal to T are needed; every key > T and
+// the first needed keys == T are kept, in position order.  One workgroup per
+// row; rows are visited longest-first when the grid is larger than the GPU.
+// Three forms:
+//   * rows up to 32768 positions: the keys stay in registers (8, 16 or 32
+//     per thread of a 1024-thread workgroup), three digit passes;
+//   * longer rows: a top_k per 16384-position segment into a candidate
+//     workspace, then the same register-resident selection over the
+//     candidates;
+//   * otherwise (no workspace): the keys are re-read from memory in four
+//     8-bit passes.
 #include "common.hpp"
 #include "kernels.hpp"
 
