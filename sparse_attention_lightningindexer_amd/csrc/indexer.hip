@@ -111,11 +111,20 @@ __device__ __forceinline__ void load_row_query(const uint8_t* q, const float* q_
 
 // ReLU-weighted sum over the 64 heads of one 16-position N-tile: lane holds
 // D[head 16*mt + 4g + i][pos j]; returns the full sum for position j.
+// max(x, 0) as one signed-integer max on the bits: negative floats (and -0)
+// are negative integers.  A float max would also quiet NaNs first (two
+// instructions); here a NaN with the sign bit clear passes through.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ __forceinline__ float head_weighted_relu_sum(const f32x4 (&acc)[4], const float (&wr)[4][4]) {
-    float v = 0.f;
-    for (int mt = 0; mt < 4; ++mt)
-        for (int i = 0; i < 4; ++i) v = fmaf(wr[mt][i], fmaxf(acc[mt][i], 0.f), v);
-    return sum_over_groups(v);
+    float v[4];  // four independent partial sums (one per M-tile), then a tree
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        v[mt] = wr[mt][0] * relu(acc[mt][0]);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) v[mt] = fmaf(wr[mt][i], relu(acc[mt][i]), v[mt]);
+    }
+    return sum_over_groups((v[0] + v[1]) + (v[2] + v[3]));
 }
 
 // Decode: a sequence's n_q <= NQ rows share every K tile.  Each wave owns TPW
@@ -263,12 +272,28 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
     // gathers issued per tile by this wave: K units (+ the scale line, wave 0, fp8)
     const int per_tile = (TILE_K - wave + 7) / 8 + ((T::SCALED && wave == 0) ? 1 : 0);
 
+    // Vector-memory operations this wave has issued (uniform), so that the wait
+    // for a tile counts exactly the operations issued after its gathers.
+    int issued = 0;
+    // Raw block-table entries of tiles 64m .. 64m+63, gathered by each wave
+    // into its own LDS window (clamped columns; validated when used).  Window
+    // m+1 is gathered when tile 64m is staged, 64 tiles before it is needed;
+    // the tile waits cover it, since operations complete in order.
+    __shared__ int tabw[8][2][kWave];
+    auto tab_fetch = [&](int m) __attribute__((always_inline)) {
+        const int j_ = min(kWave * m + lane, max_blocks - 1);
+        lds_gather4(table + (int64_t)b * max_blocks + j_, lds_addr(&tabw[wave][m & 1][0]));
+        ++issued;
+    };
+
     // Gather tile t into ring slot `buf`: unit U of the tile (row U/UNITS, column
     // U%UNITS) receives global column (U%UNITS) ^ (row % UNITS), an XOR swizzle
     // that keeps the column reads below bank-conflict free.  Absent blocks read
     // block 0 and are flagged; their scores are -inf.
-    auto stage = [&](int t, int buf) {
-        int64_t p = phys_block(table, max_blocks, b, __builtin_amdgcn_readfirstlane(t), num_blocks);
+    auto stage = [&](int t, int buf) __attribute__((always_inline)) {
+        if ((t & 63) == 0) tab_fetch((t >> 6) + 1);
+        int64_t p = tabw[wave][(t >> 6) & 1][t & 63];
+        if (t >= max_blocks || p < 0 || p >= num_blocks) p = -1;  // absent block
         if (threadIdx.x == 0) tile_ok[buf] = p >= 0;
         if (p < 0) p = 0;
         const uint8_t* base = kpool + p * TILE_BYTES;
@@ -281,6 +306,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
         if constexpr (T::SCALED) {
             if (wave == 0) lds_gather4(kscale + p * kBlock + lane, lds_addr(&kst[buf][0]));
         }
+        issued += per_tile;
     };
 
     for (int pass = 0; pass < npass; ++pass) {
@@ -301,45 +327,101 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
         // it places no wait for them inside the tile loop)
         __builtin_amdgcn_s_waitcnt(0x0f70);
 
-        for (int t = 0; t < kIdxRing - 1 && t < ntiles; ++t) stage(t, t);
+        if (ntiles > 0) {
+            tab_fetch(0);
+            wait_vmcnt<0>();
+        }
+        // mark0..2: `issued` right after the gathers of tiles t, t+1, t+2
+        int mark0 = issued, mark1 = issued, mark2 = issued;
+        static_assert(kIdxRing == 4, "three tiles are in flight ahead of the one scored");
+        if (ntiles > 0) { stage(0, 0); mark0 = issued; }
+        if (ntiles > 1) { stage(1, 1); mark1 = issued; }
+        if (ntiles > 2) { stage(2, 2); mark2 = issued; }
         for (int t = 0; t < ntiles; ++t) {
             const int buf = t % kIdxRing;
-            wait_vmcnt(per_tile * min(kIdxRing - 2, ntiles - 1 - t));  // tile t has landed
+            wait_vmcnt(issued - mark0);  // tile t has landed (operations complete in order)
             sync_lds();  // ... for every wave; slot (t-1) % 4 is free
             if (t + kIdxRing - 1 < ntiles) stage(t + kIdxRing - 1, (t + kIdxRing - 1) % kIdxRing);
+            mark0 = mark1;
+            mark1 = mark2;
+            mark2 = issued;
             const int s0 = t * kBlock;
             const bool ok = tile_ok[buf] != 0;
             if (s0 < Lr[0] || s0 < Lr[1]) {
-                for (int nt = 0; nt < 4; ++nt) {
-                    typename T::frag kf[T::KSTEPS];
+                // eight steps k = (N-tile k/2, row k%2): 16 MFMAs, then the
+                // ReLU-weighted head sum (VALU).  A wave's own MFMAs and VALU
+                // work do not overlap; waves w and w+4 share a SIMD, and waves
+                // 4..7 run each step's sum one step late, so that one wave's
+                // sum runs under the other's MFMAs.  MFMA steps run at raised
+                // wave priority, so the matrix core is fed first.
+                typename T::frag kf[2][T::KSTEPS];
+                auto read_k = [&](int nt, typename T::frag (&f)[T::KSTEPS]) __attribute__((always_inline)) {
                     const int prow = 16 * nt + j;
                     const uint8_t* rowp = &ktile[buf][prow * T::ROW];
+#pragma unroll
                     for (int ks = 0; ks < T::KSTEPS; ++ks) {
                         if constexpr (T::FB == 16) {
                             const int u = (4 * ks + g) ^ (prow % UNITS);
-                            kf[ks] = *reinterpret_cast<const bf16x8*>(rowp + u * 16);
+                            f[ks] = *reinterpret_cast<const bf16x8*>(rowp + u * 16);
                         } else {
                             const int u0 = (2 * g) ^ (prow % UNITS), u1 = (2 * g + 1) ^ (prow % UNITS);
                             const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + u0 * 16);
                             const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + u1 * 16);
-                            kf[ks] = typename T::frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                            f[ks] = typename T::frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                         }
                     }
-                    const float ksc = T::SCALED ? kst[buf][prow] : 1.f;
-                    for (int qi = 0; qi < 2; ++qi) {
-                        if (s0 >= Lr[qi]) continue;
-                        f32x4 acc[4];
-                        for (int mt = 0; mt < 4; ++mt) {
-                            acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                            for (int ks = 0; ks < T::KSTEPS; ++ks) acc[mt] = mma(qa[qi][mt][ks], kf[ks], acc[mt]);
-                        }
-                        float v = head_weighted_relu_sum(acc, wr[qi]);
-                        if constexpr (T::SCALED) v *= ksc;
-                        if (!ok) v = -INFINITY;
-                        const int s = s0 + prow;
-                        const int64_t row = (int64_t)b * n_q + rb * 16 + wave * 2 + qi;
-                        if (g == 0 && s < Lr[qi]) scores[row * ld + s] = v;
+                };
+                auto mfma_step = [&](int k, f32x4 (&acc)[4]) __attribute__((always_inline)) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_setprio(2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int nt = k >> 1, qi = k & 1;
+                    if (qi == 0) read_k(nt, kf[nt & 1]);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < T::KSTEPS; ++ks) acc[mt] = mma(qa[qi][mt][ks], kf[nt & 1][ks], acc[mt]);
                     }
+                };
+                // the sum of step k reaches all four lane groups; lane 16g + j
+                // keeps N-tile g's, which is position 16g + j
+                float sel0 = 0.f, sel1 = 0.f;
+                auto sum_step = [&](int k, const f32x4 (&acc)[4]) __attribute__((always_inline)) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_setprio(0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const float v = head_weighted_relu_sum(acc, wr[k & 1]);
+                    if (k & 1)
+                        sel1 = g == (k >> 1) ? v : sel1;
+                    else
+                        sel0 = g == (k >> 1) ? v : sel0;
+                };
+                f32x4 acc[2][4];
+                if (wave < 4) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        mfma_step(k, acc[0]);
+                        sum_step(k, acc[0]);
+                    }
+                } else {
+                    mfma_step(0, acc[0]);
+#pragma unroll
+                    for (int k = 1; k < 8; ++k) {
+                        mfma_step(k, acc[k & 1]);
+                        sum_step(k - 1, acc[(k - 1) & 1]);
+                    }
+                    sum_step(7, acc[1]);
+                }
+                // one 256-byte store per row: lane l scores position s0 + l
+#pragma unroll
+                for (int qi = 0; qi < 2; ++qi) {
+                    float v = qi ? sel1 : sel0;
+                    if constexpr (T::SCALED) v *= kst[buf][lane];
+                    if (!ok) v = -INFINITY;
+                    const int64_t row = (int64_t)b * n_q + rb * 16 + wave * 2 + qi;
+                    if (s0 + lane < Lr[qi]) scores[row * ld + s0 + lane] = v;
+                    issued += s0 < Lr[qi];  // the store issues when lane 0 is active
                 }
             }
         }

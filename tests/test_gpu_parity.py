@@ -197,6 +197,28 @@ def test_full_size_sampled_rows(cfg):
     check_attention(wl, f64(out[rows]), f64(lse[rows]), ref_o, ref_l, f"full cfg {cfg}")
 
 
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_prefill_permuted_paging_across_table_windows(cfg):
+    # 4500 causal rows: the prefill indexer kernel reads the block table in
+    # windows of 64 tiles (4096 positions), so rows past 4096 use the second
+    # window; permuted paging makes every window entry matter.  cfg 5 runs the
+    # same rows with the fp8 indexer and the MXFP8 cache.
+    wl = make_workload(cfg, batch=1, n_q=4500, lens=4500, top_k=256, paging="permuted", poison=True)
+    dev = B.DeviceInputs(wl)
+    say(f"[parity] prefill across table windows, cfg {cfg}: forward on GPU")
+    out, lse, idx = B.dsa_forward(dev)
+    sc = B.dsa_indexer_scores(dev)
+    torch.cuda.synchronize()
+    rows = [0, 63, 64, 4095, 4096, 4160, 4499]
+    sc_h = sc[rows].cpu().numpy().astype(np.float64)
+    idx_h = idx.cpu().numpy()
+    ref_sc = O.indexer_scores(wl, rows, ld=sc.shape[1])
+    check_scores(wl, sc_h, ref_sc, rows)
+    check_indices_exact(idx_h[rows], O.topk(sc_h, wl.row_lens()[rows], wl.top_k))
+    ref_o, ref_l = O.sparse_attn(wl, idx_h, rows)
+    check_attention(wl, f64(out[rows]), f64(lse[rows]), ref_o, ref_l, f"prefill windows cfg {cfg}")
+
+
 def test_full_prefill_sampled_rows():
     say("[parity] full prefill: generating 32768 x 128 x 576 queries")
     wl = make_workload(3)
