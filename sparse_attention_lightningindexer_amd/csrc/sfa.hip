@@ -76,31 +76,35 @@ __device__ __forceinline__ void dequant_unit(i32x4 codes, float scale, i32x4& lo
 // of one row are consecutive on one XCD, so the two halves' gathers of the
 // same latent rows meet in that XCD's L2.
 //
-// Workgroup: 4 waves, one per SIMD (the whole register file each), 64 heads,
-// in two roles.  Per chunk of 32 positions:
-//   QK   waves 0, 1 own heads 32w .. 32w+31 of the half over all 32 positions:
-//        S^T = K . Q^T with Q^T resident in registers, each K fragment read
-//        from LDS feeding two MFMAs; the row maxima and the softmax of the
-//        chunk are local to the wave, which writes bf16 P[head][pos] to LDS;
-//   PV   waves 2, 3 own value channels 256(w-2) .. +255 for all 64 heads:
+// Workgroup: 8 waves, two per SIMD (waves w and w+4 share SIMD w), 64 heads,
+// in two roles.  A wave's own MFMAs and vector-ALU work do not overlap on this
+// chip, but the MFMAs of one wave and the ALU work of the other wave on the
+// same SIMD do; each SIMD therefore holds one wave of each role.  Per chunk of
+// 32 positions:
+//   QK   waves 0..3 own heads 16w .. 16w+15 of the half over all 32 positions:
+//        S^T = K . Q^T with Q^T resident in registers; the row maxima and the
+//        softmax of the chunk are local to the wave, which writes bf16
+//        P[head][pos] to LDS;
+//   PV   waves 4..7 own value channels 128(w-4) .. +127 for all 64 heads:
 //        O^T[d][h] += V^T . P^T, each V^T fragment (transposing LDS read)
-//        feeding 4 MFMAs and each P^T fragment 16.
-// The QK waves run one chunk ahead: in iteration c they issue the MFMAs of
-// QK(c) together with the softmax of chunk c-1 (independent work, so the
-// matrix core and the vector ALU overlap), while the PV waves compute
-// PV(c-2).  One barrier per chunk hands P over.  Latent rows are gathered
-// through registers by the PV waves (loaded two chunks ahead of their store,
-// stored one chunk ahead of their QK); each PV wave keeps the pool rows of its
-// 16 chunk rows for every chunk in registers (row r in register r, chunk c in
-// lane c).  LDS (one workgroup per CU): 4 x 36 KiB tiles + P 10 KiB; the slot
-// list of the compaction lives in the fourth tile until the gathers start.
-constexpr int kWaves = 4, kThreads = kWaves * kWave;
+//        feeding 4 MFMAs and each P^T fragment 8;
+//   all  eight waves gather the chunk's latent rows through registers, four
+//        rows each (row r of wave w in register r, chunk c in lane c).
+// The QK waves run one chunk ahead: in iteration c they compute QK(c) and the
+// softmax of chunk c-1, while the PV waves compute PV(c-2).  One barrier per
+// chunk hands tiles and P over.  Chunks are loaded two iterations before they
+// are stored and stored one iteration before their QK.  LDS (one workgroup
+// per CU): 4 x 36 KiB tiles + P 10 KiB; the slot list of the compaction lives
+// in the fourth tile until the gathers start.
+constexpr int kWaves = 8, kThreads = kWaves * kWave;
 constexpr int kHalf = kH / 2;                   // heads per workgroup
-constexpr int kQkHeads = kHalf / 2;             // 32 heads per QK wave
-constexpr int kDvPerPv = kDv / 2;               // 256 value channels = 16 D-tiles per PV wave
+constexpr int kRoleWaves = kWaves / 2;          // waves per role
+constexpr int kQkHeads = kHalf / kRoleWaves;    // 16 heads per QK wave
+constexpr int kDvPerPv = kDv / kRoleWaves;      // 128 value channels = 8 D-tiles per PV wave
 constexpr int kRing = 4;                        // bf16 tiles resident in LDS
 constexpr int kPRow = kCh * 2 + 16;             // bytes per head row of P (64 + 16 pad)
 constexpr int kMxUnitsRow = kDqk / 16;          // 36 16-code units per MXFP8 row
+constexpr int kStRows = kCh / kWaves;           // chunk rows gathered per wave
 
 // two floats -> two bfloat16 (round to nearest even) packed in 32 bits
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -188,57 +192,49 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     if (tid == 0) overflow = 0;
     __syncthreads();
 
-    // 1. Staging, by the PV waves (sw = w - 2 owns chunk rows 16sw .. 16sw+15).
-    //    bf16: each row's 512 latent channels are one 64-lane x 16-byte load
-    //    from a row base in scalar registers; the rope units 64 + lane%8 of
-    //    rows 16sw + lane/8 + 8k (k = 0, 1) follow as two loads.  MXFP8: unit
-    //    U = 64i + lane of the wave's 16 rows x 36 units (row U/36, 16 codes
-    //    U%36) with its E8M0 scale byte, dequantized (exact) to two bf16 units
-    //    when stored.  Rows are stored at their XOR-swizzled places.
-    constexpr int kStRows = kCh / 2;                           // 16 rows per PV wave
-    constexpr int kMxPer = kStRows * kMxUnitsRow / kWave;      // 9 MXFP8 units per lane
-    constexpr int kStN = MX ? kMxPer : kStRows + 2;
-    const int sw = wave & 1;  // index of the wave within its role
-    const int srow0 = kStRows * sw;
+    // 1. Staging, by every wave: wave w owns chunk rows 4w .. 4w+3.  bf16: each
+    //    row's 512 latent channels are one 64-lane x 16-byte load from a row
+    //    base in scalar registers; the rope units 64 + lane%8 of the four rows
+    //    follow as one load (lanes 32..63 repeat lanes 0..31).  MXFP8: unit
+    //    U = 64i + lane of the wave's 4 rows x 36 units (row U/36, 16 codes
+    //    U%36; the third load's lanes past unit 143 repeat it) with its E8M0
+    //    scale byte, dequantized (exact) to two bf16 units when stored.  Rows
+    //    are stored at their XOR-swizzled places.
+    constexpr int kMxPer = (kStRows * kMxUnitsRow + kWave - 1) / kWave;  // 3 MXFP8 loads per chunk
+    constexpr int kStN = MX ? kMxPer : kStRows + 1;
+    const int srow0 = kStRows * wave;
     struct Stage {
         i32x4 v[kStN];
         uint32_t sc[MX ? kMxPer : 1];
     };
     int vid[kStRows];  // pool row of chunk row srow0 + r of chunk c, in lane c
-    auto load_row_ids = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < kStRows; ++r) vid[r] = lane < nchunks ? prow[lane * kCh + srow0 + r] : 0;
-    };
+    for (int r = 0; r < kStRows; ++r) vid[r] = lane < nchunks ? prow[lane * kCh + srow0 + r] : 0;
     // pool row of chunk row srow0 + r of chunk c (wave-uniform)
     auto sid = [&](int c, int r) __attribute__((always_inline)) -> int {
         return __builtin_amdgcn_readlane(vid[r], c);
     };
+    const int rope_r = (lane & 31) >> 3;  // the row of the lane's rope unit
     auto load_chunk = [&](int c, Stage& st) __attribute__((always_inline)) {
-        if constexpr (!MX) {
-            int rid[kStRows];
+        int rid[kStRows];
 #pragma unroll
-            for (int r = 0; r < kStRows; ++r) rid[r] = sid(c, r);
+        for (int r = 0; r < kStRows; ++r) rid[r] = sid(c, r);
+        if constexpr (!MX) {
 #pragma unroll
             for (int r = 0; r < kStRows; ++r)
                 st.v[r] = *reinterpret_cast<const i32x4*>(kv + (int64_t)rid[r] * kRowB + lane * 16);
+            int id = rid[0];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                int id = rid[8 * k];
-#pragma unroll
-                for (int m = 1; m < 8; ++m) id = (lane >> 3) == m ? rid[8 * k + m] : id;
-                st.v[kStRows + k] = *reinterpret_cast<const i32x4*>(kv + (int64_t)id * kRowB + 16 * (64 + (lane & 7)));
-            }
+            for (int m = 1; m < kStRows; ++m) id = rope_r == m ? rid[m] : id;
+            st.v[kStRows] = *reinterpret_cast<const i32x4*>(kv + (int64_t)id * kRowB + 16 * (64 + (lane & 7)));
         } else {
 #pragma unroll
             for (int i = 0; i < kMxPer; ++i) {
-                const int U = kWave * i + lane;
+                const int U = min(kWave * i + lane, kStRows * kMxUnitsRow - 1);
                 const int r = U / kMxUnitsRow, u = U - r * kMxUnitsRow;
-                constexpr int dummy = 0;
-                (void)dummy;
-                const int r0 = (kWave * i) / kMxUnitsRow;  // the instruction's rows are r0 .. r0+2
-                int id = sid(c, r0);
-                if (r0 + 1 < kStRows) id = r == r0 + 1 ? sid(c, r0 + 1) : id;
-                if (r0 + 2 < kStRows) id = r == r0 + 2 ? sid(c, r0 + 2) : id;
+                int id = rid[0];
+#pragma unroll
+                for (int m = 1; m < kStRows; ++m) id = r == m ? rid[m] : id;
                 st.v[i] = *reinterpret_cast<const i32x4*>(kv + (int64_t)id * kDqk + u * 16);
                 st.sc[i] = kvscale[(int64_t)id * (kDqk / 32) + (u >> 1)];
             }
@@ -251,15 +247,11 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
 #pragma unroll
             for (int r = 0; r < kStRows; ++r)
                 *reinterpret_cast<i32x4*>(Tw + r * kRowB + ((lane ^ row_swz(srow0 + r)) << 4)) = st.v[r];
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int row = srow0 + (lane >> 3) + 8 * k;
-                *reinterpret_cast<i32x4*>(T + lds_unit(row, 64 + (lane & 7))) = st.v[kStRows + k];
-            }
+            *reinterpret_cast<i32x4*>(T + lds_unit(srow0 + rope_r, 64 + (lane & 7))) = st.v[kStRows];
         } else {
 #pragma unroll
             for (int i = 0; i < kMxPer; ++i) {
-                const int U = kWave * i + lane;
+                const int U = min(kWave * i + lane, kStRows * kMxUnitsRow - 1);
                 const int r = U / kMxUnitsRow, u = U - r * kMxUnitsRow;
                 i32x4 lo, hi;
                 dequant_unit(st.v[i], e8m0_to_f32(st.sc[i]), lo, hi);
@@ -269,54 +261,40 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         }
     };
 
-    // The chunk pipeline: chunk c lives in tile c % 4.  Chunk k is loaded into
-    // registers in iteration k-3 and stored into its tile in iteration k-1
-    // (tile k % 4 was last read by PV(k-4) in iteration k-2).  Iteration c
-    // (after its barrier): chunk c is in LDS and P(c-2) is written; the QK
-    // waves run QK(c) with softmax(c-1), the PV waves stage and run PV(c-2).
-    // Both roles execute the same nchunks + 2 barriers.
-    auto pv_pipeline = [&](auto&& pv_chunk) __attribute__((always_inline)) {
+    // The chunk pipeline, run by both roles: chunk c lives in tile c % 4.
+    // Chunk k is loaded into registers in iteration k-3 (k < 3: before the
+    // first barrier) and stored into its tile in iteration k-1 (tile k % 4 was
+    // last read by PV(k-4) in iteration k-2).  Iteration c (c = 0 .. nchunks,
+    // after its barrier): chunk c is in LDS and P(c-2) is written; work(c) is
+    // QK(c) with softmax(c-1) in the QK waves and PV(c-2) in the PV waves.
+    // Both roles execute the same nchunks + 2 barriers; after the last one the
+    // PV waves compute PV(nchunks-1) (tail()).
+    auto pipeline = [&](auto&& early_loads, auto&& work, auto&& tail) __attribute__((always_inline)) {
         if (nchunks == 0) return;
         Stage stA, stB;  // chunk k is staged in stA (k even) or stB (k odd)
         load_chunk(0, stA);
         if (nchunks > 1) load_chunk(1, stB);
+        early_loads();
         store_chunk(0, stA);
         if (nchunks > 2) load_chunk(2, stA);
-        sync_lds();  // barrier 0
-        if (nchunks > 1) {
-            store_chunk(1, stB);
-            if (nchunks > 3) load_chunk(3, stB);
-        }
-        auto step = [&](int c, Stage& st_next) __attribute__((always_inline)) {
+        // st holds chunk c+1 and receives chunk c+3
+        auto step = [&](int c, Stage& st) __attribute__((always_inline)) {
             sync_lds();  // barrier c
             if (c + 1 < nchunks) {
-                store_chunk((c + 1) % kRing, st_next);
-                if (c + 3 < nchunks) load_chunk(c + 3, st_next);
+                store_chunk((c + 1) % kRing, st);
+                if (c + 3 < nchunks) load_chunk(c + 3, st);
             }
-            if (c >= 2) pv_chunk(c - 2);
+            work(c);
         };
+        step(0, stB);
         int c = 1;
         for (; c + 1 <= nchunks; c += 2) {
-            step(c, stA);                    // stores chunk c+1 (even), loads c+3 (even)
-            if (c + 1 <= nchunks) step(c + 1, stB);
+            step(c, stA);  // stores chunk c+1 (even), loads c+3 (even)
+            step(c + 1, stB);
         }
         if (c <= nchunks) step(c, stA);
         sync_lds();  // barrier nchunks + 1
-        pv_chunk(nchunks - 1);
-    };
-    auto qk_pipeline = [&](auto&& first_loads, auto&& qk_chunk, auto&& qk_and_softmax, auto&& softmax_only)
-                           __attribute__((always_inline)) {
-        if (nchunks == 0) return;
-        first_loads();
-        sync_lds();  // barrier 0
-        qk_chunk(0);
-        for (int c = 1; c < nchunks; ++c) {
-            sync_lds();  // barrier c
-            qk_and_softmax(c);
-        }
-        sync_lds();  // barrier nchunks
-        softmax_only(nchunks - 1);
-        sync_lds();  // barrier nchunks + 1
+        tail();
     };
 
     // Softmax without rescaling.  Each head's probabilities are taken
@@ -326,37 +304,32 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     // overflow); if one does, the whole work item is computed again with the
     // exact maximum, observed on the way, as the reference.  The result is the
     // same softmax either way (reference and denominator cancel).
-    if (wave < 2) {
+    if (wave < kRoleWaves) {
         // ---------------------------------------------------------- QK role
-        // heads hl0 .. hl0+31 of the half.  qf[ht][ks] holds
-        // q[hb + hl0 + 16ht + j][32ks + 8g .. +8] (the B operand of S^T = K . Q^T).
+        // heads hl0 .. hl0+15 of the half.  qf[ks] holds
+        // q[hb + hl0 + j][32ks + 8g .. +8] (the B operand of S^T = K . Q^T).
         const int hl0 = kQkHeads * wave;
-        bf16x8 qf[2][kDqk / 32];
+        bf16x8 qf[kDqk / 32];
         auto load_q = [&]() __attribute__((always_inline)) {
+            const uint16_t* qrow = q + ((int64_t)row * kH + hb + hl0 + j) * kDqk + 8 * g;
 #pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
-                const uint16_t* qrow = q + ((int64_t)row * kH + hb + hl0 + 16 * ht + j) * kDqk + 8 * g;
-#pragma unroll
-                for (int ks = 0; ks < kDqk / 32; ++ks)
-                    qf[ht][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-            }
+            for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
         };
-        // per head hl0 + 16ht + j (identical in the four lane groups): the
-        // reference, the largest scaled logit seen, and the denominator
-        float m_ref[2] = {-INFINITY, -INFINITY}, m_obs[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+        // per head hl0 + j (identical in the four lane groups): the reference,
+        // the largest scaled logit seen, and the denominator
+        float m_ref = -INFINITY, m_obs = -INFINITY, l_run = 0.f;
         bool exact = false;  // the reference is the exact maximum (second pass)
+        bool have_q = false;
 
-        // S for 32 heads x 32 positions: lane holds S[head hl0 + 16ht + j][pos
-        // 16pt + 4g + i] in s[ht][pt][i].  K fragment (pt, ks): row 16pt + j,
-        // unit 4ks + g; each feeds the MFMAs of both head tiles.  Reads run
-        // one batch of 6 fragments ahead of the MFMAs that consume them.
-        struct S4 { f32x4 v[2][2]; };
-        auto qk = [&](const uint8_t* T) __attribute__((always_inline)) -> S4 {
-            S4 s;
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) s.v[ht][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // S for 16 heads x 32 positions: lane holds S[head hl0 + j][pos 16pt +
+        // 4g + i] in s[pt][i].  K fragment (pt, ks): row 16pt + j, unit 4ks + g.
+        // Reads run one batch of 6 fragments ahead of the MFMAs that consume
+        // them.
+        struct S2 { f32x4 v[2]; };
+        auto qk = [&](const uint8_t* T) __attribute__((always_inline)) -> S2 {
+            S2 s;
+            s.v[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+            s.v[1] = f32x4{0.f, 0.f, 0.f, 0.f};
             constexpr int NB = 6, NBATCH = 2 * (kDqk / 32) / NB;  // 6 batches of 6 fragments
             // unit 4ks + g of row r sits at 16 * ((4(ks&1) + g) ^ swz(r)) + 128 (ks>>1);
             // rows j and 16 + j share swz, so two base addresses and immediate
@@ -379,85 +352,83 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
 #pragma unroll
                 for (int kk = 0; kk < NB; ++kk) {
                     const int f = bt * NB + kk, pt = f & 1, ks = f >> 1;
-#pragma unroll
-                    for (int ht = 0; ht < 2; ++ht) s.v[ht][pt] = mfma_bf16(ka[bt & 1][kk], qf[ht][ks], s.v[ht][pt]);
+                    s.v[pt] = mfma_bf16(ka[bt & 1][kk], qf[ks], s.v[pt]);
                 }
             }
             return s;
         };
-        // softmax of the chunk for heads hl0 + 16ht + j, local to the wave.
-        // Positions past the valid ones are -inf; exp2 of -inf is 0.
-        auto softmax = [&](const S4& s, int c) __attribute__((always_inline)) {
+        // softmax of the chunk for head hl0 + j, local to the wave.  Positions
+        // past the valid ones are -inf; exp2 of -inf is 0.
+        auto softmax = [&](const S2& s, int c) __attribute__((always_inline)) {
             const int lim = n_valid - c * kCh - 4 * g;  // position 16pt + 4g + i is valid iff 16pt + i < lim
-            bool over = false;
+            float sm[2][4];
+            float cmax = -INFINITY;
 #pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
-                float sm[2][4];
-                float cmax = -INFINITY;
+            for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-                for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        sm[pt][i] = 16 * pt + i < lim ? s.v[ht][pt][i] : -INFINITY;
-                        cmax = fmaxf(cmax, sm[pt][i]);
-                    }
-                cmax = max_over_groups(cmax) * scale_log2;  // scale_log2 > 0
-                if (!exact && c == 0) m_ref[ht] = cmax;
-                m_obs[ht] = fmaxf(m_obs[ht], cmax);
-                over |= cmax > m_ref[ht] + kSlack;          // also a reference of -inf
-                const float mneg = m_ref[ht] == -INFINITY ? 0.f : -m_ref[ht];
-                float psum = 0.f;
-                const int hl = hl0 + 16 * ht + j;
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
-                    float p[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        p[i] = __builtin_amdgcn_exp2f(fmaf(sm[pt][i], scale_log2, mneg));
-                        psum += p[i];  // fp32 denominator
-                    }
-                    *reinterpret_cast<uint2*>(pbuf[c & 1] + hl * kPRow + 2 * (16 * pt + 4 * g)) =
-                        make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+                for (int i = 0; i < 4; ++i) {
+                    sm[pt][i] = 16 * pt + i < lim ? s.v[pt][i] : -INFINITY;
+                    cmax = fmaxf(cmax, sm[pt][i]);
                 }
-                l_run[ht] += sum_over_groups(psum);
+            cmax = max_over_groups(cmax) * scale_log2;  // scale_log2 > 0
+            if (!exact && c == 0) m_ref = cmax;
+            m_obs = fmaxf(m_obs, cmax);
+            const bool over = cmax > m_ref + kSlack;     // also a reference of -inf
+            const float mneg = m_ref == -INFINITY ? 0.f : -m_ref;
+            float psum = 0.f;
+            const int hl = hl0 + j;
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = __builtin_amdgcn_exp2f(fmaf(sm[pt][i], scale_log2, mneg));
+                    psum += p[i];  // fp32 denominator
+                }
+                *reinterpret_cast<uint2*>(pbuf[c & 1] + hl * kPRow + 2 * (16 * pt + 4 * g)) =
+                    make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
             }
+            l_run += sum_over_groups(psum);
             if (ballot(over) != 0ull && lane == 0) overflow = 1;
         };
 
         for (;;) {
-            S4 s_prev;  // S of the previous chunk, its softmax pending
-            qk_pipeline([&]() __attribute__((always_inline)) { load_q(); },
-                        [&](int c) __attribute__((always_inline)) { s_prev = qk(tile[c % kRing]); },
-                        [&](int c) __attribute__((always_inline)) {
-                            const S4 s_cur = qk(tile[c % kRing]);  // independent of the softmax below
-                            softmax(s_prev, c - 1);
-                            s_prev = s_cur;
-                        },
-                        [&](int c) __attribute__((always_inline)) { softmax(s_prev, c); });
+            S2 s_prev;  // S of the previous chunk, its softmax pending
+            pipeline(
+                [&]() __attribute__((always_inline)) {
+                    if (!have_q) load_q();
+                    have_q = true;
+                },
+                [&](int c) __attribute__((always_inline)) {
+                    if (c == 0) {
+                        s_prev = qk(tile[0]);
+                    } else if (c < nchunks) {
+                        const S2 s_cur = qk(tile[c % kRing]);  // independent of the softmax below
+                        softmax(s_prev, c - 1);
+                        s_prev = s_cur;
+                    } else {
+                        softmax(s_prev, c - 1);
+                    }
+                },
+                []() __attribute__((always_inline)) {});
             if (overflow == 0) break;  // read by every wave after the pipeline's last barrier
             __syncthreads();           // every wave has read the flag
             if (tid == 0) overflow = 0;
             exact = true;
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
-                m_ref[ht] = m_obs[ht];
-                l_run[ht] = 0.f;
-            }
+            m_ref = m_obs;
+            l_run = 0.f;
         }
         if (g == 0) {
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
-                l_s[hl0 + 16 * ht + j] = l_run[ht];
-                m_s[hl0 + 16 * ht + j] = m_ref[ht];
-            }
+            l_s[hl0 + j] = l_run;
+            m_s[hl0 + j] = m_ref;
         }
         __syncthreads();  // l and m are in LDS
         __syncthreads();  // the PV waves' results are in LDS
     } else {
         // ---------------------------------------------------------- PV role
-        // value channels 256pw + 16dt + 4g + i for the half's 64 heads:
-        // o[dt][ht] holds O^T[256pw + 16dt + 4g + i][head hb + 16ht + j].
-        const int pw = wave - 2;
+        // value channels 128pw + 16dt + 4g + i for the half's 64 heads:
+        // o[dt][ht] holds O^T[128pw + 16dt + 4g + i][head hb + 16ht + j].
+        const int pw = wave - kRoleWaves;
         f32x4 o[kDvPerPv / 16][kHalf / 16];
 #pragma unroll
         for (int dt = 0; dt < kDvPerPv / 16; ++dt)
@@ -465,11 +436,11 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
             for (int ht = 0; ht < kHalf / 16; ++ht) o[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // V^T fragment (d-tile dt): lane j of group g addresses row 8g + 4h +
-        // j/4, channels 256pw + 16dt + 4(j%4) (two transposing reads give
+        // j/4, channels 128pw + 16dt + 4(j%4) (two transposing reads give
         // positions 8g .. 8g+7 in order); P^T fragment: lane reads P[head
-        // 16ht + j][pos 8g .. 8g+7].  Channel 256pw + 16dt + 4(j%4) is unit
-        // 32pw + 2dt + (j%4)/2, byte 8((j%4)&1); d-tiles 4 apart differ by one
-        // 128-byte step, so four bases per row and immediates cover all 16.
+        // 16ht + j][pos 8g .. 8g+7].  Channel 128pw + 16dt + 4(j%4) is unit
+        // 16pw + 2dt + (j%4)/2, byte 8((j%4)&1); d-tiles 4 apart differ by one
+        // 128-byte step, so four bases per row and immediates cover all 8.
         auto pv = [&](const uint8_t* T, int c) __attribute__((always_inline)) {
             bf16x8 pf[kHalf / 16];
 #pragma unroll
@@ -478,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
             const int e_ = j >> 2, q4 = j & 3;
             const int r0 = 8 * g + e_, r1 = 8 * g + 4 + e_;
             auto vaddr = [&](int r_, int dd) __attribute__((always_inline)) -> const uint8_t* {
-                const int unit = 32 * pw + 2 * dd + (q4 >> 1);
+                const int unit = 16 * pw + 2 * dd + (q4 >> 1);
                 return T + r_ * kRowB + ((unit ^ row_swz(r_)) << 4) + 8 * (q4 & 1);
             };
             constexpr int NBT = 2;  // d-tiles per batch
@@ -509,9 +480,12 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
             issue_fence();
         };
 
-        load_row_ids();
         for (;;) {
-            pv_pipeline([&](int c) __attribute__((always_inline)) { pv(tile[c % kRing], c); });
+            pipeline([]() __attribute__((always_inline)) {},
+                     [&](int c) __attribute__((always_inline)) {
+                         if (c >= 2) pv(tile[(c - 2) % kRing], c - 2);
+                     },
+                     [&]() __attribute__((always_inline)) { pv(tile[(nchunks - 1) % kRing], nchunks - 1); });
             if (overflow == 0) break;
             __syncthreads();  // every wave has read the flag; the work item is computed again
 #pragma unroll
