@@ -150,47 +150,57 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     // 0. ordered compaction of the valid index slots into pool-row numbers.
     //    All of the split's indices are loaded first, then all of their table
     //    entries (two memory round trips in total), then compacted.
-    constexpr int kSlotIters = kAttnMaxSplitSlots / kThreads;
-    int pr_[kSlotIters];
-    {
-        // reads are unconditional (clamped to in-range slots and blocks) so
-        // that each round trip is one batch of loads
-        int sv[kSlotIters];
+    //    Run by both roles (the QK waves first issue their query loads, which
+    //    then arrive during the compaction); it ends with a barrier, after
+    //    which every wave loads the pool rows of its chunk rows (vid).
+    const int srow0 = kStRows * wave;  // the wave's first chunk row (staging, below)
+    int n_valid = 0, nchunks = 0;
+    int vid[kStRows];  // pool row of chunk row srow0 + r of chunk c, in lane c
+    auto compact = [&]() __attribute__((always_inline)) {
+        constexpr int kSlotIters = kAttnMaxSplitSlots / kThreads;
+        int pr_[kSlotIters];
+        {
+            // reads are unconditional (clamped to in-range slots and blocks) so
+            // that each round trip is one batch of loads
+            int sv[kSlotIters];
+#pragma unroll
+            for (int k = 0; k < kSlotIters; ++k) {
+                const int t = slot0 + kThreads * k + tid;
+                const int v = indices[(int64_t)row * top_k + min(t, top_k - 1)];
+                sv[k] = t < slot1 && v >= 0 && v < L ? v : -1;
+            }
+#pragma unroll
+            for (int k = 0; k < kSlotIters; ++k) {
+                const int sk = sv[k];
+                const int64_t p = phys_block(table, max_blocks, b, sk < 0 ? 0 : sk / kBlock, num_blocks);
+                pr_[k] = (sk >= 0 && p >= 0) ? (int)(p * kBlock + (sk % kBlock)) : -1;
+            }
+        }
+        n_valid = 0;
 #pragma unroll
         for (int k = 0; k < kSlotIters; ++k) {
-            const int t = slot0 + kThreads * k + tid;
-            const int v = indices[(int64_t)row * top_k + min(t, top_k - 1)];
-            sv[k] = t < slot1 && v >= 0 && v < L ? v : -1;
+            if (slot0 + kThreads * k >= slot1) break;  // workgroup-uniform
+            const int pr = pr_[k];
+            const uint64_t m = ballot(pr >= 0);
+            if (lane == 0) wave_cnt[wave] = __popcll(m);
+            __syncthreads();
+            int before = 0, tot = 0;
+            for (int w = 0; w < kWaves; ++w) {
+                before += w < wave ? wave_cnt[w] : 0;
+                tot += wave_cnt[w];
+            }
+            if (pr >= 0) prow[n_valid + before + lanes_below(m)] = pr;
+            n_valid += tot;
+            __syncthreads();
         }
-#pragma unroll
-        for (int k = 0; k < kSlotIters; ++k) {
-            const int sk = sv[k];
-            const int64_t p = phys_block(table, max_blocks, b, sk < 0 ? 0 : sk / kBlock, num_blocks);
-            pr_[k] = (sk >= 0 && p >= 0) ? (int)(p * kBlock + (sk % kBlock)) : -1;
-        }
-    }
-    int n_valid = 0;
-#pragma unroll
-    for (int k = 0; k < kSlotIters; ++k) {
-        if (slot0 + kThreads * k >= slot1) break;  // workgroup-uniform
-        const int pr = pr_[k];
-        const uint64_t m = ballot(pr >= 0);
-        if (lane == 0) wave_cnt[wave] = __popcll(m);
+        nchunks = (n_valid + kCh - 1) / kCh;
+        // pad the last chunk with a valid row, so every chunk row names real data
+        if (tid < nchunks * kCh - n_valid) prow[n_valid + tid] = prow[0];
+        if (tid == 0) overflow = 0;
         __syncthreads();
-        int before = 0, tot = 0;
-        for (int w = 0; w < kWaves; ++w) {
-            before += w < wave ? wave_cnt[w] : 0;
-            tot += wave_cnt[w];
-        }
-        if (pr >= 0) prow[n_valid + before + lanes_below(m)] = pr;
-        n_valid += tot;
-        __syncthreads();
-    }
-    const int nchunks = (n_valid + kCh - 1) / kCh;
-    // pad the last chunk with a valid row, so every chunk row names real data
-    if (tid < nchunks * kCh - n_valid) prow[n_valid + tid] = prow[0];
-    if (tid == 0) overflow = 0;
-    __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kStRows; ++r) vid[r] = lane < nchunks ? prow[lane * kCh + srow0 + r] : 0;
+    };
 
     // 1. Staging, by every wave: wave w owns chunk rows 4w .. 4w+3.  bf16: each
     //    row's 512 latent channels are one 64-lane x 16-byte load from a row
@@ -202,14 +212,10 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     //    are stored at their XOR-swizzled places.
     constexpr int kMxPer = (kStRows * kMxUnitsRow + kWave - 1) / kWave;  // 3 MXFP8 loads per chunk
     constexpr int kStN = MX ? kMxPer : kStRows + 1;
-    const int srow0 = kStRows * wave;
     struct Stage {
         i32x4 v[kStN];
         uint32_t sc[MX ? kMxPer : 1];
     };
-    int vid[kStRows];  // pool row of chunk row srow0 + r of chunk c, in lane c
-#pragma unroll
-    for (int r = 0; r < kStRows; ++r) vid[r] = lane < nchunks ? prow[lane * kCh + srow0 + r] : 0;
     // pool row of chunk row srow0 + r of chunk c (wave-uniform)
     auto sid = [&](int c, int r) __attribute__((always_inline)) -> int {
         return __builtin_amdgcn_readlane(vid[r], c);
@@ -269,12 +275,11 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     // QK(c) with softmax(c-1) in the QK waves and PV(c-2) in the PV waves.
     // Both roles execute the same nchunks + 2 barriers; after the last one the
     // PV waves compute PV(nchunks-1) (tail()).
-    auto pipeline = [&](auto&& early_loads, auto&& work, auto&& tail) __attribute__((always_inline)) {
+    auto pipeline = [&](auto&& work, auto&& tail) __attribute__((always_inline)) {
         if (nchunks == 0) return;
         Stage stA, stB;  // chunk k is staged in stA (k even) or stB (k odd)
         load_chunk(0, stA);
         if (nchunks > 1) load_chunk(1, stB);
-        early_loads();
         store_chunk(0, stA);
         if (nchunks > 2) load_chunk(2, stA);
         // st holds chunk c+1 and receives chunk c+3
@@ -310,16 +315,16 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         // q[hb + hl0 + j][32ks + 8g .. +8] (the B operand of S^T = K . Q^T).
         const int hl0 = kQkHeads * wave;
         bf16x8 qf[kDqk / 32];
-        auto load_q = [&]() __attribute__((always_inline)) {
+        {
             const uint16_t* qrow = q + ((int64_t)row * kH + hb + hl0 + j) * kDqk + 8 * g;
 #pragma unroll
             for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-        };
+        }
+        compact();
         // per head hl0 + j (identical in the four lane groups): the reference,
         // the largest scaled logit seen, and the denominator
         float m_ref = -INFINITY, m_obs = -INFINITY, l_run = 0.f;
         bool exact = false;  // the reference is the exact maximum (second pass)
-        bool have_q = false;
 
         // S for 16 heads x 32 positions: lane holds S[head hl0 + j][pos 16pt +
         // 4g + i] in s[pt][i].  K fragment (pt, ks): row 16pt + j, unit 4ks + g.
@@ -395,10 +400,6 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         for (;;) {
             S2 s_prev;  // S of the previous chunk, its softmax pending
             pipeline(
-                [&]() __attribute__((always_inline)) {
-                    if (!have_q) load_q();
-                    have_q = true;
-                },
                 [&](int c) __attribute__((always_inline)) {
                     if (c == 0) {
                         s_prev = qk(tile[0]);
@@ -429,6 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         // value channels 128pw + 16dt + 4g + i for the half's 64 heads:
         // o[dt][ht] holds O^T[128pw + 16dt + 4g + i][head hb + 16ht + j].
         const int pw = wave - kRoleWaves;
+        compact();
         f32x4 o[kDvPerPv / 16][kHalf / 16];
 #pragma unroll
         for (int dt = 0; dt < kDvPerPv / 16; ++dt)
@@ -481,8 +483,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         };
 
         for (;;) {
-            pipeline([]() __attribute__((always_inline)) {},
-                     [&](int c) __attribute__((always_inline)) {
+            pipeline([&](int c) __attribute__((always_inline)) {
                          if (c >= 2) pv(tile[(c - 2) % kRing], c - 2);
                      },
                      [&]() __attribute__((always_inline)) { pv(tile[(nchunks - 1) % kRing], nchunks - 1); });
@@ -547,6 +548,9 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const uint16_t* __rest
     const int row = blockIdx.x;
     const int h = 4 * blockIdx.y + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (h >= H) return;
+    // the splits' LSEs, then (for the common split counts) all partial rows are
+    // loaded before any is used, so the loads issue back to back
+    constexpr int kBatch = 8;
     float M = -INFINITY;
     for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_lse[((int64_t)row * splits + s) * H + h]);
     float W = 0.f;
@@ -557,16 +561,24 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const uint16_t* __rest
     const float inv = W > 0.f ? 1.f / W : 0.f;
     for (int d = 8 * lane; d < Dv; d += 8 * 64) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits; ++s) {
-            const float ls = ws_lse[((int64_t)row * splits + s) * H + h];
-            if (M == -INFINITY || ls == -INFINITY) continue;
-            const float wgt = expf(ls - M);
-            const uint4 v = *reinterpret_cast<const uint4*>(ws_o + (((int64_t)row * splits + s) * H + h) * Dv + d);
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        for (int s0 = 0; s0 < splits; s0 += kBatch) {
+            uint4 v[kBatch];
+            float wgt[kBatch];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] = fmaf(wgt, __uint_as_float(w4[i] << 16), acc[2 * i]);
-                acc[2 * i + 1] = fmaf(wgt, __uint_as_float(w4[i] & 0xffff0000u), acc[2 * i + 1]);
+            for (int k = 0; k < kBatch; ++k) {
+                const int s = min(s0 + k, splits - 1);  // in range; weight 0 past the last split
+                const float ls = ws_lse[((int64_t)row * splits + s) * H + h];
+                wgt[k] = (s0 + k >= splits || M == -INFINITY || ls == -INFINITY) ? 0.f : expf(ls - M);
+                v[k] = *reinterpret_cast<const uint4*>(ws_o + (((int64_t)row * splits + s) * H + h) * Dv + d);
+            }
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] = fmaf(wgt[k], __uint_as_float(w4[i] << 16), acc[2 * i]);
+                    acc[2 * i + 1] = fmaf(wgt[k], __uint_as_float(w4[i] & 0xffff0000u), acc[2 * i + 1]);
+                }
             }
         }
         uint16_t* o = out + ((int64_t)row * H + h) * Dv + d;
