@@ -548,9 +548,10 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const uint16_t* __rest
     const int row = blockIdx.x;
     const int h = 4 * blockIdx.y + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (h >= H) return;
-    // the splits' LSEs, then (for the common split counts) all partial rows are
-    // loaded before any is used, so the loads issue back to back
-    constexpr int kBatch = 8;
+    // the splits' LSEs, then the partial rows four splits at a time (the
+    // decode split count), each group loaded before any of it is used, so
+    // the loads issue back to back
+    constexpr int kBatch = 4;
     float M = -INFINITY;
     for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_lse[((int64_t)row * splits + s) * H + h]);
     float W = 0.f;
