@@ -42,9 +42,12 @@
  *    padding, is skipped; a row with nothing to attend outputs zeros and
  *    lse = -inf.  A failed launch returns DSA_ERR_HIP.  Nothing prints.
  *  - Supported shapes (anything else returns DSA_ERR_UNSUPPORTED):
- *      indexer  BF16 or E4M3(+fp32 scale per 128): n_heads 64, head_dim 128
+ *      indexer  BF16, E4M3 + fp32 scale per 128, or MXFP8 (E4M3 + E8M0 per
+ *               32): n_heads 64, head_dim 128
  *               F32: n_heads <= 16, head_dim <= 128
- *      attention BF16 q, BF16 or MXFP8 (E4M3 + E8M0 per 32) KV:
+ *      attention BF16 q, and BF16, MXFP8 (E4M3 + E8M0 per 32) or E4M3 with
+ *               an fp32 scale per 128 (groups 0..4 of a 576 row; the
+ *               last covers the 64 rope channels) KV:
  *               n_heads 128, d_qk 576, d_v 512
  *               F32 q and KV: n_heads <= 16, d_qk <= 128, d_v <= d_qk
  *      block_size 64, 1 <= top_k <= 4096, n_q <= 8 unless n_q == L_b
@@ -86,7 +89,9 @@ typedef enum {
  * MLA latent KV pool ([D] §2.2: KV compressed into a low-rank latent row
  * per position, shared by all heads).  For quantized pools ([A] §5
  * "Layered Quantization") `scales` holds [num_blocks][block_size]
- * [width/group] factors; the element value is value(code) * factor. */
+ * [ceil(width/group)] factors; the element value is value(code) * factor,
+ * element c using factor c/group (a last, shorter group when group does not
+ * divide width). */
 typedef struct {
     const void* data;           /* device, see above                               */
     const void* scales;         /* device, fp32 or E8M0 bytes; NULL when NONE      */
@@ -114,7 +119,8 @@ typedef struct {
 typedef struct {
     const void* q;              /* device [rows][n_heads][head_dim] in dtype       */
     dsa_dtype dtype;            /* F32, BF16 or E4M3; k.dtype must match           */
-    const float* q_scale;       /* device [rows][n_heads*head_dim/128] for E4M3    */
+    const void* q_scale;        /* device, E4M3 only, same kind and group as k:    */
+                                /*   [rows][n_heads][head_dim/group] fp32 or E8M0  */
     int32_t n_heads;            /* H_I                                             */
     int32_t head_dim;           /* d_I                                             */
     const float* head_w;        /* device [rows][n_heads] fp32                     */

@@ -108,10 +108,13 @@ static double load_scale(const void* scales, int kind, int64_t idx) {
 }
 
 /* Dequantize one vector of `width` elements that starts at element `row*width`
- * of `data`; groups of `group` elements share scale number row*(width/group)+g. */
+ * of `data`; element c belongs to group c/group, and the row's groups share
+ * scales number row*ngroups + c/group, ngroups = ceil(width/group) (a last,
+ * shorter group when group does not divide width, as for the 576-wide
+ * latent row in groups of 128). */
 static void dequant_row(const void* data, int dtype, const void* scales, int scale_kind,
                         int group, int width, int64_t row, double* out) {
-    int ngroups = (scale_kind == ORC_SCALE_NONE || group <= 0) ? 0 : width / group;
+    int ngroups = (scale_kind == ORC_SCALE_NONE || group <= 0) ? 0 : (width + group - 1) / group;
     for (int c = 0; c < width; ++c) {
         double v = load_elem(data, dtype, row * (int64_t)width + c);
         if (ngroups > 0) v *= load_scale(scales, scale_kind, row * (int64_t)ngroups + c / group);
@@ -158,17 +161,18 @@ static int64_t pool_row(const orc_batch* B, int b, int s) {
  * rows == NULL).  Output row i of `scores` (leading dimension ld) holds
  * I[rows[i], s] for s < L_r and NaN beyond.
  *  q_idx   [rows_total, H_I, d_I] in q_dtype; q_scale [rows_total, H_I, d_I/q_group]
+ *          of kind q_kind (fp32 factors or E8M0 bytes)
  *  head_w  [rows_total, H_I] fp32
- *  k_pool  [num_blocks*block_size, d_I] in k_dtype; k_scale [.., d_I/k_group] */
+ *  k_pool  [num_blocks*block_size, d_I] in k_dtype; k_scale [.., d_I/k_group] of kind k_kind */
 int oracle_indexer_scores(int batch, int n_q, const int32_t* seq_lens, const int32_t* block_table,
                           int max_blocks, int block_size, int64_t num_blocks,
-                          const void* q_idx, int q_dtype, const float* q_scale, int q_group,
+                          const void* q_idx, int q_dtype, const void* q_scale, int q_kind, int q_group,
                           int n_idx_heads, int d_idx, const float* head_w,
-                          const void* k_pool, int k_dtype, const float* k_scale, int k_group,
+                          const void* k_pool, int k_dtype, const void* k_scale, int k_kind, int k_group,
                           const int32_t* rows, int n_rows, double* scores, int64_t ld) {
     orc_batch B = {batch, n_q, seq_lens, block_table, max_blocks, block_size, num_blocks};
-    int q_kind = q_scale ? ORC_SCALE_F32 : ORC_SCALE_NONE;
-    int k_kind = k_scale ? ORC_SCALE_F32 : ORC_SCALE_NONE;
+    if (q_scale == NULL) q_kind = ORC_SCALE_NONE;
+    if (k_scale == NULL) k_kind = ORC_SCALE_NONE;
     if (rows == NULL) n_rows = batch * n_q;
     #pragma omp parallel for schedule(dynamic, 1)
     for (int i = 0; i < n_rows; ++i) {

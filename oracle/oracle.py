@@ -14,8 +14,11 @@ import numpy as np
 
 from . import build as _build
 
-_DT = {"f32": 0, "bf16": 1, "e4m3": 2, "mxfp8": 2}
+_DT = {"f32": 0, "bf16": 1, "e4m3": 2, "mxfp8": 2, "e4m3_128": 2}
 _SCALE_NONE, _SCALE_F32, _SCALE_E8M0 = 0, 1, 2
+#: storage format -> (scale kind, elements per scale)
+_SCALES = {"f32": (_SCALE_NONE, 0), "bf16": (_SCALE_NONE, 0), "e4m3": (_SCALE_F32, 128),
+           "e4m3_128": (_SCALE_F32, 128), "mxfp8": (_SCALE_E8M0, 32)}
 _lib = None
 
 
@@ -34,8 +37,8 @@ def lib():
         L.oracle_e8m0_to_f64.argtypes = [C.c_uint8]
         L.oracle_dequant.argtypes = [p, i32, p, i32, i32, i32, i64, p]
         L.oracle_indexer_scores.argtypes = [i32, i32, p, p, i32, i32, i64,
-                                            p, i32, p, i32, i32, i32, p,
-                                            p, i32, p, i32, p, i32, p, i64]
+                                            p, i32, p, i32, i32, i32, i32, p,
+                                            p, i32, p, i32, i32, p, i32, p, i64]
         L.oracle_topk.argtypes = [i32, p, p, i64, i32, p]
         attn = [i32, i32, p, p, i32, i32, i64, p, i32, i32, i32, i32, p, i32, p, i32, i32]
         L.oracle_sparse_attn.argtypes = attn + [p, i32, d, p, i32, p, p]
@@ -98,10 +101,11 @@ def indexer_scores(wl, rows=None, ld=None):
     seq, tab = _c(wl.seq_lens, np.int32), _c(wl.block_table, np.int32)
     qi, kp, hw = _c(wl.q_idx), _c(wl.k_pool), _c(wl.head_w, np.float32)
     qs, ks = _c(wl.q_idx_scale), _c(wl.k_scale)
+    kind, grp = _SCALES[wl.idx_dtype]
     lib().oracle_indexer_scores(wl.batch, wl.n_q, _ptr(seq), _ptr(tab), wl.max_blocks, 64,
-                                wl.num_blocks, _ptr(qi), _DT[wl.idx_dtype], _ptr(qs), 128,
+                                wl.num_blocks, _ptr(qi), _DT[wl.idx_dtype], _ptr(qs), kind, grp,
                                 wl.H_I, wl.d_I, _ptr(hw), _ptr(kp), _DT[wl.idx_dtype], _ptr(ks),
-                                128, _ptr(r), n, _ptr(out), out.shape[1])
+                                kind, grp, _ptr(r), n, _ptr(out), out.shape[1])
     return out
 
 
@@ -115,8 +119,8 @@ def topk(scores, row_len, top_k: int):
 
 
 def _kv_args(wl):
-    kind = _SCALE_E8M0 if wl.kv_dtype == "mxfp8" else _SCALE_NONE
-    return _c(wl.kv_pool), _DT[wl.kv_dtype], _c(wl.kv_scale), kind, 32
+    kind, grp = _SCALES[wl.kv_dtype]
+    return _c(wl.kv_pool), _DT[wl.kv_dtype], _c(wl.kv_scale), kind, grp
 
 
 def sparse_attn(wl, indices, rows=None, top_k=None):

@@ -114,7 +114,11 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
-_DT = {"f32": DSA_F32, "bf16": DSA_BF16, "e4m3": DSA_E4M3, "mxfp8": DSA_E4M3}
+_DT = {"f32": DSA_F32, "bf16": DSA_BF16, "e4m3": DSA_E4M3, "mxfp8": DSA_E4M3, "e4m3_128": DSA_E4M3}
+#: storage format name -> (element dtype, scale kind, elements per scale)
+_FMT = {"f32": (DSA_F32, DSA_SCALE_NONE, 0), "bf16": (DSA_BF16, DSA_SCALE_NONE, 0),
+        "e4m3": (DSA_E4M3, DSA_SCALE_F32, 128), "e4m3_128": (DSA_E4M3, DSA_SCALE_F32, 128),
+        "mxfp8": (DSA_E4M3, DSA_SCALE_E8M0, 32)}
 
 
 def _dev(a, device):
@@ -151,17 +155,17 @@ class DeviceInputs:
         self.batch = dsa_batch(wl.batch, wl.n_q, self.seq_lens.data_ptr() if wl.batch else None,
                                self.block_table.data_ptr() if wl.batch else None, wl.max_blocks, 64,
                                wl.max_seq_len)
-        idx_scaled = wl.idx_dtype == "e4m3"
+        idt, ikind, igroup = _FMT[wl.idx_dtype]
+        idx_scaled = ikind != DSA_SCALE_NONE
         kcache = dsa_cache(self.k_pool.data_ptr(), self.k_scale.data_ptr() if idx_scaled else None,
-                           _DT[wl.idx_dtype], DSA_SCALE_F32 if idx_scaled else DSA_SCALE_NONE,
-                           128 if idx_scaled else 0, wl.d_I, wl.num_blocks)
-        self.idx = dsa_indexer_args(self.q_idx.data_ptr(), _DT[wl.idx_dtype],
+                           idt, ikind, igroup, wl.d_I, wl.num_blocks)
+        self.idx = dsa_indexer_args(self.q_idx.data_ptr(), idt,
                                     self.q_idx_scale.data_ptr() if idx_scaled else None, wl.H_I, wl.d_I,
                                     self.head_w.data_ptr(), kcache)
-        mx = wl.kv_dtype == "mxfp8"
-        kvcache = dsa_cache(self.kv_pool.data_ptr(), self.kv_scale.data_ptr() if mx else None,
-                            _DT[wl.kv_dtype], DSA_SCALE_E8M0 if mx else DSA_SCALE_NONE, 32 if mx else 0,
-                            wl.d_qk, wl.num_blocks)
+        kdt, kkind, kgroup = _FMT[wl.kv_dtype]
+        kv_scaled = kkind != DSA_SCALE_NONE
+        kvcache = dsa_cache(self.kv_pool.data_ptr(), self.kv_scale.data_ptr() if kv_scaled else None,
+                            kdt, kkind, kgroup, wl.d_qk, wl.num_blocks)
         self.attn = dsa_attn_args(self.q.data_ptr(), _DT[wl.q_dtype], wl.H, wl.d_v, float(wl.sm_scale),
                                   kvcache, self.out.data_ptr(), self.lse.data_ptr())
 

@@ -5,8 +5,11 @@
 //   v_mfma_f32_16x16x32_bf16   A: lane holds A[j][8g + 0..7], B: B[8g + 0..7][j],
 //                              D: lane holds D[4g + 0..3][j]
 //   v_mfma_f32_16x16x32_fp8    same as bf16 with 8 e4m3 bytes per lane (OCP e4m3)
-//   v_mfma_scale_f32_16x16x128_f8f6f4 (fp8 operands, unit scales):
-//                              A: lane holds A[j][32g + 0..31], B: B[32g + 0..31][j]
+//   v_mfma_scale_f32_16x16x128_f8f6f4 (fp8 operands): bytes 0..15 of a lane are
+//                              A[j][16g + 0..15] / B[16g + 0..15][j], bytes 16..31
+//                              A[j][64 + 16g + 0..15] / B[64 + 16g + 0..15][j]; the
+//                              E8M0 scale byte of lane 16b + j applies to k-block b
+//                              (k = 32b .. 32b+31) of row j of A / column j of B
 //   ds_read_b64_tr_b16         in each 16-lane group, lane j's element e is the
 //                              16-bit word (j % 4) at the address given by lane
 //                              4e + j/4 of that group.
@@ -77,6 +80,10 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 // 16x16x128 e4m3 x e4m3 with unit (E8M0 = 127) block scales.
 __device__ __forceinline__ f32x4 mfma_fp8_k128(i32x8 a, i32x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// The same with this lane's E8M0 block scales for A and B (layout above).
+__device__ __forceinline__ f32x4 mfma_mx_k128(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
 // Number of lanes below this one whose bit is set in `mask`.

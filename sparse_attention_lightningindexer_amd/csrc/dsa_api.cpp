@@ -50,9 +50,11 @@ dsa_status check_indexer(const dsa_batch* b, const dsa_indexer_args* a) {
         if (a->n_heads != 64 || a->head_dim != 128) return DSA_ERR_UNSUPPORTED;
         if (a->k.scale_kind != DSA_SCALE_NONE) return DSA_ERR_UNSUPPORTED;
         return DSA_OK;
-    case DSA_E4M3:
+    case DSA_E4M3:  // fp32 per 128 (one per head vector) or MXFP8 (E8M0 per 32)
         if (a->n_heads != 64 || a->head_dim != 128) return DSA_ERR_UNSUPPORTED;
-        if (a->k.scale_kind != DSA_SCALE_F32 || a->k.group != 128) return DSA_ERR_UNSUPPORTED;
+        if (!((a->k.scale_kind == DSA_SCALE_F32 && a->k.group == 128) ||
+              (a->k.scale_kind == DSA_SCALE_E8M0 && a->k.group == 32)))
+            return DSA_ERR_UNSUPPORTED;
         if (a->k.scales == nullptr || (b->batch > 0 && a->q_scale == nullptr)) return DSA_ERR_NULL;
         return DSA_OK;
     default:
@@ -75,19 +77,20 @@ dsa_status check_attn(const dsa_batch* b, const dsa_attn_args* a) {
     if (a->dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
     if (a->n_heads != 128 || a->kv.width != 576 || a->d_v != 512) return DSA_ERR_UNSUPPORTED;
     if (a->kv.dtype == DSA_BF16 && a->kv.scale_kind == DSA_SCALE_NONE) return DSA_OK;
-    if (a->kv.dtype == DSA_E4M3 && a->kv.scale_kind == DSA_SCALE_E8M0 && a->kv.group == 32)
+    if (a->kv.dtype == DSA_E4M3 && ((a->kv.scale_kind == DSA_SCALE_E8M0 && a->kv.group == 32) ||
+                                    (a->kv.scale_kind == DSA_SCALE_F32 && a->kv.group == 128)))
         return a->kv.scales == nullptr ? DSA_ERR_NULL : DSA_OK;
     return DSA_ERR_UNSUPPORTED;
 }
 
 dsa::IndexerLaunch indexer_launch(const dsa_batch* b, const dsa_indexer_args* a, float* scores, int64_t ld) {
     dsa::IndexerLaunch L{};
-    L.dtype = a->dtype == DSA_F32 ? 0 : (a->dtype == DSA_BF16 ? 1 : 2);
+    L.dtype = a->dtype == DSA_F32 ? 0 : a->dtype == DSA_BF16 ? 1 : a->k.scale_kind == DSA_SCALE_E8M0 ? 3 : 2;
     L.q = a->q;
     L.q_scale = a->q_scale;
     L.w = a->head_w;
     L.kpool = a->k.data;
-    L.kscale = (const float*)a->k.scales;
+    L.kscale = a->k.scales;
     L.seq_lens = b->seq_lens;
     L.table = b->block_table;
     L.max_blocks = b->max_blocks;
@@ -106,10 +109,13 @@ dsa::AttnLaunch attn_launch(const dsa_batch* b, const dsa_attn_args* a, const in
                             float* ws) {
     dsa::AttnLaunch L{};
     L.q_dtype = a->dtype == DSA_F32 ? 0 : 1;
-    L.kv_kind = a->kv.dtype == DSA_F32 ? 0 : (a->kv.dtype == DSA_BF16 ? 1 : 2);
+    L.kv_kind = a->kv.dtype == DSA_F32    ? 0
+                : a->kv.dtype == DSA_BF16 ? 1
+                : a->kv.scale_kind == DSA_SCALE_E8M0 ? 2
+                                                      : 3;
     L.q = a->q;
     L.kv = a->kv.data;
-    L.kvscale = (const uint8_t*)a->kv.scales;
+    L.kvscale = a->kv.scales;
     L.seq_lens = b->seq_lens;
     L.table = b->block_table;
     L.max_blocks = b->max_blocks;

@@ -59,45 +59,71 @@ struct IdxBf16 {
     static constexpr int FB = 16;         // fragment bytes per lane
     static constexpr int ROW = 256;       // bytes per 128-wide vector
     static constexpr bool SCALED = false;
+    static constexpr bool MX = false;
 };
-struct IdxFp8 {
+struct IdxFp8 {  // e4m3 with one fp32 scale per 128-element vector, applied after the MFMA
     using frag = i32x8;
     static constexpr int KSTEPS = 1;      // 1 x K=128
     static constexpr int FB = 32;
     static constexpr int ROW = 128;
     static constexpr bool SCALED = true;
+    static constexpr bool MX = false;
+};
+struct IdxMx {   // MXFP8: e4m3 with one E8M0 scale per 32 elements, applied inside the MFMA
+    using frag = i32x8;
+    static constexpr int KSTEPS = 1;
+    static constexpr int FB = 32;
+    static constexpr int ROW = 128;
+    static constexpr bool SCALED = false;
+    static constexpr bool MX = true;
 };
 
-__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) { return mfma_bf16(a, b, c); }
-__device__ __forceinline__ f32x4 mma(i32x8 a, i32x8 b, f32x4 c) { return mfma_fp8_k128(a, b, c); }
+// sa, sb: this lane's E8M0 block scales of A and B (MXFP8 only).
+template <class T>
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c, int, int) { return mfma_bf16(a, b, c); }
+template <class T>
+__device__ __forceinline__ f32x4 mma(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
+    if constexpr (T::MX) return mfma_mx_k128(a, b, c, sa, sb);
+    else return mfma_fp8_k128(a, b, c);
+}
 
 constexpr int kIdxHeads = 64;  // 4 M-tiles of 16 heads
 
-// Lane's fragment of vector `vec` (ROW bytes each) for k-step ks: FB bytes at
-// ks*4*FB + g*FB -- i.e. elements [K*ks + (K/4)*g, +K/4) of the vector.
+// Lane's fragment of vector `vec` (ROW bytes each) for k-step ks.  bf16: 16
+// bytes at 64ks + 16g, elements [32ks + 8g, +8).  fp8: elements [16g, +16) and
+// [64 + 16g, +16), the operand order of the scaled 16x16x128 MFMA.
 template <class T>
 __device__ __forceinline__ typename T::frag load_frag(const uint8_t* vec, int ks, int g) {
-    return *reinterpret_cast<const typename T::frag*>(vec + ks * 4 * T::FB + g * T::FB);
+    if constexpr (T::FB == 16) {
+        return *reinterpret_cast<const typename T::frag*>(vec + ks * 4 * T::FB + g * T::FB);
+    } else {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(vec + 16 * g);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(vec + 64 + 16 * g);
+        return typename T::frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
 }
 
 // Query fragments and head weights of one row.  Loads are unconditional
 // (a row past the end reads row 0 and is zeroed afterwards), so they issue
 // back to back.
+// MXFP8: qs[mt] is this lane's E8M0 scale of head 16mt + j, k-block g.
 template <class T>
-__device__ __forceinline__ void load_row_query(const uint8_t* q, const float* q_scale, const float* w,
+__device__ __forceinline__ void load_row_query(const uint8_t* q, const void* q_scale, const float* w,
                                                int64_t row, bool valid, int g, int j,
-                                               typename T::frag (&qa)[4][T::KSTEPS], float (&wr)[4][4]) {
+                                               typename T::frag (&qa)[4][T::KSTEPS], float (&wr)[4][4],
+                                               int (&qs)[4]) {
     const int64_t rr = valid ? row : 0;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const uint8_t* v = q + ((rr * kIdxHeads) + 16 * mt + j) * (int64_t)T::ROW;
 #pragma unroll
         for (int ks = 0; ks < T::KSTEPS; ++ks) qa[mt][ks] = load_frag<T>(v, ks, g);
+        qs[mt] = T::MX ? (int)static_cast<const uint8_t*>(q_scale)[(rr * kIdxHeads + 16 * mt + j) * 4 + g] : 127;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int h = 16 * mt + 4 * g + i;
             float x = w[rr * kIdxHeads + h];
-            if constexpr (T::SCALED) x *= q_scale[rr * kIdxHeads + h];
+            if constexpr (T::SCALED) x *= static_cast<const float*>(q_scale)[rr * kIdxHeads + h];
             wr[mt][i] = valid ? x : 0.f;
         }
     }
@@ -135,8 +161,8 @@ __device__ __forceinline__ float head_weighted_relu_sum(const f32x4 (&acc)[4], c
 // block 64*NW.
 template <class T, int NQ, int TPW, int NW>
 __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
-    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
-    const uint8_t* __restrict__ kpool, const float* __restrict__ kscale,
+    const uint8_t* __restrict__ q, const void* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ kpool, const void* __restrict__ kscale,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
     int64_t num_blocks, int n_q, int max_seq_len, float* __restrict__ scores, int64_t ld) {
     static_assert(NQ <= 2, "decode rows per sequence");
@@ -170,7 +196,7 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
         pt[u] = t * kBlock < Lb ? p : -1;
     }
     typename T::frag kf[2][4][T::KSTEPS];
-    float ksc[2][4];
+    float ksc[2][4];  // fp8: the position's scale; MXFP8: its E8M0 byte of k-block g (as bits)
     auto load_tile = [&](int u, typename T::frag (&f)[4][T::KSTEPS], float (&sc)[4]) {
         const int64_t p = pt[u] < 0 ? 0 : pt[u];
 #pragma unroll
@@ -178,7 +204,9 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
             const uint8_t* v = kpool + (p * kBlock + 16 * nt + j) * (int64_t)T::ROW;
 #pragma unroll
             for (int ks = 0; ks < T::KSTEPS; ++ks) f[nt][ks] = load_frag<T>(v, ks, g);
-            if constexpr (T::SCALED) sc[nt] = kscale[p * kBlock + 16 * nt + j];
+            if constexpr (T::SCALED) sc[nt] = static_cast<const float*>(kscale)[p * kBlock + 16 * nt + j];
+            if constexpr (T::MX)
+                sc[nt] = __int_as_float(static_cast<const uint8_t*>(kscale)[(p * kBlock + 16 * nt + j) * 4 + g]);
         }
     };
     load_tile(0, kf[0], ksc[0]);
@@ -186,6 +214,7 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
 
     typename T::frag qa[NQ][4][T::KSTEPS];
     float wr[NQ][4][4];
+    int qsx[NQ][4];  // MXFP8: E8M0 scale of head 16mt + j, k-block g
     __syncthreads();
 #pragma unroll
     for (int qi = 0; qi < NQ; ++qi) {
@@ -196,11 +225,13 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
             const uint8_t* v = q_s + (qi * kIdxHeads + 16 * mt + j) * QROW;
 #pragma unroll
             for (int ks = 0; ks < T::KSTEPS; ++ks) qa[qi][mt][ks] = load_frag<T>(v, ks, g);
+            qsx[qi][mt] = T::MX ? (int)static_cast<const uint8_t*>(q_scale)[(rr * kIdxHeads + 16 * mt + j) * 4 + g]
+                                : 127;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int h = 16 * mt + 4 * g + i;
                 float x = w[rr * kIdxHeads + h];
-                if constexpr (T::SCALED) x *= q_scale[rr * kIdxHeads + h];
+                if constexpr (T::SCALED) x *= static_cast<const float*>(q_scale)[rr * kIdxHeads + h];
                 wr[qi][mt][i] = valid ? x : 0.f;
             }
         }
@@ -227,7 +258,9 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
                 for (int mt = 0; mt < 4; ++mt) {
                     acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < T::KSTEPS; ++ks) acc[mt] = mma(qa[qi][mt][ks], f[nt][ks], acc[mt]);
+                    for (int ks = 0; ks < T::KSTEPS; ++ks)
+                        acc[mt] = mma<T>(qa[qi][mt][ks], f[nt][ks], acc[mt], qsx[qi][mt],
+                                         __float_as_int(ksc[u & 1][nt]));
                 }
                 float v = head_weighted_relu_sum(acc, wr[qi]);
                 if constexpr (T::SCALED) v *= ksc[u & 1][nt];
@@ -250,15 +283,16 @@ constexpr int kIdxRing = 4;
 
 template <class T>
 __global__ __launch_bounds__(512) void indexer_prefill_kernel(
-    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
-    const uint8_t* __restrict__ kpool, const float* __restrict__ kscale,
+    const uint8_t* __restrict__ q, const void* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ kpool, const void* __restrict__ kscale,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
     int64_t num_blocks, int n_q, int max_seq_len, float* __restrict__ scores, int64_t ld) {
     constexpr int UNITS = T::ROW / 16;              // 16-byte units per K row
     constexpr int TILE_BYTES = kBlock * T::ROW;
     constexpr int TILE_K = TILE_BYTES / (16 * kWave);  // wave-instructions per tile (16 or 8)
     __shared__ __attribute__((aligned(16))) uint8_t ktile[kIdxRing][TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) float kst[kIdxRing][kBlock];  // fp8 scales of the tile
+    // fp8: the scale of each position of the tile; MXFP8: its four E8M0 bytes (k-blocks 0..3)
+    __shared__ __attribute__((aligned(16))) float kst[kIdxRing][kBlock];
     __shared__ int tile_ok[kIdxRing];
 
     const int b = blockIdx.y;
@@ -270,7 +304,8 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
     const int rbs[2] = {(int)blockIdx.x, NB - 1 - (int)blockIdx.x};
     const int npass = (rbs[1] > rbs[0]) ? 2 : 1;
     // gathers issued per tile by this wave: K units (+ the scale line, wave 0, fp8)
-    const int per_tile = (TILE_K - wave + 7) / 8 + ((T::SCALED && wave == 0) ? 1 : 0);
+    constexpr bool kScaleLine = T::SCALED || T::MX;  // the tile's scales are gathered too
+    const int per_tile = (TILE_K - wave + 7) / 8 + ((kScaleLine && wave == 0) ? 1 : 0);
 
     // Vector-memory operations this wave has issued (uniform), so that the wait
     // for a tile counts exactly the operations issued after its gathers.
@@ -303,8 +338,9 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
             const int row = U / UNITS, col = (U % UNITS) ^ (row % UNITS);
             lds_gather16(base + row * T::ROW + col * 16, dst + k * kWave * 16);
         }
-        if constexpr (T::SCALED) {
-            if (wave == 0) lds_gather4(kscale + p * kBlock + lane, lds_addr(&kst[buf][0]));
+        if constexpr (kScaleLine) {  // one dword per position: the fp32 scale or the four E8M0 bytes
+            if (wave == 0)
+                lds_gather4(static_cast<const uint32_t*>(kscale) + p * kBlock + lane, lds_addr(&kst[buf][0]));
         }
         issued += per_tile;
     };
@@ -313,12 +349,13 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
         const int rb = rbs[pass];
         typename T::frag qa[2][4][T::KSTEPS];
         float wr[2][4][4];
+        int qsx[2][4];
         int Lr[2];
         for (int qi = 0; qi < 2; ++qi) {
             const int i = rb * 16 + wave * 2 + qi;
             const bool valid = i < n_q;
             Lr[qi] = valid ? history_len(Lb, n_q, i) : 0;
-            load_row_query<T>(q, q_scale, w, (int64_t)b * n_q + i, valid, g, j, qa[qi], wr[qi]);
+            load_row_query<T>(q, q_scale, w, (int64_t)b * n_q + i, valid, g, j, qa[qi], wr[qi], qsx[qi]);
         }
         const int last = (rb * 16 + 15 < n_q - 1) ? rb * 16 + 15 : n_q - 1;
         const int Lmax = history_len(Lb, n_q, last);
@@ -355,16 +392,18 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
                 // sum runs under the other's MFMAs.  MFMA steps run at raised
                 // wave priority, so the matrix core is fed first.
                 typename T::frag kf[2][T::KSTEPS];
-                auto read_k = [&](int nt, typename T::frag (&f)[T::KSTEPS]) __attribute__((always_inline)) {
+                int ksx[2];  // MXFP8: E8M0 scale of position 16nt + j, k-block g
+                auto read_k = [&](int nt, typename T::frag (&f)[T::KSTEPS], int& kx) __attribute__((always_inline)) {
                     const int prow = 16 * nt + j;
                     const uint8_t* rowp = &ktile[buf][prow * T::ROW];
+                    kx = T::MX ? (int)reinterpret_cast<const uint8_t*>(&kst[buf][0])[prow * 4 + g] : 127;
 #pragma unroll
                     for (int ks = 0; ks < T::KSTEPS; ++ks) {
                         if constexpr (T::FB == 16) {
                             const int u = (4 * ks + g) ^ (prow % UNITS);
                             f[ks] = *reinterpret_cast<const bf16x8*>(rowp + u * 16);
-                        } else {
-                            const int u0 = (2 * g) ^ (prow % UNITS), u1 = (2 * g + 1) ^ (prow % UNITS);
+                        } else {  // elements [16g, +16) and [64 + 16g, +16) (the MFMA's operand order)
+                            const int u0 = g ^ (prow % UNITS), u1 = (4 + g) ^ (prow % UNITS);
                             const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + u0 * 16);
                             const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + u1 * 16);
                             f[ks] = typename T::frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -376,12 +415,13 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
                     __builtin_amdgcn_s_setprio(2);
                     __builtin_amdgcn_sched_barrier(0);
                     const int nt = k >> 1, qi = k & 1;
-                    if (qi == 0) read_k(nt, kf[nt & 1]);
+                    if (qi == 0) read_k(nt, kf[nt & 1], ksx[nt & 1]);
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) {
                         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int ks = 0; ks < T::KSTEPS; ++ks) acc[mt] = mma(qa[qi][mt][ks], kf[nt & 1][ks], acc[mt]);
+                        for (int ks = 0; ks < T::KSTEPS; ++ks)
+                            acc[mt] = mma<T>(qa[qi][mt][ks], kf[nt & 1][ks], acc[mt], qsx[qi][mt], ksx[nt & 1]);
                     }
                 };
                 // the sum of step k reaches all four lane groups; lane 16g + j
@@ -442,7 +482,6 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
                            a.n_q, a.max_seq_len, a.H, a.D, a.scores, a.ld);
         return hipGetLastError();
     }
-    const bool fp8 = a.dtype == 2;
     if (a.n_q <= 2) {
         // one row: 8 waves x 2 tiles (both in flight, two waves per SIMD); two
         // rows need more registers: 4 waves x 4 tiles, two in flight
@@ -453,8 +492,10 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
                        (const uint8_t*)a.q, a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale,   \
                        a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len,   \
                        a.scores, a.ld)
-        if (fp8) {
+        if (a.dtype == 2) {
             if (a.n_q == 1) DSA_DEC(IdxFp8, 1, 2, 8); else DSA_DEC(IdxFp8, 2, 4, 4);
+        } else if (a.dtype == 3) {
+            if (a.n_q == 1) DSA_DEC(IdxMx, 1, 2, 8); else DSA_DEC(IdxMx, 2, 4, 4);
         } else {
             if (a.n_q == 1) DSA_DEC(IdxBf16, 1, 2, 8); else DSA_DEC(IdxBf16, 2, 4, 4);
         }
@@ -463,16 +504,14 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
     }
     const int NB = (a.n_q + 15) / 16;
     dim3 grid((NB + 1) / 2, a.batch);
-    if (fp8)
-        hipLaunchKernelGGL((indexer_prefill_kernel<IdxFp8>), grid, dim3(512), 0, st,
-                           (const uint8_t*)a.q, a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale,
-                           a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len,
-                           a.scores, a.ld);
-    else
-        hipLaunchKernelGGL((indexer_prefill_kernel<IdxBf16>), grid, dim3(512), 0, st,
-                           (const uint8_t*)a.q, a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale,
-                           a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len,
-                           a.scores, a.ld);
+#define DSA_PRE(T)                                                                                   \
+    hipLaunchKernelGGL((indexer_prefill_kernel<T>), grid, dim3(512), 0, st, (const uint8_t*)a.q,    \
+                       a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale, a.seq_lens, a.table,      \
+                       a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len, a.scores, a.ld)
+    if (a.dtype == 2) DSA_PRE(IdxFp8);
+    else if (a.dtype == 3) DSA_PRE(IdxMx);
+    else DSA_PRE(IdxBf16);
+#undef DSA_PRE
     return hipGetLastError();
 }
 

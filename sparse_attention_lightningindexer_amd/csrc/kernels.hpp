@@ -12,12 +12,12 @@ constexpr int kAttnMaxSplits = 32;        // split partials merged per row
 constexpr int kAttnMaxSplitSlots = 2048;  // index slots one attention workgroup compacts
 
 struct IndexerLaunch {
-    int dtype;                 // 0 f32, 1 bf16, 2 e4m3
+    int dtype;                 // 0 f32, 1 bf16, 2 e4m3 + fp32 per 128, 3 MXFP8 (e4m3 + e8m0 per 32)
     const void* q;
-    const float* q_scale;
+    const void* q_scale;       // fp32 [rows][heads] (2) or e8m0 [rows][heads][4] (3)
     const float* w;
     const void* kpool;
-    const float* kscale;
+    const void* kscale;        // fp32 [pool rows] (2) or e8m0 [pool rows][4] (3)
     const int32_t* seq_lens;
     const int32_t* table;
     int max_blocks;
@@ -38,10 +38,10 @@ struct TopkLaunch {
 
 struct AttnLaunch {
     int q_dtype;               // 0 f32, 1 bf16
-    int kv_kind;               // 0 f32, 1 bf16, 2 MXFP8 (e4m3 + e8m0 per 32)
+    int kv_kind;               // 0 f32, 1 bf16, 2 MXFP8 (e4m3 + e8m0 per 32), 3 e4m3 + fp32 per 128
     const void* q;
     const void* kv;
-    const uint8_t* kvscale;
+    const void* kvscale;       // e8m0 [pool rows][18] (2) or fp32 [pool rows][5] (3)
     const int32_t* seq_lens;
     const int32_t* table;
     int max_blocks;

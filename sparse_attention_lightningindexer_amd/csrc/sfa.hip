@@ -70,6 +70,10 @@ __device__ __forceinline__ void dequant_unit(i32x4 codes, float scale, i32x4& lo
     hi = i32x4{(int)packed[4], (int)packed[5], (int)packed[6], (int)packed[7]};
 }
 
+// 16 e4m3 codes times an fp32 scale -> 16 bf16: the fp32 product, rounded to
+// nearest-even bf16 (not exact; defined below, after pack_bf16x2).
+__device__ __forceinline__ void dequant_unit_rne(i32x4 codes, float scale, i32x4& lo, i32x4& hi);
+
 // Work decomposition: one workgroup per (row, half of the heads, split of the
 // index list).  The two head halves write disjoint outputs (no merge); only
 // position splits produce partials, merged by LSE afterwards.  The workgroups
@@ -114,13 +118,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-template <bool MX>
+__device__ __forceinline__ void dequant_unit_rne(i32x4 codes, float scale, i32x4& lo, i32x4& hi) {
+    uint32_t packed[8];
+    for (int w = 0; w < 4; ++w) {
+        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(codes[w], false);
+        const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(codes[w], true);
+        packed[2 * w] = pack_bf16x2(a[0] * scale, a[1] * scale);
+        packed[2 * w + 1] = pack_bf16x2(c[0] * scale, c[1] * scale);
+    }
+    lo = i32x4{(int)packed[0], (int)packed[1], (int)packed[2], (int)packed[3]};
+    hi = i32x4{(int)packed[4], (int)packed[5], (int)packed[6], (int)packed[7]};
+}
+
+// KV: 1 bf16, 2 MXFP8 (e4m3 + E8M0 per 32), 3 e4m3 + fp32 scale per 128.
+template <int KV>
 __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kvscale,
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, const void* __restrict__ kvscale,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
     int64_t num_blocks, int n_q, int max_seq_len, int rows, const int32_t* __restrict__ indices,
     int top_k, int per_split, int splits, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, uint16_t* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    constexpr bool MX = KV != 1;  // e4m3 codes, dequantized to bf16 while staged
     __shared__ __attribute__((aligned(16))) uint8_t tile[kRing][kTileB];
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][kHalf * kPRow];  // P[head][pos] bf16, by chunk parity
     __shared__ float l_s[kHalf], m_s[kHalf];
@@ -242,7 +260,10 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
 #pragma unroll
                 for (int m = 1; m < kStRows; ++m) id = r == m ? rid[m] : id;
                 st.v[i] = *reinterpret_cast<const i32x4*>(kv + (int64_t)id * kDqk + u * 16);
-                st.sc[i] = kvscale[(int64_t)id * (kDqk / 32) + (u >> 1)];
+                if constexpr (KV == 2)  // E8M0 of the 32-code group u/2
+                    st.sc[i] = static_cast<const uint8_t*>(kvscale)[(int64_t)id * (kDqk / 32) + (u >> 1)];
+                else  // fp32 of the 128-code group u/8 (five per row, the last one the rope)
+                    st.sc[i] = __float_as_uint(static_cast<const float*>(kvscale)[(int64_t)id * 5 + (u >> 3)]);
             }
         }
     };
@@ -260,7 +281,8 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                 const int U = min(kWave * i + lane, kStRows * kMxUnitsRow - 1);
                 const int r = U / kMxUnitsRow, u = U - r * kMxUnitsRow;
                 i32x4 lo, hi;
-                dequant_unit(st.v[i], e8m0_to_f32(st.sc[i]), lo, hi);
+                if constexpr (KV == 2) dequant_unit(st.v[i], e8m0_to_f32(st.sc[i]), lo, hi);
+                else dequant_unit_rne(st.v[i], __uint_as_float(st.sc[i]), lo, hi);
                 *reinterpret_cast<i32x4*>(T + lds_unit(srow0 + r, 2 * u)) = lo;
                 *reinterpret_cast<i32x4*>(T + lds_unit(srow0 + r, 2 * u + 1)) = hi;
             }
@@ -681,13 +703,18 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st) {
     const float scale_log2 = a.sm_scale * kLog2e;
     uint16_t* ws_o = (uint16_t*)a.ws;
     float* ws_lse = splits == 1 ? nullptr : (float*)(ws_o + (size_t)rows * splits * kH * kDv);
-    if (a.kv_kind == 2)
-        hipLaunchKernelGGL((sfa_mla_kernel<true>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,
+    if (a.kv_kind == 3)
+        hipLaunchKernelGGL((sfa_mla_kernel<3>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,
+                           (const uint8_t*)a.kv, a.kvscale, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
+                           a.n_q, a.max_seq_len, rows, a.indices, a.top_k, per, splits, scale_log2,
+                           (uint16_t*)a.out, a.lse, ws_o, ws_lse);
+    else if (a.kv_kind == 2)
+        hipLaunchKernelGGL((sfa_mla_kernel<2>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,
                            (const uint8_t*)a.kv, a.kvscale, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
                            a.n_q, a.max_seq_len, rows, a.indices, a.top_k, per, splits, scale_log2,
                            (uint16_t*)a.out, a.lse, ws_o, ws_lse);
     else
-        hipLaunchKernelGGL((sfa_mla_kernel<false>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,
+        hipLaunchKernelGGL((sfa_mla_kernel<1>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,
                            (const uint8_t*)a.kv, a.kvscale, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
                            a.n_q, a.max_seq_len, rows, a.indices, a.top_k, per, splits, scale_log2,
                            (uint16_t*)a.out, a.lse, ws_o, ws_lse);

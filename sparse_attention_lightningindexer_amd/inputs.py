@@ -20,11 +20,15 @@ independent of each other and of the draw order):
 * values    -- standard normal float32 times sqrt(var): q_I and k_I use
                var = 1/d_I, head weights 1/H_I, q and kv 1/d_qk.  They are then
                rounded to nearest-even into the storage dtype.
-* fp8 index -- q_I and k_I as OCP e4m3 with one fp32 scale per 128 elements:
-               scale = amax/448 (1 when amax = 0), code = e4m3(x/scale).
-* MXFP8 KV  -- e4m3 codes with one E8M0 scale per 32 elements:
+* fp32-scaled e4m3 -- one fp32 scale per 128 elements: scale = amax/448 (1
+               when amax = 0), code = e4m3(x/scale).  The fp8 decode workload
+               stores q_I and k_I this way; the pages' assignment (workload 6)
+               stores the latent KV this way, a 576 row in groups 0..4 of 128
+               (the last one covering the 64 rope channels).
+* MXFP8     -- e4m3 codes with one E8M0 scale per 32 elements:
                e = floor(log2(amax)) - 8, code = e4m3(clamp(x/2^e, +-448)),
-               scale byte = e + 127.
+               scale byte = e + 127.  The fp8 decode workload stores the
+               latent KV this way; workload 6 stores q_I and k_I this way.
 * poison    -- when requested, every pool element that no valid position maps
                to (the tail of each sequence's last block, and the spare block)
                is NaN, so a kernel that reads outside the history shows it.
@@ -60,6 +64,11 @@ CONFIGS = {
     5: dict(name="fp8_decode_b64_ctx16384", batch=64, n_q=1, lens=16384, H_I=64, d_I=128,
             H=128, d_qk=576, d_v=512, top_k=2048, idx_dtype="e4m3", kv_dtype="mxfp8",
             q_dtype="bf16", out_dtype="bf16", paging="permuted", seed=5),
+    # the pages' own assignment: MXFP8 indexer q/k (E8M0 per 32) and an fp8
+    # KV cache with an fp32 scale per 128 channels
+    6: dict(name="fp8_pages_decode_b64_ctx16384", batch=64, n_q=1, lens=16384, H_I=64, d_I=128,
+            H=128, d_qk=576, d_v=512, top_k=2048, idx_dtype="mxfp8", kv_dtype="e4m3_128",
+            q_dtype="bf16", out_dtype="bf16", paging="permuted", seed=6),
 }
 
 _CHUNK = 1 << 22  # elements per drawn chunk, keeps host memory bounded
@@ -116,8 +125,17 @@ def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
 
 
 def quantize_e4m3_f32scale(x: np.ndarray, group: int):
-    """Per-group (last axis) e4m3 codes with an fp32 scale amax/448 per group."""
+    """Per-group (last axis) e4m3 codes with an fp32 scale amax/448 per group.
+
+    When `group` does not divide the last axis, the last group is shorter
+    (zero padding changes no amax); there are ceil(n/group) scales."""
     shp = x.shape
+    n = shp[-1]
+    ng = (n + group - 1) // group
+    if ng * group != n:
+        pad = np.zeros((*shp[:-1], ng * group - n), np.float32)
+        codes, scale = quantize_e4m3_f32scale(np.concatenate([x.astype(np.float32), pad], axis=-1), group)
+        return np.ascontiguousarray(codes[..., :n]), scale
     g = x.reshape(*shp[:-1], shp[-1] // group, group)
     amax = np.abs(g).max(axis=-1)
     scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
@@ -142,7 +160,8 @@ def quantize_mxfp8(x: np.ndarray, group: int = 32):
             (e + 127).to(torch.uint8).numpy().reshape(*shp[:-1], shp[-1] // group))
 
 
-_NAN_BITS = {"f32": None, "bf16": np.uint16(0x7FC0), "e4m3": np.uint8(0x7F)}
+_NAN_BITS = {"f32": None, "bf16": np.uint16(0x7FC0), "e4m3": np.uint8(0x7F), "mxfp8": np.uint8(0x7F),
+             "e4m3_128": np.uint8(0x7F)}
 
 
 @dataclass
@@ -165,18 +184,18 @@ class Workload:
     seq_lens: np.ndarray          # int32 [batch]
     block_table: np.ndarray       # int32 [batch, max_blocks]
     num_blocks: int
-    idx_dtype: str                # "f32" | "bf16" | "e4m3"
-    kv_dtype: str                 # "f32" | "bf16" | "mxfp8"
+    idx_dtype: str                # "f32" | "bf16" | "e4m3" (fp32 per 128) | "mxfp8" (E8M0 per 32)
+    kv_dtype: str                 # "f32" | "bf16" | "mxfp8" (E8M0 per 32) | "e4m3_128" (fp32 per 128)
     q_dtype: str
     out_dtype: str
     q_idx: np.ndarray             # [rows, H_I, d_I]  f32 | uint16(bf16) | uint8(e4m3)
-    q_idx_scale: np.ndarray | None  # f32 [rows, H_I] (one per 128 elements) or None
+    q_idx_scale: np.ndarray | None  # f32 [rows, H_I] (per 128) | uint8 [rows, H_I, 4] (per 32) | None
     head_w: np.ndarray            # f32 [rows, H_I]
     k_pool: np.ndarray            # [num_blocks, 64, d_I]
-    k_scale: np.ndarray | None    # f32 [num_blocks, 64]
+    k_scale: np.ndarray | None    # f32 [num_blocks, 64] | uint8 e8m0 [num_blocks, 64, 4]
     q: np.ndarray                 # [rows, H, d_qk]
     kv_pool: np.ndarray           # [num_blocks, 64, d_qk]
-    kv_scale: np.ndarray | None   # uint8 e8m0 [num_blocks, 64, d_qk/32]
+    kv_scale: np.ndarray | None   # uint8 e8m0 [num_blocks, 64, d_qk/32] | f32 [num_blocks, 64, 5]
     extra: dict = field(default_factory=dict)
 
     @property
@@ -201,7 +220,7 @@ def make_workload(cfg_id: int, *, seed: int | None = None, rotation: int = 0,
                   batch: int | None = None, n_q: int | None = None, lens=None,
                   top_k: int | None = None, paging: str | None = None,
                   poison: bool = False, spare_table_blocks: int = 1) -> Workload:
-    """Build the inputs of workload `cfg_id` (1..5), optionally reshaped for small tests.
+    """Build the inputs of workload `cfg_id` (1..6), optionally reshaped for small tests.
 
     `lens` may be an int (all sequences), a sequence of ints, or None (the
     workload's own).  `spare_table_blocks` extra columns are added to the
@@ -284,6 +303,9 @@ def make_workload(cfg_id: int, *, seed: int | None = None, rotation: int = 0,
         q_idx_scale = qs.reshape(rows, H_I * d_I // 128)
         k_pool, ks = quantize_e4m3_f32scale(kf, 128)
         k_scale = ks.reshape(num_blocks * BLOCK, d_I // 128)
+    elif idx_dtype == "mxfp8":
+        q_idx, q_idx_scale = quantize_mxfp8(qif, 32)   # [rows, H_I, d_I], [rows, H_I, d_I/32]
+        k_pool, k_scale = quantize_mxfp8(kf, 32)       # [pool rows, d_I], [pool rows, d_I/32]
     else:
         raise ValueError(idx_dtype)
 
@@ -293,6 +315,8 @@ def make_workload(cfg_id: int, *, seed: int | None = None, rotation: int = 0,
         kv_pool = f32_to_bf16_bits(kvf)
     elif kv_dtype == "mxfp8":
         kv_pool, kv_scale = quantize_mxfp8(kvf, 32)
+    elif kv_dtype == "e4m3_128":
+        kv_pool, kv_scale = quantize_e4m3_f32scale(kvf, 128)  # scales [pool rows, 5]
     else:
         raise ValueError(kv_dtype)
 
@@ -303,14 +327,14 @@ def make_workload(cfg_id: int, *, seed: int | None = None, rotation: int = 0,
         else:
             k_pool[inv_k] = _NAN_BITS[idx_dtype]
         if k_scale is not None:
-            k_scale[inv_k] = np.nan
+            k_scale[inv_k] = np.uint8(0xFF) if k_scale.dtype == np.uint8 else np.nan
         if kv_dtype == "f32":
             kv_pool[inv_kv] = np.nan
         elif kv_dtype == "bf16":
             kv_pool[inv_kv] = _NAN_BITS["bf16"]
         else:
             kv_pool[inv_kv] = _NAN_BITS["e4m3"]
-            kv_scale[inv_kv] = np.uint8(0xFF)
+            kv_scale[inv_kv] = np.uint8(0xFF) if kv_scale.dtype == np.uint8 else np.nan
 
     def blocks(a):
         return None if a is None else np.ascontiguousarray(a.reshape(num_blocks, BLOCK, *a.shape[1:]))
@@ -321,7 +345,8 @@ def make_workload(cfg_id: int, *, seed: int | None = None, rotation: int = 0,
         idx_dtype=idx_dtype, kv_dtype=kv_dtype, q_dtype=cfg["q_dtype"], out_dtype=cfg["out_dtype"],
         q_idx=np.ascontiguousarray(q_idx), q_idx_scale=q_idx_scale,
         head_w=np.ascontiguousarray(w), k_pool=blocks(k_pool),
-        k_scale=None if k_scale is None else np.ascontiguousarray(k_scale.reshape(num_blocks, BLOCK)),
+        k_scale=(None if k_scale is None else np.ascontiguousarray(
+            k_scale.reshape(num_blocks, BLOCK) if idx_dtype == "e4m3" else blocks(k_scale))),
         q=np.ascontiguousarray(q), kv_pool=blocks(kv_pool), kv_scale=blocks(kv_scale),
     )
     return wl

@@ -49,9 +49,15 @@ def score_bound(wl, rows):
         L = int(wl.row_lens()[r])
         K = np.abs(dequant_np(logical_rows(wl.k_pool, wl, b, L), wl.idx_dtype))
         Q = np.abs(dequant_np(wl.q_idx[r], wl.idx_dtype))
-        if wl.q_idx_scale is not None:
+        if wl.idx_dtype == "e4m3":  # one fp32 factor per 128-element vector
             Q = Q * wl.q_idx_scale[r][:, None].astype(np.float64)
             K = K * logical_rows(wl.k_scale[..., None], wl, b, L)[:, :1].astype(np.float64)
+        elif wl.idx_dtype == "mxfp8":  # one E8M0 factor per 32 elements
+            def e8m0(a):
+                f = torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e8m0fnu).double().numpy()
+                return np.repeat(f, 32, axis=-1)
+            Q = Q * e8m0(wl.q_idx_scale[r])
+            K = K * e8m0(logical_rows(wl.k_scale, wl, b, L))
         S = np.abs(wl.head_w[r]).astype(np.float64) @ (Q @ K.T)
         out.append(4 * (wl.d_I + wl.H_I + 4) * 2.0 ** -24 * S + 1e-30)
     return out

@@ -33,6 +33,8 @@ SMALL = {
     "decode_bf16_dense": (2, dict(batch=2, lens=[200, 77], top_k=256, poison=True)),
     "skewed_nq2": (4, dict(batch=3, lens=[700, 1500, 1], top_k=256, poison=True)),
     "fp8_decode": (5, dict(batch=3, lens=[500, 900, 130], top_k=256, poison=True)),
+    "fp8_pages_decode": (6, dict(batch=3, lens=[500, 900, 130], top_k=256, poison=True)),
+    "fp8_pages_nq2": (6, dict(batch=2, n_q=2, lens=[700, 66], top_k=256, poison=True)),
     "prefill_bf16": (3, dict(lens=333, top_k=96, poison=True)),
 }
 
@@ -169,11 +171,12 @@ FULL_SAMPLES = {
     2: [0, 7, 31],
     4: [0, 5, 15],
     5: [0, 33, 63],
+    6: [0, 33, 63],
     1: None,
 }
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 4, 5, 6])
 def test_full_size_sampled_rows(cfg):
     say(f"[parity] full cfg {cfg}: generating")
     wl = make_workload(cfg)
@@ -197,12 +200,13 @@ def test_full_size_sampled_rows(cfg):
     check_attention(wl, f64(out[rows]), f64(lse[rows]), ref_o, ref_l, f"full cfg {cfg}")
 
 
-@pytest.mark.parametrize("cfg", [3, 5])
+@pytest.mark.parametrize("cfg", [3, 5, 6])
 def test_prefill_permuted_paging_across_table_windows(cfg):
     # 4500 causal rows: the prefill indexer kernel reads the block table in
     # windows of 64 tiles (4096 positions), so rows past 4096 use the second
     # window; permuted paging makes every window entry matter.  cfg 5 runs the
-    # same rows with the fp8 indexer and the MXFP8 cache.
+    # same rows with the fp8 indexer and the MXFP8 cache, cfg 6 with the MXFP8
+    # indexer and the fp32-per-128 cache.
     wl = make_workload(cfg, batch=1, n_q=4500, lens=4500, top_k=256, paging="permuted", poison=True)
     dev = B.DeviceInputs(wl)
     say(f"[parity] prefill across table windows, cfg {cfg}: forward on GPU")

@@ -98,9 +98,19 @@ def _f64(a, dtype):
         return a.astype(np.float64)
     if dtype == "bf16":
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).double().numpy()
-    if dtype in ("e4m3", "mxfp8"):
+    if dtype in ("e4m3", "mxfp8", "e4m3_128"):
         return torch.from_numpy(a).view(torch.float8_e4m3fn).double().numpy()
     raise ValueError(dtype)
+
+
+def _scales_f64(sc, per: int, width: int):
+    """Per-element float64 factors of a scale array [..., groups]: E8M0 bytes (torch's
+    float8_e8m0fnu) or fp32; group g covers elements [g*per, (g+1)*per), cut at `width`."""
+    if sc.dtype == np.uint8:
+        f = torch.from_numpy(np.ascontiguousarray(sc)).view(torch.float8_e8m0fnu).double().numpy()
+    else:
+        f = sc.astype(np.float64)
+    return np.repeat(f, per, axis=-1)[..., :width]
 
 
 def _logical(pool, wl, b, L):
@@ -109,7 +119,7 @@ def _logical(pool, wl, b, L):
     return pool.reshape(-1, *pool.shape[2:])[wl.block_table[b, s // 64].astype(np.int64) * 64 + s % 64]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 5, 6])
 def test_indexer_one_hot_head_weight_is_relu_matmul(cfg):
     """w = e_j reduces the score to relu(q_j . K^T): one fp64 library matmul."""
     wl = make_workload(cfg, batch=2, n_q=3, lens=[150, 77]) if cfg != 1 else make_workload(1)
@@ -124,10 +134,13 @@ def test_indexer_one_hot_head_weight_is_relu_matmul(cfg):
             L = int(wl.row_lens()[r])
             K = _f64(_logical(wl.k_pool, wl, b, L), wl.idx_dtype)
             q = _f64(wl.q_idx[r, j], wl.idx_dtype)
-            if wl.q_idx_scale is not None:
+            if wl.idx_dtype == "e4m3":  # one fp32 factor per 128-element vector
                 q = q * np.float64(wl.q_idx_scale[r, j])
                 kr = _logical(wl.k_scale[..., None], wl, b, L)[:, 0].astype(np.float64)
                 K = K * kr[:, None]
+            elif wl.idx_dtype == "mxfp8":  # one E8M0 factor per 32 elements
+                q = q * _scales_f64(wl.q_idx_scale[r, j], 32, wl.d_I)
+                K = K * _scales_f64(_logical(wl.k_scale, wl, b, L), 32, wl.d_I)
             ref = np.maximum(K @ q, 0.0)
             # forward error bound of an fp64 dot product of length d: gamma_d * sum |q_c k_c|
             bound = 2 * wl.d_I * 2.0 ** -53 * (np.abs(K) @ np.abs(q))
@@ -271,10 +284,9 @@ def _sdpa_ref(wl, rows):
         b, i = r // wl.n_q, r % wl.n_q
         Lb = int(wl.seq_lens[b])
         kv = _f64(_logical(wl.kv_pool, wl, b, Lb), wl.kv_dtype)
-        if wl.kv_scale is not None:
-            sc = _logical(wl.kv_scale, wl, b, Lb)
-            e = torch.from_numpy(sc).view(torch.float8_e8m0fnu).double().numpy()
-            kv = kv * np.repeat(e, 32, axis=-1)
+        if wl.kv_scale is not None:  # E8M0 per 32, or fp32 per 128 (five groups of a 576 row)
+            kv = kv * _scales_f64(_logical(wl.kv_scale, wl, b, Lb), 32 if wl.kv_dtype == "mxfp8" else 128,
+                                  wl.d_qk)
         q = torch.from_numpy(_f64(wl.q[r], wl.q_dtype))[None, :, None, :]   # [1,H,1,d]
         K = torch.from_numpy(kv)[None, None].expand(1, wl.H, Lb, wl.d_qk)
         V = torch.from_numpy(np.ascontiguousarray(kv[:, :wl.d_v]))[None, None].expand(1, wl.H, Lb, wl.d_v)
@@ -293,6 +305,7 @@ def _sdpa_ref(wl, rows):
     (2, dict(batch=2, n_q=1, lens=[70, 129])),
     (4, dict(batch=2, n_q=2, lens=[66, 130])),
     (5, dict(batch=2, n_q=1, lens=[100, 65])),
+    (6, dict(batch=2, n_q=1, lens=[100, 65])),
 ])
 def test_sparse_equals_dense_sdpa_when_topk_covers_history(cfg, kw):
     wl = make_workload(cfg, **kw)
@@ -384,6 +397,38 @@ def test_mxfp8_cache_equals_its_dequantized_fp32_copy():
     a, la = O.sparse_attn(wl, idx)
     b, lb = O.sparse_attn(w2, idx)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_fp32_per_128_cache_dequantizes_with_a_short_last_group():
+    """A 576 row with one fp32 factor per 128 channels has five groups, the last covering
+    the 64 rope channels: the oracle's decoding equals torch's e4m3 decode times the
+    factor of group c // 128, exactly (both in float64)."""
+    wl = make_workload(6, batch=2, n_q=1, lens=[70, 64])
+    assert wl.kv_scale.shape[-1] == 5 and wl.kv_scale.dtype == np.float32
+    codes = wl.kv_pool.reshape(-1, wl.d_qk)[:200]
+    scl = wl.kv_scale.reshape(-1, 5)[:200]
+    got = O.dequant(codes, "e4m3", scl, "f32", 128)
+    ref = _f64(codes, "e4m3") * np.repeat(scl.astype(np.float64), 128, axis=-1)[:, :576]
+    assert np.array_equal(got, ref)
+    assert not np.array_equal(got[:, 512:], _f64(codes, "e4m3")[:, 512:] * scl[:, 3:4])  # group 4 is its own
+
+
+def test_quantized_inputs_round_trip_within_e4m3_rounding():
+    """Codes times scales reproduce the values, clamped to +-448 times their scale, within
+    half an e4m3 step (2^-4 relative for normals, 2^-10 times the scale below), for both
+    scale formats of workload 6.  (The MX rule e = floor(log2 amax) - 8 puts amax/2^e in
+    [256, 512), so the largest values of a group can saturate at 448.)"""
+    from sparse_attention_lightningindexer_amd.inputs import quantize_e4m3_f32scale, quantize_mxfp8
+    x = np.random.default_rng(3).standard_normal((64, 576)).astype(np.float32) / 24
+    for codes, scl, kind, group in [(*quantize_e4m3_f32scale(x, 128), "f32", 128),
+                                    (*quantize_mxfp8(x, 32), "e8m0", 32)]:
+        deq = O.dequant(codes, "e4m3", scl, kind, group)
+        f = _scales_f64(scl, group, 576)
+        xc = np.clip(x.astype(np.float64), -448 * f, 448 * f)
+        err = np.abs(deq - xc)
+        assert (err <= np.maximum(np.abs(xc) * 2.0 ** -4, f * 2.0 ** -10) * (1 + 1e-12)).all()
+        if kind == "f32":  # amax/448 scales never saturate (up to the rounding of the division)
+            assert (np.abs(x) <= 448 * f * (1 + 2.0 ** -20)).all()
 
 
 def test_forward_with_full_topk_is_dense_attention():
