@@ -22,7 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "DSA tokens/s (LI+TopK+SFA), decode B32@8k & prefill 32k; % HBM/MFMA peak"
-WORKLOADS = {"tiny": 1, "decode": 2, "prefill": 3, "skewed": 4, "fp8": 5}
+WORKLOADS = {"tiny": 1, "decode": 2, "prefill": 3, "skewed": 4, "fp8": 5, "fp8pages": 6}
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -37,17 +37,20 @@ def algorithmic(wl):
     L = wl.row_lens().astype(np.int64)
     k = np.minimum(L, wl.top_k)
     rows = wl.rows
-    esz = {"f32": 4, "bf16": 2, "e4m3": 1, "mxfp8": 1}
+    esz = {"f32": 4, "bf16": 2, "e4m3": 1, "mxfp8": 1, "e4m3_128": 1}
+    # scale bytes per index vector (d_I) and per latent row (d_qk)
+    idx_sc = {"e4m3": 4, "mxfp8": wl.d_I // 32}.get(wl.idx_dtype, 0)
+    kv_sc = {"mxfp8": wl.d_qk // 32, "e4m3_128": 4 * ((wl.d_qk + 127) // 128)}.get(wl.kv_dtype, 0)
     # indexer: each sequence's K_I rows once (shared by its n_q queries), q_I, w, scales
     seq_hist = wl.seq_lens.astype(np.int64)
-    k_row = wl.d_I * esz[wl.idx_dtype] + (4 if wl.idx_dtype == "e4m3" else 0)
-    q_row = wl.H_I * wl.d_I * esz[wl.idx_dtype] + wl.H_I * 4 * (2 if wl.idx_dtype == "e4m3" else 1)
+    k_row = wl.d_I * esz[wl.idx_dtype] + idx_sc
+    q_row = wl.H_I * wl.d_I * esz[wl.idx_dtype] + wl.H_I * (4 + idx_sc)  # codes, scales, head weights
     idx_bytes = int(seq_hist.sum() * k_row + rows * q_row)
     idx_flops = int(2 * L.sum() * wl.H_I * wl.d_I)
     # Top-K: the k_r indices written (scores are the unfused intermediate)
     topk_bytes = int(rows * wl.top_k * 4)
     # attention: gathered latent rows, q, out, indices
-    kv_row = wl.d_qk * esz[wl.kv_dtype] + (wl.d_qk // 32 if wl.kv_dtype == "mxfp8" else 0)
+    kv_row = wl.d_qk * esz[wl.kv_dtype] + kv_sc
     qb = wl.H * wl.d_qk * esz[wl.q_dtype]
     ob = wl.H * wl.d_v * (4 if wl.out_dtype == "f32" else 2)
     attn_bytes = int(k.sum() * kv_row + rows * (qb + ob + wl.top_k * 4))
@@ -295,7 +298,8 @@ def main():
     res = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "fp8e4m3+bf16"}[wl0.idx_dtype],
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "fp8e4m3+bf16", "mxfp8": "fp8e4m3+bf16"}[wl0.idx_dtype],
         "data": "synthetic",
         "config": {"workload": wl0.cfg["name"], "batch": wl0.batch, "n_q": wl0.n_q,
                    "context": int(wl0.max_seq_len), "top_k": wl0.top_k, "index_heads": wl0.H_I,
@@ -304,6 +308,18 @@ def main():
         "roofline": roof,
         "stages_us": stage_us,
     }
+    if wl0.idx_dtype in ("e4m3", "mxfp8"):
+        # reported, not a parity bound: how much of the quantized indexer's
+        # Top-K the bf16 indexer (same drawn values, rounded to bf16) also
+        # selects, over every row of the first input set
+        wl_b = make_workload(cfg, rotation=0, idx_dtype="bf16")
+        dev_b = B.DeviceInputs(wl_b)
+        idx_b = B.dsa_topk(dev_b, B.dsa_indexer_scores(dev_b)).cpu().numpy()
+        idx_q = sets[0][3].cpu().numpy()
+        rec = [len(set(a[a >= 0].tolist()) & set(c[c >= 0].tolist())) / max(1, int((c >= 0).sum()))
+               for a, c in zip(idx_q, idx_b)]
+        res["topk_recall_vs_bf16"] = {"mean": float(np.mean(rec)), "min": float(np.min(rec)), "rows": len(rec)}
+        del dev_b
     if args.copy_calib:
         src = torch.randn(args.copy_calib * 2 ** 18, device="cuda")
         dst = torch.empty_like(src)

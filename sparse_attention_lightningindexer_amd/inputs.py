@@ -219,12 +219,14 @@ class Workload:
 def make_workload(cfg_id: int, *, seed: int | None = None, rotation: int = 0,
                   batch: int | None = None, n_q: int | None = None, lens=None,
                   top_k: int | None = None, paging: str | None = None,
-                  poison: bool = False, spare_table_blocks: int = 1) -> Workload:
+                  poison: bool = False, spare_table_blocks: int = 1,
+                  idx_dtype: str | None = None) -> Workload:
     """Build the inputs of workload `cfg_id` (1..6), optionally reshaped for small tests.
 
     `lens` may be an int (all sequences), a sequence of ints, or None (the
     workload's own).  `spare_table_blocks` extra columns are added to the
-    block table; they point at the never-valid spare block.
+    block table; they point at the never-valid spare block.  `idx_dtype`
+    stores the indexer's q/k in another format; the drawn values are the same.
     """
     cfg = dict(CONFIGS[cfg_id])
     seed = cfg["seed"] if seed is None else seed
@@ -265,6 +267,8 @@ def make_workload(cfg_id: int, *, seed: int | None = None, rotation: int = 0,
         off += nblk_seq[b]
 
     rows = B * nq
+    if idx_dtype is not None:
+        cfg["idx_dtype"] = idx_dtype
     idx_dtype, kv_dtype = cfg["idx_dtype"], cfg["kv_dtype"]
 
     def pooled(tid, width, var):
