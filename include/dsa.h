@@ -219,6 +219,32 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_indexer_args* idx,
                        const dsa_attn_args* attn, int32_t top_k, int32_t* indices_out,
                        void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * dsa_cache_append -- write this step's index keys and latent KV rows into the
+ * paged pools, quantizing them when the pool is quantized ([A] §5 "Layered
+ * Quantization": dynamic quantization, scales computed in the operator that
+ * writes the cache; [D] §4.2).
+ *
+ * Row r = b*n_q + i is the token at position s = L_b - n_q + i of sequence b
+ * (the last position row r sees).  k_new[r][0:k->width] is stored at the
+ * index-K pool row of s and kv_new[r][0:kv->width] at the latent pool row of
+ * s; a row with s < 0 or an absent block is skipped.  Per pool format:
+ *   BF16 or F32 (no scales): a copy (k_new/kv_new in the same dtype);
+ *   E4M3 + F32 scale per `group` (a power of two, 4 to 256): scale =
+ *       amax/448 (1 when amax = 0), code = e4m3(x/scale);
+ *   E4M3 + E8M0 scale per `group` (32): e = floor(log2 amax) - 8 (-127 when
+ *       amax = 0, clamped to [-127, 127]), code = e4m3(x * 2^-e), byte e + 127;
+ * with amax over the group (a shorter last group when group does not divide
+ * the width), the quotient clamped to +-448 and rounded to the nearest e4m3
+ * (ties to even), all in fp32; quantized pools take BF16 input.  The pools'
+ * `data` and `scales` are written (device memory the caller owns).
+ * new_dtype: F32 (F32 pools) or BF16.  Widths: multiples of 4, at most 256
+ * (index key) and 768 (latent row).  Errors: NULL, SHAPE, UNSUPPORTED, HIP.
+ */
+dsa_status dsa_cache_append(const dsa_batch* batch, const void* k_new, const void* kv_new,
+                            dsa_dtype new_dtype, const dsa_cache* k, const dsa_cache* kv,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,10 @@
  *     z_s = sm_scale * q[r,h,:].kv[s,:], two-pass softmax, out = sum p_s *
  *     kv[s, :d_v], lse = m + log sum exp(z - m)  ([A] §2, [D] §2.2: the
  *     sparse core reads only the selected KV entries);
- *  5. dense causal attention over all s < L_r (used only by invariants).
+ *  5. dense causal attention over all s < L_r (used only by invariants);
+ *  6. cache append: this step's index keys and latent rows written into the
+ *     paged pools, quantized in fp32 when the pool is (the quantizer's
+ *     decisions are integer codes, so they are taken in the kernel's fp32).
  *
  * Paging ([A] §4 "Sparse attention read"; [D] §8 "Paged KV cache"): logical
  * position s of sequence b lives at pool row
@@ -346,6 +349,108 @@ int oracle_dense_attn(int batch, int n_q, const int32_t* seq_lens, const int32_t
 }
 
 /* Number of OpenMP threads a parallel region of the oracle will use. */
+/* ------------------------------------------------------------ cache append */
+
+/* Nearest-even rounding of a non-negative double to an integer. */
+static double round_half_even(double q) {
+    double f = floor(q), d = q - f;
+    if (d > 0.5) return f + 1.0;
+    if (d < 0.5) return f;
+    return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+/* OCP FP8 E4M3 code of a float, from the format's definition: magnitudes
+ * below 2^-6 on the subnormal grid m * 2^-9, the others as (1 + m/8) * 2^E,
+ * E in [-6, 8], both rounded to the nearest code (ties to the even mantissa);
+ * magnitudes above 448 saturate to 448; NaN gives 0x7F. */
+uint8_t oracle_f32_to_e4m3(float x) {
+    if (isnan(x)) return 0x7F;
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs((double)x);
+    if (a > 448.0) a = 448.0;
+    if (a < ldexp(1.0, -6)) return (uint8_t)(sign | (uint8_t)round_half_even(a / ldexp(1.0, -9)));
+    int e2;
+    frexp(a, &e2);              /* a = f * 2^e2, f in [0.5, 1) */
+    int E = e2 - 1;             /* floor(log2 a) */
+    double m = round_half_even((a / ldexp(1.0, E) - 1.0) * 8.0);
+    if (m == 8.0) { m = 0.0; E += 1; }
+    return (uint8_t)(sign | ((E + 7) << 3) | (int)m);
+}
+
+/* Quantize one vector of `width` values (fp32) into `codes` with one scale per
+ * `group` elements (a shorter last group when group does not divide width),
+ * in fp32 as the dynamic quantization of the pages' layered quantization
+ * ([A] §5 "Layered Quantization"; [D] §4.2: scales computed in the adjacent
+ * operator):
+ *   ORC_SCALE_F32:  scale = amax/448 (1 when amax = 0), code = e4m3(x/scale)
+ *   ORC_SCALE_E8M0: e = floor(log2 amax) - 8 (-127 when amax = 0), clamped to
+ *                   [-127, 127]; code = e4m3(x * 2^-e); the byte is e + 127
+ * The quotient is clamped to +-448 before the rounding. */
+static void quantize_vector(const float* x, int width, int kind, int group, uint8_t* codes, void* scales) {
+    int ng = (width + group - 1) / group;
+    for (int g = 0; g < ng; ++g) {
+        int c0 = g * group, c1 = c0 + group < width ? c0 + group : width;
+        float amax = 0.0f;
+        for (int c = c0; c < c1; ++c) amax = fabsf(x[c]) > amax ? fabsf(x[c]) : amax;
+        if (kind == ORC_SCALE_F32) {
+            volatile float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+            ((float*)scales)[g] = scale;
+            for (int c = c0; c < c1; ++c) {
+                volatile float v = x[c] / scale;
+                float w = v > 448.0f ? 448.0f : (v < -448.0f ? -448.0f : v);
+                codes[c] = oracle_f32_to_e4m3(w);
+            }
+        } else {
+            int e2 = 0;
+            frexpf(amax, &e2);
+            int e = amax > 0.0f ? e2 - 1 - 8 : -127;
+            e = e < -127 ? -127 : (e > 127 ? 127 : e);
+            ((uint8_t*)scales)[g] = (uint8_t)(e + 127);
+            for (int c = c0; c < c1; ++c) {
+                volatile float v = ldexpf(x[c], -e);   /* exact: a power-of-two scaling */
+                float w = v > 448.0f ? 448.0f : (v < -448.0f ? -448.0f : v);
+                codes[c] = oracle_f32_to_e4m3(w);
+            }
+        }
+    }
+}
+
+/* Cache append: row r = b*n_q + i is this step's token at position
+ * s = L_b - n_q + i of sequence b; its `width` values x_new[r] are written to
+ * the pool row of s (skipped when s < 0 or its block is absent), as fp32
+ * (ORC_F32), nearest-even bf16 (ORC_BF16), or e4m3 codes plus scales
+ * (ORC_E4M3, scale kind and group as above).  scales: [pool rows][ceil(width/group)]. */
+int oracle_cache_append(int batch, int n_q, const int32_t* seq_lens, const int32_t* block_table,
+                        int max_blocks, int64_t num_blocks, const float* x_new, int width,
+                        int dtype, int scale_kind, int group, void* pool, void* scales) {
+    orc_batch B = {batch, n_q, seq_lens, block_table, max_blocks, 64, num_blocks};
+    int ng = scale_kind == ORC_SCALE_NONE ? 0 : (width + group - 1) / group;
+    for (int r = 0; r < batch * n_q; ++r) {
+        int b = r / n_q;
+        int s = history_len(&B, r) - 1;
+        if (s < 0) continue;
+        int64_t pr = pool_row(&B, b, s);
+        if (pr < 0) continue;
+        const float* x = x_new + (int64_t)r * width;
+        if (dtype == ORC_F32) {
+            memcpy((float*)pool + pr * width, x, sizeof(float) * (size_t)width);
+        } else if (dtype == ORC_BF16) {
+            for (int c = 0; c < width; ++c) {   /* nearest-even to the upper 16 bits */
+                uint32_t u;
+                memcpy(&u, &x[c], sizeof u);
+                uint32_t lsb = (u >> 16) & 1u;
+                ((uint16_t*)pool)[pr * width + c] = (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+            }
+        } else {
+            uint8_t* codes = (uint8_t*)pool + pr * width;
+            void* sc = scale_kind == ORC_SCALE_F32 ? (void*)((float*)scales + pr * ng)
+                                                   : (void*)((uint8_t*)scales + pr * ng);
+            quantize_vector(x, width, scale_kind, group, codes, sc);
+        }
+    }
+    return 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

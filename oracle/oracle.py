@@ -43,6 +43,9 @@ def lib():
         attn = [i32, i32, p, p, i32, i32, i64, p, i32, i32, i32, i32, p, i32, p, i32, i32]
         L.oracle_sparse_attn.argtypes = attn + [p, i32, d, p, i32, p, p]
         L.oracle_dense_attn.argtypes = attn + [d, p, i32, p, p]
+        L.oracle_f32_to_e4m3.restype = C.c_uint8
+        L.oracle_f32_to_e4m3.argtypes = [C.c_float]
+        L.oracle_cache_append.argtypes = [i32, i32, p, p, i32, i64, p, i32, i32, i32, i32, p, p]
         L.oracle_num_threads.restype = i32
         _lib = L
     return _lib
@@ -164,3 +167,19 @@ def forward(wl, rows=None):
     full[rows_l] = idx_rows
     out, lse = sparse_attn(wl, full, rows_l)
     return sc, idx_rows, out, lse
+
+
+def f32_to_e4m3(x: float) -> int:
+    """The oracle's OCP e4m3 code of one float (nearest, ties to even, saturating)."""
+    return int(lib().oracle_f32_to_e4m3(float(x)))
+
+
+def cache_append(wl, x_new, fmt: str, pool, scales):
+    """Write rows x_new [rows, width] (fp32 values) into `pool` (and `scales`) in place, as
+    storage format `fmt` ("f32", "bf16", "e4m3" = fp32 per 128, "e4m3_128", "mxfp8")."""
+    x = _c(x_new, np.float32)
+    kind, grp = _SCALES[fmt]
+    seq, tab = _c(wl.seq_lens, np.int32), _c(wl.block_table, np.int32)
+    assert pool.flags.c_contiguous and (scales is None or scales.flags.c_contiguous)
+    lib().oracle_cache_append(wl.batch, wl.n_q, _ptr(seq), _ptr(tab), wl.max_blocks, wl.num_blocks,
+                              _ptr(x), x.shape[1], _DT[fmt], kind, grp, _ptr(pool), _ptr(scales))

@@ -63,7 +63,7 @@ _lib = None
 #: every entry point include/dsa.h declares
 EXPORTS = ("dsa_status_string", "dsa_version", "dsa_indexer_scores", "dsa_topk_workspace_bytes",
            "dsa_topk", "dsa_sparse_attn_workspace_bytes", "dsa_sparse_attn",
-           "dsa_forward_workspace_bytes", "dsa_forward")
+           "dsa_forward_workspace_bytes", "dsa_forward", "dsa_cache_append")
 
 
 def lib():
@@ -92,6 +92,9 @@ def lib():
         L.dsa_forward_workspace_bytes.restype = S
         L.dsa_forward_workspace_bytes.argtypes = [P(dsa_batch), P(dsa_indexer_args), P(dsa_attn_args),
                                                   C.c_int32]
+        L.dsa_cache_append.restype = C.c_int
+        L.dsa_cache_append.argtypes = [P(dsa_batch), C.c_void_p, C.c_void_p, C.c_int, P(dsa_cache), P(dsa_cache),
+                                       C.c_void_p]
         L.dsa_forward.restype = C.c_int
         L.dsa_forward.argtypes = [P(dsa_batch), P(dsa_indexer_args), P(dsa_attn_args), C.c_int32, C.c_void_p,
                                   C.c_void_p, S, C.c_void_p]
@@ -233,3 +236,11 @@ def dsa_forward(dev: DeviceInputs, top_k=None, indices_out=None, ws=None, stream
     _check(lib().dsa_forward(C.byref(dev.batch), C.byref(dev.idx), C.byref(dev.attn), top_k, _ptr(indices_out),
                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "dsa_forward")
     return dev.out, dev.lse, indices_out
+
+
+def dsa_cache_append(dev: DeviceInputs, k_new, kv_new, stream=None):
+    """Write rows k_new [rows, d_I] and kv_new [rows, d_qk] (bf16, or fp32 for fp32 pools)
+    into dev's pools (and scales) at each row's own position."""
+    new_dt = DSA_F32 if k_new.dtype == torch.float32 else DSA_BF16
+    _check(lib().dsa_cache_append(C.byref(dev.batch), _ptr(k_new), _ptr(kv_new), new_dt, C.byref(dev.idx.k),
+                                  C.byref(dev.attn.kv), _stream(stream)), "dsa_cache_append")

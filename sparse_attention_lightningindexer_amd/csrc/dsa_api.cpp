@@ -248,4 +248,55 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_indexer_args* idx, cons
     return hip_status(dsa::launch_sparse_attn(attn_launch(batch, attn, indices, top_k, attn_ws_p), st));
 }
 
+dsa_status dsa_cache_append(const dsa_batch* batch, const void* k_new, const void* kv_new, dsa_dtype new_dtype,
+                            const dsa_cache* k, const dsa_cache* kv, void* stream) {
+    dsa_status s = check_batch(batch);
+    if (s != DSA_OK) return s;
+    if (k == nullptr || kv == nullptr) return DSA_ERR_NULL;
+    // pool format -> kernel kind (0 fp32, 1 bf16, 2 e4m3 + fp32 scale, 3 e4m3 + E8M0 scale), or -1
+    auto kind_of = [&](const dsa_cache* c) -> int {
+        if (c->dtype == DSA_F32 && c->scale_kind == DSA_SCALE_NONE) return new_dtype == DSA_F32 ? 0 : -1;
+        if (new_dtype != DSA_BF16) return -1;
+        if (c->dtype == DSA_BF16 && c->scale_kind == DSA_SCALE_NONE) return 1;
+        if (c->dtype != DSA_E4M3) return -1;
+        // groups are whole aligned lane groups of one wave: powers of two from 4 to 256
+        if (c->scale_kind == DSA_SCALE_F32 && c->group >= 4 && c->group <= 256 && (c->group & (c->group - 1)) == 0)
+            return 2;
+        if (c->scale_kind == DSA_SCALE_E8M0 && c->group == 32) return 3;
+        return -1;
+    };
+    const int kk = kind_of(k), kvk = kind_of(kv);
+    if (kk < 0 || kvk < 0) return DSA_ERR_UNSUPPORTED;
+    if (k->width < 4 || k->width % 4 != 0 || k->width > 256 || kv->width < 4 || kv->width % 4 != 0 ||
+        kv->width > 768 || k->num_blocks < 1 || kv->num_blocks < 1)
+        return DSA_ERR_SHAPE;
+    if (k->num_blocks * 64 > (int64_t)INT_MAX || kv->num_blocks * 64 > (int64_t)INT_MAX) return DSA_ERR_UNSUPPORTED;
+    if (batch->batch > 0 && (k_new == nullptr || kv_new == nullptr)) return DSA_ERR_NULL;
+    if (k->data == nullptr || kv->data == nullptr) return DSA_ERR_NULL;
+    if ((kk >= 2 && k->scales == nullptr) || (kvk >= 2 && kv->scales == nullptr)) return DSA_ERR_NULL;
+    dsa::AppendLaunch L{};
+    L.in_f32 = new_dtype == DSA_F32;
+    L.k_new = k_new;
+    L.kv_new = kv_new;
+    L.seq_lens = batch->seq_lens;
+    L.table = batch->block_table;
+    L.max_blocks = batch->max_blocks;
+    L.batch = batch->batch;
+    L.n_q = batch->n_q;
+    L.max_seq_len = batch->max_seq_len;
+    L.k_width = k->width;
+    L.k_kind = kk;
+    L.k_group = kk >= 2 ? k->group : 0;
+    L.k_blocks = k->num_blocks;
+    L.k_pool = const_cast<void*>(k->data);
+    L.k_scales = const_cast<void*>(k->scales);
+    L.kv_width = kv->width;
+    L.kv_kind = kvk;
+    L.kv_group = kvk >= 2 ? kv->group : 0;
+    L.kv_blocks = kv->num_blocks;
+    L.kv_pool = const_cast<void*>(kv->data);
+    L.kv_scales = const_cast<void*>(kv->scales);
+    return hip_status(dsa::launch_cache_append(L, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -55,7 +55,25 @@ struct AttnLaunch {
     int splits;
 };
 
+struct AppendLaunch {
+    bool in_f32;               // new values in fp32 (else bf16)
+    const void* k_new;         // [rows][k_width]
+    const void* kv_new;        // [rows][kv_width]
+    const int32_t* seq_lens;
+    const int32_t* table;
+    int max_blocks, batch, n_q, max_seq_len;
+    int k_width, k_kind, k_group;     // kind: 0 fp32, 1 bf16, 2 e4m3 + fp32 scale, 3 e4m3 + E8M0 scale
+    int64_t k_blocks;
+    void* k_pool;
+    void* k_scales;
+    int kv_width, kv_kind, kv_group;
+    int64_t kv_blocks;
+    void* kv_pool;
+    void* kv_scales;
+};
+
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st);
+hipError_t launch_cache_append(const AppendLaunch& a, hipStream_t st);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t st);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st);
 

@@ -248,3 +248,45 @@ def test_full_prefill_sampled_rows():
     assert (valid.sum(1) == k).all()
     assert (np.where(valid, idx_h, -1).max(1) < L).all()
     assert bool(torch.isfinite(out).all())
+
+
+# (config, overrides): the pool formats of every workload, with n_q 1 and 2
+APPEND = {
+    "f32": (1, dict(batch=2, n_q=3, lens=[150, 80])),
+    "bf16": (2, dict(batch=3, lens=[300, 1000, 453])),
+    "fp8_mx_kv": (5, dict(batch=3, lens=[300, 1000, 453])),
+    "mx_idx_fp32_kv": (6, dict(batch=2, n_q=2, lens=[700, 66])),
+}
+
+
+@pytest.mark.parametrize("case", list(APPEND))
+def test_cache_append_matches_oracle(case):
+    """dsa_cache_append on the GPU writes the same pools and scales as the oracle's append
+    (bit for bit), and leaves every other pool row as it was."""
+    cfg, kw = APPEND[case]
+    wl = make_workload(cfg, **kw)
+    say(f"[parity] append {case}: cfg {cfg} {kw}")
+    dev = B.DeviceInputs(wl)
+    rng = np.random.default_rng(11)
+    f32 = wl.idx_dtype == "f32"
+    k_new = (rng.standard_normal((wl.rows, wl.d_I)) / np.sqrt(wl.d_I)).astype(np.float32)
+    kv_new = (rng.standard_normal((wl.rows, wl.d_qk)) / np.sqrt(wl.d_qk)).astype(np.float32)
+    if not f32:  # the new rows arrive in bf16
+        k_new = torch.from_numpy(k_new).to(torch.bfloat16).float().numpy()
+        kv_new = torch.from_numpy(kv_new).to(torch.bfloat16).float().numpy()
+    dt = torch.float32 if f32 else torch.bfloat16
+    B.dsa_cache_append(dev, torch.from_numpy(k_new).to(dt).cuda(), torch.from_numpy(kv_new).to(dt).cuda())
+    torch.cuda.synchronize()
+    # the oracle on host copies of the same pools
+    kp, kvp = wl.k_pool.copy(), wl.kv_pool.copy()
+    ks = None if wl.k_scale is None else wl.k_scale.copy()
+    kvs = None if wl.kv_scale is None else wl.kv_scale.copy()
+    O.cache_append(wl, k_new, wl.idx_dtype, kp, ks)
+    O.cache_append(wl, kv_new, wl.kv_dtype, kvp, kvs)
+    assert not np.array_equal(kvp, wl.kv_pool)  # the append changed something
+    for name, got, ref in [("k_pool", dev.k_pool, kp), ("kv_pool", dev.kv_pool, kvp),
+                           ("k_scale", dev.k_scale, ks), ("kv_scale", dev.kv_scale, kvs)]:
+        if ref is None:
+            continue
+        g = got.cpu().numpy().reshape(ref.shape)
+        assert np.array_equal(g.view(np.uint8), np.ascontiguousarray(ref).view(np.uint8)), f"{case}: {name} differs"

@@ -441,3 +441,45 @@ def test_forward_with_full_topk_is_dense_attention():
         assert idx[r, :L[r]].tolist() == list(range(L[r]))
     dout, dlse = O.dense_attn(wl)
     np.testing.assert_allclose(out, dout, rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------------------ cache append pins
+
+def test_e4m3_encoder_matches_torch_conversion():
+    """The oracle's e4m3 encoder (written from the format's definition) against torch's
+    float8_e4m3fn conversion: random magnitudes over the whole range, every code, every
+    midpoint between neighbouring codes (the ties) and the subnormals."""
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([rng.standard_normal(20000).astype(np.float32) * s for s in (1e-3, 0.05, 1, 30, 300)])
+    codes = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+    fin = np.sort(codes[np.isfinite(codes)])
+    mids = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)
+    vals = np.clip(np.concatenate([vals, fin, mids, -mids, np.float32([2.0 ** -10, 3 * 2.0 ** -10, -0.0])]),
+                   -448, 448)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([O.f32_to_e4m3(v) for v in vals], np.uint8)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3_128", "mxfp8"])
+def test_cache_append_quantizes_like_the_input_generator(fmt):
+    """The oracle's append (C, fp32 decisions) and the seeded input generator's quantizers
+    (numpy + torch) are independent implementations of one rule: the appended rows must
+    hold the same codes and scales, bit for bit, and every other pool row stays unchanged."""
+    from sparse_attention_lightningindexer_amd.inputs import quantize_e4m3_f32scale, quantize_mxfp8
+    wl = make_workload(2, batch=3, n_q=2, lens=[300, 130, 65])
+    x = (np.random.default_rng(5).standard_normal((wl.rows, 576)).astype(np.float32) / 24)
+    x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()          # bf16 inputs
+    nrows = wl.num_blocks * 64
+    pool = np.zeros((nrows, 576), np.uint8)
+    scl = np.zeros((nrows, 5), np.float32) if fmt == "e4m3_128" else np.zeros((nrows, 18), np.uint8)
+    O.cache_append(wl, x, fmt, pool, scl)
+    codes, sref = quantize_e4m3_f32scale(x, 128) if fmt == "e4m3_128" else quantize_mxfp8(x, 32)
+    touched = np.zeros(nrows, bool)
+    for r in range(wl.rows):
+        b = r // wl.n_q
+        s = int(wl.row_lens()[r]) - 1
+        pr = int(wl.block_table[b, s // 64]) * 64 + s % 64
+        assert np.array_equal(pool[pr], codes[r]) and np.array_equal(scl[pr], sref[r])
+        touched[pr] = True
+    assert not pool[~touched].any() and not scl[~touched].any()
