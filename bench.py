@@ -320,6 +320,23 @@ def main():
                for a, c in zip(idx_q, idx_b)]
         res["topk_recall_vs_bf16"] = {"mean": float(np.mean(rec)), "min": float(np.min(rec)), "rows": len(rec)}
         del dev_b
+    # cache append (the step before the indexer): this step's index keys and
+    # latent rows written into the first input set's pools, quantized when the
+    # pool is; timed like the stages, after every other measurement (it
+    # overwrites those pool rows)
+    _, dev0, _, _ = sets[0]
+    k_new = torch.randn(wl0.rows, wl0.d_I, device="cuda").to(torch.bfloat16 if wl0.idx_dtype != "f32" else torch.float32)
+    kv_new = torch.randn(wl0.rows, wl0.d_qk, device="cuda").to(k_new.dtype)
+    B.dsa_cache_append(dev0, k_new, kv_new, stream=stream)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(600_000 * args.steps)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(args.steps):
+        B.dsa_cache_append(dev0, k_new, kv_new, stream=stream)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    res["append_us"] = a0.elapsed_time(a1) / args.steps * 1e3
     if args.copy_calib:
         src = torch.randn(args.copy_calib * 2 ** 18, device="cuda")
         dst = torch.empty_like(src)
