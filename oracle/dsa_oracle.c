@@ -36,7 +36,10 @@
  *  5. dense causal attention over all s < L_r (used only by invariants);
  *  6. cache append: this step's index keys and latent rows written into the
  *     paged pools, quantized in fp32 when the pool is (the quantizer's
- *     decisions are integer codes, so they are taken in the kernel's fp32).
+ *     decisions are integer codes, so they are taken in the kernel's fp32);
+ *  7. indexer prolog: the index query and head weights projected from the
+ *     hidden state and the new index key RMS-normalized, exactly in fp64
+ *     ([D] §4.2 "Three-Stream Coordination for Indexer Preprocessing").
  *
  * Paging ([A] §4 "Sparse attention read"; [D] §8 "Paged KV cache"): logical
  * position s of sequence b lives at pool row
@@ -447,6 +450,66 @@ int oracle_cache_append(int batch, int n_q, const int32_t* seq_lens, const int32
                                                    : (void*)((uint8_t*)scales + pr * ng);
             quantize_vector(x, width, scale_kind, group, codes, sc);
         }
+    }
+    return 0;
+}
+
+/* Exported for the tests: e4m3 codes of n floats (the encoder above). */
+int oracle_e4m3_encode(const float* x, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_e4m3(x[i]);
+    return 0;
+}
+
+/* ---------------------------------------------------------- indexer prolog */
+
+/* Indexer prolog ([D] §4.2 "Three-Stream Coordination for Indexer
+ * Preprocessing"; [A] §4 "Three-stream coordination in input preparation"):
+ * the inputs of the indexer made from each query token's hidden state x,
+ *   q[r][n]      = sum_c W_q[n][c] * x[r][c]     for n < n_heads*head_dim
+ *                  (the query projection, n = head*head_dim + channel)
+ *   head_w[r][j] = sum_c W_h[j][c] * x[r][c]     for j < n_heads
+ *                  (the head-weight projection)
+ *   k_norm[r][c] = k[r][c] * gain[c] / sqrt(mean_c' k[r][c']^2 + eps)
+ *                  (the RMS normalization of the new index key)
+ * in fp64 on the decoded bf16 inputs (x [rows][d_x], W_q [n_heads*head_dim]
+ * [d_x], W_h [n_heads][d_x], k [rows][head_dim]; gain fp32 [head_dim]).  The
+ * projections use bf16 operands as the pages keep them ([A] §5: projections
+ * stay BF16); quantizing q for the index path ([A] §5: MXFP8, one scale per
+ * 32) and rounding outputs to bf16 are decisions taken from these values. */
+int oracle_indexer_prolog(int rows, int d_x, const uint16_t* x, const uint16_t* w_q,
+                          const uint16_t* w_h, const uint16_t* k, const float* gain, double eps,
+                          int n_heads, int head_dim, double* q, double* head_w, double* k_norm) {
+    const int nq = n_heads * head_dim, ncols = nq + n_heads;
+    double* xd = (double*)malloc(sizeof(double) * (size_t)rows * (size_t)d_x);
+    if (!xd) return -1;
+    for (int64_t i = 0; i < (int64_t)rows * d_x; ++i) xd[i] = oracle_bf16_to_f64(x[i]);
+    #pragma omp parallel
+    {
+        double* wrow = (double*)malloc(sizeof(double) * (size_t)d_x);
+        #pragma omp for schedule(dynamic, 16)
+        for (int n = 0; n < ncols; ++n) {
+            const uint16_t* src = n < nq ? w_q + (int64_t)n * d_x : w_h + (int64_t)(n - nq) * d_x;
+            for (int c = 0; c < d_x; ++c) wrow[c] = oracle_bf16_to_f64(src[c]);
+            for (int r = 0; r < rows; ++r) {
+                double acc = 0.0;
+                for (int c = 0; c < d_x; ++c) acc += wrow[c] * xd[(int64_t)r * d_x + c];
+                if (n < nq) q[(int64_t)r * nq + n] = acc;
+                else head_w[(int64_t)r * n_heads + (n - nq)] = acc;
+            }
+        }
+        free(wrow);
+    }
+    free(xd);
+    for (int r = 0; r < rows; ++r) {
+        double ss = 0.0;
+        for (int c = 0; c < head_dim; ++c) {
+            double v = oracle_bf16_to_f64(k[(int64_t)r * head_dim + c]);
+            ss += v * v;
+        }
+        double inv = 1.0 / sqrt(ss / head_dim + eps);
+        for (int c = 0; c < head_dim; ++c)
+            k_norm[(int64_t)r * head_dim + c] =
+                oracle_bf16_to_f64(k[(int64_t)r * head_dim + c]) * (double)gain[c] * inv;
     }
     return 0;
 }

@@ -46,6 +46,8 @@ def lib():
         L.oracle_f32_to_e4m3.restype = C.c_uint8
         L.oracle_f32_to_e4m3.argtypes = [C.c_float]
         L.oracle_cache_append.argtypes = [i32, i32, p, p, i32, i64, p, i32, i32, i32, i32, p, p]
+        L.oracle_e4m3_encode.argtypes = [p, i64, p]
+        L.oracle_indexer_prolog.argtypes = [i32, i32, p, p, p, p, p, d, i32, i32, p, p, p]
         L.oracle_num_threads.restype = i32
         _lib = L
     return _lib
@@ -183,3 +185,24 @@ def cache_append(wl, x_new, fmt: str, pool, scales):
     assert pool.flags.c_contiguous and (scales is None or scales.flags.c_contiguous)
     lib().oracle_cache_append(wl.batch, wl.n_q, _ptr(seq), _ptr(tab), wl.max_blocks, wl.num_blocks,
                               _ptr(x), x.shape[1], _DT[fmt], kind, grp, _ptr(pool), _ptr(scales))
+
+
+def e4m3_encode(x):
+    """The oracle's e4m3 codes (uint8) of a float32 array, elementwise."""
+    v = _c(x, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().oracle_e4m3_encode(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def indexer_prolog(p):
+    """q [rows, H_I, d_I], head_w [rows, H_I] and k_norm [rows, d_I] (float64) of the
+    prolog inputs `p` (bf16 bit arrays x, w_q, w_h, k; fp32 gain; eps)."""
+    x, wq, wh, k = _c(p.x), _c(p.w_q), _c(p.w_h), _c(p.k)
+    gain = _c(p.gain, np.float32)
+    q = np.empty((p.rows, p.H_I, p.d_I), np.float64)
+    hw = np.empty((p.rows, p.H_I), np.float64)
+    kn = np.empty((p.rows, p.d_I), np.float64)
+    lib().oracle_indexer_prolog(p.rows, p.d_x, _ptr(x), _ptr(wq), _ptr(wh), _ptr(k), _ptr(gain),
+                                float(p.eps), p.H_I, p.d_I, _ptr(q), _ptr(hw), _ptr(kn))
+    return q, hw, kn

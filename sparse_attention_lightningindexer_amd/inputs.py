@@ -29,6 +29,13 @@ independent of each other and of the draw order):
                e = floor(log2(amax)) - 8, code = e4m3(clamp(x/2^e, +-448)),
                scale byte = e + 127.  The fp8 decode workload stores the
                latent KV this way; workload 6 stores q_I and k_I this way.
+* prolog    -- the indexer prolog's inputs (make_prolog): hidden states x ~
+               N(0, 1), the index-key rows k ~ N(0, 1) before normalization,
+               projection weights W_q ~ N(0, 1/(d_I*d_x)) and W_h ~
+               N(0, 1/(H_I*d_x)), so that the projections have the variances
+               of the indexer inputs above, all rounded to bf16; an fp32
+               normalization gain 1 + N(0, 0.01).  The hidden width d_x is not
+               given by the pages; the decode prolog workload takes 7168.
 * poison    -- when requested, every pool element that no valid position maps
                to (the tail of each sequence's last block, and the spare block)
                is NaN, so a kernel that reads outside the history shows it.
@@ -45,6 +52,7 @@ BLOCK = 64
 
 # tensor ids of the counter-keyed streams
 _T_LENS, _T_PERM, _T_QI, _T_KI, _T_W, _T_Q, _T_KV = 1, 2, 3, 4, 5, 6, 7
+_T_X, _T_WQ, _T_WH, _T_KNEW, _T_GAIN = 8, 9, 10, 11, 12
 
 #: The workloads: the tiny fp32 prefill, decode B=32 at 8k, prefill 32k,
 #: skewed long-context decode with 2 verify tokens, and fp8 decode B=64 at 16k.
@@ -354,3 +362,35 @@ def make_workload(cfg_id: int, *, seed: int | None = None, rotation: int = 0,
         q=np.ascontiguousarray(q), kv_pool=blocks(kv_pool), kv_scale=blocks(kv_scale),
     )
     return wl
+
+
+#: The indexer prolog of one decode step of the decode workload (32 query
+#: tokens), from a hidden state of width 7168.
+PROLOG = dict(name="prolog_decode_b32_dx7168", rows=32, d_x=7168, H_I=64, d_I=128, eps=1e-6, seed=7)
+
+
+@dataclass
+class PrologInputs:
+    rows: int
+    d_x: int
+    H_I: int
+    d_I: int
+    eps: float
+    x: np.ndarray      # uint16 bf16 bits [rows, d_x]
+    w_q: np.ndarray    # uint16 bf16 bits [H_I*d_I, d_x]
+    w_h: np.ndarray    # uint16 bf16 bits [H_I, d_x]
+    k: np.ndarray      # uint16 bf16 bits [rows, d_I]
+    gain: np.ndarray   # float32 [d_I]
+
+
+def make_prolog(rows: int, d_x: int = 7168, H_I: int = 64, d_I: int = 128, *, seed: int = 7,
+                rotation: int = 0, eps: float = 1e-6) -> PrologInputs:
+    """Seeded inputs of the indexer prolog (recipe in the module docstring)."""
+    bf = f32_to_bf16_bits
+    x = _normal((rows, d_x), 1.0, seed, rotation, _T_X, bf, np.uint16)
+    w_q = _normal((H_I * d_I, d_x), 1.0 / (d_I * d_x), seed, rotation, _T_WQ, bf, np.uint16)
+    w_h = _normal((H_I, d_x), 1.0 / (H_I * d_x), seed, rotation, _T_WH, bf, np.uint16)
+    k = _normal((rows, d_I), 1.0, seed, rotation, _T_KNEW, bf, np.uint16)
+    gain = (1.0 + _normal((d_I,), 0.01, seed, rotation, _T_GAIN)).astype(np.float32)
+    return PrologInputs(rows=rows, d_x=d_x, H_I=H_I, d_I=d_I, eps=eps, x=x.reshape(rows, d_x),
+                        w_q=w_q, w_h=w_h, k=k.reshape(rows, d_I), gain=gain)

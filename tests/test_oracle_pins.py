@@ -483,3 +483,94 @@ def test_cache_append_quantizes_like_the_input_generator(fmt):
         assert np.array_equal(pool[pr], codes[r]) and np.array_equal(scl[pr], sref[r])
         touched[pr] = True
     assert not pool[~touched].any() and not scl[~touched].any()
+
+
+# ------------------------------------------------------------ indexer prolog pins
+
+def _bf16_f64(bits):
+    """torch's bf16 decoder, independent of the oracle's."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def test_vector_e4m3_encoder_matches_torch_conversion():
+    rng = np.random.default_rng(3)
+    vals = np.clip(np.concatenate([rng.standard_normal(50000).astype(np.float32) * s for s in (0.01, 1, 100)]),
+                   -448, 448)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(vals), ref)
+
+
+def test_prolog_projections_match_fp64_matmul():
+    """q and the head weights are fp64 matrix products of the decoded bf16 operands
+    (numpy's matmul on torch-decoded values); q's channel n of the flat projection is
+    head n // d_I, channel n % d_I."""
+    from sparse_attention_lightningindexer_amd.inputs import make_prolog
+    p = make_prolog(5, d_x=256, H_I=4, d_I=32, seed=11)
+    q, hw, _ = O.indexer_prolog(p)
+    x = _bf16_f64(p.x)
+    qref = (x @ _bf16_f64(p.w_q).T).reshape(5, 4, 32)
+    href = x @ _bf16_f64(p.w_h).T
+    np.testing.assert_allclose(q, qref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(hw, href, rtol=1e-12, atol=1e-14)
+
+
+def test_prolog_one_hot_hidden_state_selects_weight_columns():
+    """A hidden state that is the unit vector e_c projects to column c of each weight
+    matrix, exactly."""
+    from sparse_attention_lightningindexer_amd.inputs import make_prolog
+    p = make_prolog(3, d_x=128, H_I=2, d_I=64, seed=12)
+    cols = [0, 77, 127]
+    p.x[:] = 0
+    for r, c in enumerate(cols):
+        p.x[r, c] = np.uint16(0x3F80)       # bf16 1.0
+    q, hw, _ = O.indexer_prolog(p)
+    wq, wh = _bf16_f64(p.w_q), _bf16_f64(p.w_h)
+    for r, c in enumerate(cols):
+        assert np.array_equal(q[r].reshape(-1), wq[:, c])
+        assert np.array_equal(hw[r], wh[:, c])
+
+
+def test_prolog_rmsnorm_worked_example():
+    """k = (3, 4), gain (1, 2): the mean square is 12.5, so k_norm = (3, 8)/sqrt(12.5 + eps):
+    (0.848528137423857, 2.262741699796952) at eps = 0 and
+    (0.8320502943378437, 2.2188007849009166) at eps = 0.5."""
+    from sparse_attention_lightningindexer_amd.inputs import make_prolog
+    for eps, want in ((0.0, (0.848528137423857, 2.262741699796952)),
+                      (0.5, (0.8320502943378437, 2.2188007849009166))):
+        p = make_prolog(1, d_x=128, H_I=1, d_I=2, seed=13, eps=eps)
+        p.k[0] = np.array([0x4040, 0x4080], np.uint16)      # bf16 3.0, 4.0
+        p.gain[:] = (1.0, 2.0)
+        _, _, kn = O.indexer_prolog(p)
+        np.testing.assert_allclose(kn[0], want, rtol=1e-14)
+
+
+def test_prolog_rmsnorm_invariants():
+    """With gain 1: the output's mean square is ms/(ms + eps) (1 at eps = 0); doubling k
+    (exact in bf16) or flipping its sign scales nothing but the sign; the gain multiplies
+    channelwise."""
+    from sparse_attention_lightningindexer_amd.inputs import make_prolog
+    p = make_prolog(6, d_x=128, H_I=1, d_I=128, seed=14, eps=0.0)
+    g = p.gain.copy()
+    p.gain[:] = 1.0
+    _, _, kn = O.indexer_prolog(p)
+    np.testing.assert_allclose((kn ** 2).mean(axis=1), 1.0, rtol=1e-13)
+    k = _bf16_f64(p.k)
+    p2 = copy.deepcopy(p)
+    p2.k = (p.k.astype(np.uint32) + (1 << 7)).astype(np.uint16)   # exponent + 1: k * 2
+    p2.k[p.k & 0x7F80 == 0] = p.k[p.k & 0x7F80 == 0]               # leave zeros/subnormals alone
+    assert np.array_equal(_bf16_f64(p2.k)[k != 0], 2 * k[k != 0])
+    _, _, kn2 = O.indexer_prolog(p2)
+    np.testing.assert_allclose(kn2, kn, rtol=1e-14, atol=1e-300)
+    p3 = copy.deepcopy(p)
+    p3.k = p.k ^ np.uint16(0x8000)
+    _, _, kn3 = O.indexer_prolog(p3)
+    assert np.array_equal(kn3, -kn)
+    p4 = copy.deepcopy(p)
+    p4.gain[:] = g
+    _, _, kn4 = O.indexer_prolog(p4)
+    np.testing.assert_allclose(kn4, kn * g.astype(np.float64), rtol=1e-14)
+    p5 = copy.deepcopy(p)
+    p5.eps = 0.25
+    _, _, kn5 = O.indexer_prolog(p5)
+    ms = (k ** 2).mean(axis=1)
+    np.testing.assert_allclose((kn5 ** 2).mean(axis=1), ms / (ms + 0.25), rtol=1e-13)
