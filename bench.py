@@ -140,6 +140,44 @@ def traffic_summary(stage: str, workload: str, fetch_dir: str, write_dir: str, c
     return rec
 
 
+def prolog_bytes(rows, d_x, H_I, d_I, mx):
+    """Algorithmic HBM bytes of one indexer prolog: both weight matrices, the hidden
+    states and keys read once, and every output written once."""
+    reads = 2 * (H_I * d_I + H_I) * d_x + 2 * rows * d_x + 2 * rows * d_I + 4 * d_I
+    writes = rows * H_I * d_I * (1 if mx else 2) + (rows * H_I * d_I // 32 if mx else 0) + 4 * rows * H_I \
+        + 2 * rows * d_I
+    return reads + writes
+
+
+def time_prolog(wl0, args, stream):
+    """The indexer prolog for this workload's query rows from a hidden state of width
+    7168: 3 weight sets rotating (356 MB, more than the Infinity Cache), K launches
+    between two events after a spin, like the stages."""
+    import torch
+    from sparse_attention_lightningindexer_amd import binding as B
+    from sparse_attention_lightningindexer_amd.inputs import PROLOG, make_prolog
+    fmt = "mxfp8" if wl0.idx_dtype == "mxfp8" else "bf16"
+    pds, outs = [], []
+    for s in range(3):
+        p = make_prolog(wl0.rows, PROLOG["d_x"], wl0.H_I, wl0.d_I, seed=PROLOG["seed"], rotation=s,
+                        eps=PROLOG["eps"])
+        pds.append(B.PrologDevice(p))
+        outs.append(B.dsa_indexer_prolog(pds[-1], fmt, stream=stream))
+    torch.cuda.synchronize()
+    torch.cuda._sleep(600_000 * args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        B.dsa_indexer_prolog(pds[i % 3], fmt, outs=outs[i % 3], stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    nb = prolog_bytes(wl0.rows, PROLOG["d_x"], wl0.H_I, wl0.d_I, fmt == "mxfp8")
+    ach = nb / (us * 1e-6) / 1e9
+    return {"us": us, "rows": wl0.rows, "d_x": PROLOG["d_x"], "q_format": fmt, "algorithmic_bytes": nb,
+            "achieved_GBs": ach, "frac_hbm": ach / HBM_PEAK_GBS}
+
+
 def cpu_baseline(wl, budget_s: float):
     """The oracle as it stands, on the host's cores, over a bounded sample of rows."""
     import numpy as np
@@ -337,6 +375,8 @@ def main():
     a1.record(stream)
     torch.cuda.synchronize()
     res["append_us"] = a0.elapsed_time(a1) / args.steps * 1e3
+    if wl0.rows <= 256:
+        res["prolog"] = time_prolog(wl0, args, stream)
     if args.copy_calib:
         src = torch.randn(args.copy_calib * 2 ** 18, device="cuda")
         dst = torch.empty_like(src)

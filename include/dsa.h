@@ -245,6 +245,50 @@ dsa_status dsa_cache_append(const dsa_batch* batch, const void* k_new, const voi
                             dsa_dtype new_dtype, const dsa_cache* k, const dsa_cache* kv,
                             void* stream);
 
+/* Indexer prolog inputs and outputs ([D] §4.2 "Three-Stream Coordination for
+ * Indexer Preprocessing"; [A] §4 "Three-stream coordination in input
+ * preparation"): what the indexer of one step needs, made from each query
+ * token's hidden state. */
+typedef struct {
+    int32_t rows;               /* query tokens (0: nothing to do)                 */
+    int32_t d_x;                /* hidden width: a positive multiple of 128        */
+    int32_t n_heads;            /* H_I >= 1                                        */
+    int32_t head_dim;           /* d_I: a multiple of 32, at most 256              */
+    const void* x;              /* device bf16 [rows][d_x]: hidden states          */
+    const void* w_q;            /* device bf16 [n_heads*head_dim][d_x]             */
+    const void* w_h;            /* device bf16 [n_heads][d_x]                      */
+    const void* k;              /* device bf16 [rows][head_dim]: new index keys    */
+    const float* k_gain;        /* device fp32 [head_dim]: normalization gain      */
+    float eps;                  /* normalization epsilon, finite and >= 0          */
+    dsa_dtype q_dtype;          /* BF16, or E4M3 with E8M0 scales per 32 (MXFP8)   */
+    void* q_out;                /* device [rows][n_heads][head_dim] in q_dtype     */
+    void* q_scale_out;          /* device E8M0 [rows][n_heads][head_dim/32] (E4M3) */
+    float* head_w_out;          /* device fp32 [rows][n_heads]                     */
+    void* k_out;                /* device bf16 [rows][head_dim]: normalized keys   */
+} dsa_prolog_args;
+
+/*
+ * dsa_indexer_prolog -- the indexer's input preparation ([D] §4.2: query
+ * projection, key normalization, query quantization and head-weight
+ * projection, the independent ones overlapped; [A] §5: projections in BF16,
+ * the index query in MXFP8 with one scale per 32 elements).
+ *
+ *   q[r][n]      = sum_c w_q[n][c] * x[r][c]    (n = head*head_dim + channel)
+ *   head_w[r][j] = sum_c w_h[j][c] * x[r][c]
+ *   k_out[r][c]  = k[r][c] * k_gain[c] / sqrt(mean_c' k[r][c']^2 + eps)
+ *
+ * Projections accumulate in fp32.  q is stored nearest-even in BF16, or as
+ * MXFP8 from the fp32 values: per 32 channels e = floor(log2 amax) - 8 (-127
+ * when amax = 0, clamped to [-127, 127]), code = e4m3(x * 2^-e) with the
+ * quotient clamped to +-448 (nearest, ties to even), scale byte e + 127 --
+ * the layout dsa_indexer_args takes for an E4M3 query with E8M0 scales.
+ * k_out is rounded nearest-even to BF16 and is what dsa_cache_append stores
+ * as the index key.  All branches run in one launch on `stream`.  Alignment
+ * (else SHAPE): x, w_q and w_h 16 bytes, q_out 8, head_w_out and k_gain 4,
+ * k and k_out 2.  Errors: NULL, SHAPE, UNSUPPORTED, HIP.
+ */
+dsa_status dsa_indexer_prolog(const dsa_prolog_args* p, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

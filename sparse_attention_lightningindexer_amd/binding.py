@@ -10,6 +10,8 @@ Functions with the C names:
     dsa_topk(dev, scores, top_k=None)             -> indices int32 [rows, top_k]
     dsa_sparse_attn(dev, indices, top_k=None)     -> (out, lse)
     dsa_forward(dev, top_k=None, indices_out=...) -> (out, lse, indices)
+    dsa_cache_append(dev, k_new, kv_new)
+    dsa_indexer_prolog(pd, q_fmt)                 -> (q, q_scale, head_w, k_norm)
 and their *_workspace_bytes queries, where `dev` is a DeviceInputs (device
 copies of a Workload plus the ABI structs that point at them).
 """
@@ -58,12 +60,19 @@ class dsa_attn_args(C.Structure):
                 ("sm_scale", C.c_float), ("kv", dsa_cache), ("out", C.c_void_p), ("lse", C.c_void_p)]
 
 
+class dsa_prolog_args(C.Structure):
+    _fields_ = [("rows", C.c_int32), ("d_x", C.c_int32), ("n_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("x", C.c_void_p), ("w_q", C.c_void_p), ("w_h", C.c_void_p), ("k", C.c_void_p),
+                ("k_gain", C.c_void_p), ("eps", C.c_float), ("q_dtype", C.c_int), ("q_out", C.c_void_p),
+                ("q_scale_out", C.c_void_p), ("head_w_out", C.c_void_p), ("k_out", C.c_void_p)]
+
+
 _lib = None
 
 #: every entry point include/dsa.h declares
 EXPORTS = ("dsa_status_string", "dsa_version", "dsa_indexer_scores", "dsa_topk_workspace_bytes",
            "dsa_topk", "dsa_sparse_attn_workspace_bytes", "dsa_sparse_attn",
-           "dsa_forward_workspace_bytes", "dsa_forward", "dsa_cache_append")
+           "dsa_forward_workspace_bytes", "dsa_forward", "dsa_cache_append", "dsa_indexer_prolog")
 
 
 def lib():
@@ -95,6 +104,8 @@ def lib():
         L.dsa_cache_append.restype = C.c_int
         L.dsa_cache_append.argtypes = [P(dsa_batch), C.c_void_p, C.c_void_p, C.c_int, P(dsa_cache), P(dsa_cache),
                                        C.c_void_p]
+        L.dsa_indexer_prolog.restype = C.c_int
+        L.dsa_indexer_prolog.argtypes = [P(dsa_prolog_args), C.c_void_p]
         L.dsa_forward.restype = C.c_int
         L.dsa_forward.argtypes = [P(dsa_batch), P(dsa_indexer_args), P(dsa_attn_args), C.c_int32, C.c_void_p,
                                   C.c_void_p, S, C.c_void_p]
@@ -244,3 +255,37 @@ def dsa_cache_append(dev: DeviceInputs, k_new, kv_new, stream=None):
     new_dt = DSA_F32 if k_new.dtype == torch.float32 else DSA_BF16
     _check(lib().dsa_cache_append(C.byref(dev.batch), _ptr(k_new), _ptr(kv_new), new_dt, C.byref(dev.idx.k),
                                   C.byref(dev.attn.kv), _stream(stream)), "dsa_cache_append")
+
+
+class PrologDevice:
+    """Device copies of the indexer prolog's inputs (a PrologInputs)."""
+
+    def __init__(self, p, device="cuda"):
+        self.p = p
+        self.x = _dev(p.x, device)
+        self.w_q = _dev(p.w_q, device)
+        self.w_h = _dev(p.w_h, device)
+        self.k = _dev(p.k, device)
+        self.gain = _dev(p.gain.astype(np.float32), device)
+
+
+def dsa_indexer_prolog(pd: PrologDevice, q_fmt: str = "bf16", outs=None, stream=None):
+    """q [rows, H_I, d_I] (bf16 bits as int16, or e4m3 codes as uint8 for q_fmt "mxfp8"),
+    q_scale (E8M0 bytes [rows, H_I, d_I/32], or None), head_w fp32 [rows, H_I] and
+    k_norm (bf16 bits as int16) [rows, d_I].  `outs` reuses those four tensors."""
+    p, dev = pd.p, pd.x.device
+    mx = q_fmt == "mxfp8"
+    if q_fmt not in ("bf16", "mxfp8"):
+        raise ValueError(f"prolog query format {q_fmt!r}: bf16 or mxfp8")
+    if outs is None:
+        q = torch.empty((p.rows, p.H_I, p.d_I), dtype=torch.uint8 if mx else torch.int16, device=dev)
+        qs = torch.empty((p.rows, p.H_I, p.d_I // 32), dtype=torch.uint8, device=dev) if mx else None
+        hw = torch.empty((p.rows, p.H_I), dtype=torch.float32, device=dev)
+        kn = torch.empty((p.rows, p.d_I), dtype=torch.int16, device=dev)
+    else:
+        q, qs, hw, kn = outs
+    args = dsa_prolog_args(p.rows, p.d_x, p.H_I, p.d_I, pd.x.data_ptr(), pd.w_q.data_ptr(), pd.w_h.data_ptr(),
+                           pd.k.data_ptr(), pd.gain.data_ptr(), float(p.eps), DSA_E4M3 if mx else DSA_BF16,
+                           q.data_ptr(), None if qs is None else qs.data_ptr(), hw.data_ptr(), kn.data_ptr())
+    _check(lib().dsa_indexer_prolog(C.byref(args), _stream(stream)), "dsa_indexer_prolog")
+    return q, qs, hw, kn

@@ -15,6 +15,7 @@ namespace {
 
 constexpr int kMaxTopK = 4096;
 constexpr size_t kAlign = 256;
+constexpr int kPrologChunk = 128;  // the prolog's hidden width must be a multiple of this
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -297,6 +298,42 @@ dsa_status dsa_cache_append(const dsa_batch* batch, const void* k_new, const voi
     L.kv_pool = const_cast<void*>(kv->data);
     L.kv_scales = const_cast<void*>(kv->scales);
     return hip_status(dsa::launch_cache_append(L, (hipStream_t)stream));
+}
+
+dsa_status dsa_indexer_prolog(const dsa_prolog_args* p, void* stream) {
+    if (p == nullptr) return DSA_ERR_NULL;
+    if (p->rows < 0 || p->d_x < kPrologChunk || p->d_x % kPrologChunk != 0 || p->n_heads < 1 || p->head_dim < 32 ||
+        p->head_dim % 32 != 0 || p->head_dim > 256 || !(p->eps >= 0.f) || p->eps > 3.0e38f)
+        return DSA_ERR_SHAPE;
+    if ((int64_t)p->n_heads * p->head_dim > (int64_t)INT_MAX / 2 || (int64_t)p->rows * p->d_x > (int64_t)INT_MAX * 64)
+        return DSA_ERR_SHAPE;
+    if (p->q_dtype != DSA_BF16 && p->q_dtype != DSA_E4M3) return DSA_ERR_UNSUPPORTED;
+    if (p->rows == 0) return DSA_OK;
+    if (p->x == nullptr || p->w_q == nullptr || p->w_h == nullptr || p->k == nullptr || p->k_gain == nullptr ||
+        p->q_out == nullptr || p->head_w_out == nullptr || p->k_out == nullptr ||
+        (p->q_dtype == DSA_E4M3 && p->q_scale_out == nullptr))
+        return DSA_ERR_NULL;
+    // the projections' operands are read 16 bytes at a time; q is stored up to 8 bytes at a time
+    if (((uintptr_t)p->x | (uintptr_t)p->w_q | (uintptr_t)p->w_h) % 16 != 0 || (uintptr_t)p->q_out % 8 != 0 ||
+        ((uintptr_t)p->head_w_out | (uintptr_t)p->k_gain) % 4 != 0 || ((uintptr_t)p->k | (uintptr_t)p->k_out) % 2 != 0)
+        return DSA_ERR_SHAPE;
+    dsa::PrologLaunch L{};
+    L.x = static_cast<const uint16_t*>(p->x);
+    L.w_q = static_cast<const uint16_t*>(p->w_q);
+    L.w_h = static_cast<const uint16_t*>(p->w_h);
+    L.k = static_cast<const uint16_t*>(p->k);
+    L.gain = p->k_gain;
+    L.eps = p->eps;
+    L.rows = p->rows;
+    L.d_x = p->d_x;
+    L.H_I = p->n_heads;
+    L.d_I = p->head_dim;
+    L.q_mx = p->q_dtype == DSA_E4M3;
+    L.q_out = p->q_out;
+    L.q_scale = static_cast<uint8_t*>(p->q_scale_out);
+    L.head_w = p->head_w_out;
+    L.k_norm = static_cast<uint16_t*>(p->k_out);
+    return hip_status(dsa::launch_indexer_prolog(L, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -72,7 +72,23 @@ struct AppendLaunch {
     void* kv_scales;
 };
 
+struct PrologLaunch {
+    const uint16_t* x;         // bf16 [rows][d_x]
+    const uint16_t* w_q;       // bf16 [H_I*d_I][d_x]
+    const uint16_t* w_h;       // bf16 [H_I][d_x]
+    const uint16_t* k;         // bf16 [rows][d_I]
+    const float* gain;         // fp32 [d_I]
+    float eps;
+    int rows, d_x, H_I, d_I;
+    bool q_mx;                 // q as e4m3 + E8M0 per 32 (else bf16)
+    void* q_out;               // [rows][H_I*d_I]
+    uint8_t* q_scale;          // [rows][H_I*d_I/32] when q_mx
+    float* head_w;             // [rows][H_I]
+    uint16_t* k_norm;          // bf16 [rows][d_I]
+};
+
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st);
+hipError_t launch_indexer_prolog(const PrologLaunch& a, hipStream_t st);
 hipError_t launch_cache_append(const AppendLaunch& a, hipStream_t st);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t st);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st);

@@ -137,3 +137,84 @@ def gpu_all(wl, dev=None):
     out, lse = B.dsa_sparse_attn(dev, idx)
     torch.cuda.synchronize()
     return dev, sc.cpu().numpy().astype(np.float64), idx.cpu().numpy(), f64(out), f64(lse)
+
+
+# ------------------------------------------------------------ indexer prolog
+
+_U = 2.0 ** -24
+
+
+def _bf16_bits_f64(bits) -> np.ndarray:
+    b = np.ascontiguousarray(bits)
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def _to_bf16_f64(v: np.ndarray) -> np.ndarray:
+    """Nearest-even bf16 of float32(v) (monotone in v), as float64."""
+    return torch.from_numpy(np.ascontiguousarray(v, np.float64).astype(np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def prolog_bound(p) -> tuple:
+    """Forward error bounds of the prolog's fp32 projections: along any path of the
+    kernel's sums a result passes at most n = 32 (inside one MFMA) + 4*ceil(d_x/1024)
+    (a wave's MFMA chain) + 8 (the waves' partials) + 4 additions, so
+        |v_gpu - v| <= n * 2^-24 * sum_c |w_nc x_rc| + 2^-24 |v|."""
+    x = np.abs(_bf16_bits_f64(p.x))
+    n = 32 + 4 * -(-p.d_x // 1024) + 8 + 4
+    sq = n * _U * (x @ np.abs(_bf16_bits_f64(p.w_q)).T)
+    sh = n * _U * (x @ np.abs(_bf16_bits_f64(p.w_h)).T)
+    return sq.reshape(p.rows, p.H_I, p.d_I), sh
+
+
+def _mx_exponent(a: np.ndarray) -> np.ndarray:
+    """floor(log2 a) - 8, -127 for a = 0, clamped to [-127, 127] (monotone in a)."""
+    m, e2 = np.frexp(a)
+    e = np.where(a > 0, e2.astype(np.int64) - 1 - 8, -127)
+    return np.clip(e, -127, 127)
+
+
+def check_prolog(p, q_fmt, q_gpu, qs_gpu, hw_gpu, kn_gpu, ref):
+    """GPU prolog outputs against the oracle's fp64 values: every stored value must be
+    one that the kernel's rounding rule gives for some fp32 result within the forward
+    error bound (an interval check: bf16 and e4m3 rounding are monotone), and the
+    E8M0 exponent must lie between those of the bound's smallest and largest amax."""
+    q64, hw64, kn64 = ref
+    bq, bh = prolog_bound(p)
+    lo, hi = q64 - bq - _U * np.abs(q64), q64 + bq + _U * np.abs(q64)
+    # head weights, fp32
+    d = np.abs(hw_gpu.astype(np.float64) - hw64)
+    assert (d <= bh + 2 * _U * np.abs(hw64)).all(), f"head_w: worst excess {np.max(d - bh)}"
+    # normalized keys, bf16: fp32 sum of squares, square root, division, two products
+    kn = _bf16_bits_f64(kn_gpu)
+    rel = (2 * p.d_I + 16) * _U
+    klo, khi = kn64 - rel * np.abs(kn64), kn64 + rel * np.abs(kn64)
+    assert ((kn >= _to_bf16_f64(klo)) & (kn <= _to_bf16_f64(khi))).all(), "k_norm outside its interval"
+    if q_fmt == "bf16":
+        qg = _bf16_bits_f64(q_gpu)
+        ok = (qg >= _to_bf16_f64(lo)) & (qg <= _to_bf16_f64(hi))
+        assert ok.all(), f"q (bf16): {np.count_nonzero(~ok)} values outside their interval"
+        return
+    # MXFP8: one exponent per 32 channels
+    g = 32
+    shp = (p.rows, p.H_I, p.d_I // g, g)
+    lo_g, hi_g = lo.reshape(shp), hi.reshape(shp)
+    amax_hi = np.maximum(np.abs(lo_g), np.abs(hi_g)).max(axis=-1)
+    amin_each = np.where((lo_g <= 0) & (hi_g >= 0), 0.0, np.minimum(np.abs(lo_g), np.abs(hi_g)))
+    amax_lo = amin_each.max(axis=-1)
+    e_gpu = qs_gpu.astype(np.int64) - 127
+    e_lo = _mx_exponent(amax_lo.astype(np.float32).astype(np.float64))
+    e_hi = _mx_exponent(amax_hi.astype(np.float32).astype(np.float64))
+    ok_e = (e_gpu >= e_lo) & (e_gpu <= e_hi)
+    assert ok_e.all(), f"q scale: {np.count_nonzero(~ok_e)} E8M0 exponents outside their range"
+    sc = np.ldexp(1.0, -e_gpu)[..., None]
+
+    def enc(v):
+        w = np.clip((v.astype(np.float32).astype(np.float64) * sc), -448, 448).astype(np.float32)
+        return O.dequant(O.e4m3_encode(w).reshape(-1, 1), "e4m3")[:, 0].reshape(shp)
+
+    got = O.dequant(np.ascontiguousarray(q_gpu).reshape(-1, 1), "e4m3")[:, 0].reshape(shp)
+    ok = (got >= enc(lo_g)) & (got <= enc(hi_g))
+    assert ok.all(), f"q (MXFP8): {np.count_nonzero(~ok)} codes outside their interval"
+    # the interval check is tight: nearly every code equals the one of the fp64 value
+    same = got == enc(q64.reshape(shp))
+    assert same.mean() > 0.99, same.mean()

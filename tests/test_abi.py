@@ -111,3 +111,27 @@ def test_workspace_sizes_follow_the_split_rule():
     batch, idx, attn = _fake_structs(wl)
     assert lib.dsa_sparse_attn_workspace_bytes(C.byref(batch), C.byref(attn), 2048) == 0
     assert lib.dsa_topk_workspace_bytes(C.byref(batch), 2048) == 0
+
+
+def test_prolog_validation_errors_are_returned_before_any_launch():
+    lib = B.lib()
+    fake = 0x10000
+    ok = dict(rows=32, d_x=7168, n_heads=64, head_dim=128, x=fake, w_q=fake, w_h=fake, k=fake, k_gain=fake,
+              eps=1e-6, q_dtype=B.DSA_E4M3, q_out=fake, q_scale_out=fake, head_w_out=fake, k_out=fake)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.dsa_indexer_prolog(C.byref(B.dsa_prolog_args(**a)), None)
+
+    assert lib.dsa_indexer_prolog(None, None) == B.DSA_ERR_NULL
+    assert call(rows=0) == B.DSA_OK                       # nothing to do, nothing launched
+    for bad in (dict(rows=-1), dict(d_x=0), dict(d_x=7168 + 64), dict(head_dim=48), dict(head_dim=288),
+                dict(n_heads=0), dict(eps=-1.0), dict(eps=float("nan")), dict(eps=float("inf")),
+                dict(x=fake + 8), dict(w_q=fake + 2), dict(q_out=fake + 4), dict(head_w_out=fake + 2),
+                dict(k_out=fake + 1)):
+        assert call(**bad) == B.DSA_ERR_SHAPE, bad
+    for bad in (dict(q_dtype=B.DSA_F32), dict(q_dtype=7)):
+        assert call(**bad) == B.DSA_ERR_UNSUPPORTED, bad
+    for name in ("x", "w_q", "w_h", "k", "k_gain", "q_out", "q_scale_out", "head_w_out", "k_out"):
+        assert call(**{name: None}) == B.DSA_ERR_NULL, name

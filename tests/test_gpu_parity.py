@@ -290,3 +290,70 @@ def test_cache_append_matches_oracle(case):
             continue
         g = got.cpu().numpy().reshape(ref.shape)
         assert np.array_equal(g.view(np.uint8), np.ascontiguousarray(ref).view(np.uint8)), f"{case}: {name} differs"
+
+
+# (rows, d_x, H_I, d_I, query format): one row and one k chunk; ragged row tiles
+# of every tile height (16, 32, 64 rows); fewer k chunks than waves and uneven
+# chunk counts per wave; head columns that do not fill a tile (H_I 4 and 40);
+# the decode prolog workload (32 rows, d_x 7168) in both formats.
+PROLOG = {
+    "r1_dx128_mx": (1, 128, 64, 128, "mxfp8"),
+    "r5_dx1024_bf16": (5, 1024, 64, 128, "bf16"),
+    "r17_dx896_mx": (17, 896, 64, 128, "mxfp8"),
+    "r70_dx1152_h4_mx": (70, 1152, 4, 32, "mxfp8"),
+    "r130_dx256_h40_bf16": (130, 256, 40, 64, "bf16"),
+    "decode_b32_dx7168_mx": (32, 7168, 64, 128, "mxfp8"),
+    "decode_b32_dx7168_bf16": (32, 7168, 64, 128, "bf16"),
+}
+
+
+@pytest.mark.parametrize("case", list(PROLOG))
+def test_indexer_prolog_matches_oracle(case):
+    """dsa_indexer_prolog against the oracle's fp64 projections and normalization, by
+    the interval rule of check_prolog; then the same call again into the same
+    buffers gives the same bytes (no state kept between calls)."""
+    from sparse_attention_lightningindexer_amd.inputs import make_prolog
+    from parity import check_prolog
+    rows, d_x, H_I, d_I, fmt = PROLOG[case]
+    say(f"[parity] prolog {case}: rows {rows} d_x {d_x} H_I {H_I} d_I {d_I} {fmt}")
+    p = make_prolog(rows, d_x, H_I, d_I, seed=21 + rows)
+    pd = B.PrologDevice(p)
+    outs = B.dsa_indexer_prolog(pd, fmt)
+    torch.cuda.synchronize()
+    host = [None if t is None else t.cpu().numpy() for t in outs]
+    check_prolog(p, fmt, host[0].reshape(rows, H_I, d_I) if fmt == "bf16" else host[0],
+                 None if host[1] is None else host[1], host[2], host[3], O.indexer_prolog(p))
+    for t in outs:
+        if t is not None:
+            t.fill_(0x55)
+    B.dsa_indexer_prolog(pd, fmt, outs=outs)
+    torch.cuda.synchronize()
+    for a, t in zip(host, outs):
+        if t is not None:
+            assert np.array_equal(a, t.cpu().numpy())
+
+
+def test_indexer_prolog_zero_inputs_and_feeds_the_indexer():
+    """A zero hidden state gives q = 0 (E8M0 byte 0, codes 0) and head weights 0; a zero
+    key gives a zero normalized key.  The prolog's MXFP8 query and head weights then
+    drive dsa_indexer_scores like the same values written by the input generator."""
+    from sparse_attention_lightningindexer_amd.inputs import make_prolog
+    say("[parity] prolog zero inputs and indexer hand-off")
+    p = make_prolog(4, 256, 64, 128, seed=5)
+    p.x[1] = 0
+    p.k[2] = 0
+    q, qs, hw, kn = B.dsa_indexer_prolog(B.PrologDevice(p), "mxfp8")
+    torch.cuda.synchronize()
+    assert not q[1].any() and not qs[1].any() and not hw[1].any()
+    assert not kn[2].any()
+    # hand-off: a decode workload of 4 sequences whose index query and head weights
+    # are the prolog's outputs
+    wl = make_workload(6, batch=4, lens=[300, 129, 64, 1000])
+    wl.q_idx = q.cpu().numpy().reshape(wl.q_idx.shape)
+    wl.q_idx_scale = qs.cpu().numpy().reshape(wl.q_idx_scale.shape)
+    wl.head_w = hw.cpu().numpy().reshape(wl.head_w.shape)
+    dev = B.DeviceInputs(wl)
+    sc = B.dsa_indexer_scores(dev)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.rows, dtype=np.int32)
+    check_scores(wl, sc.cpu().numpy().astype(np.float64), O.indexer_scores(wl, rows), rows)
