@@ -15,7 +15,7 @@ namespace {
 
 constexpr int kMaxTopK = 4096;
 constexpr size_t kAlign = 256;
-constexpr int kPrologChunk = 128;  // the prolog's hidden width must be a multiple of this
+constexpr int kPrologChunk = 256;  // the prolog's hidden width must be a multiple of this
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
