@@ -66,7 +66,8 @@ def source_hash(files):
 
 
 # kernels of each stage, by name, as rocprofv3 reports them
-STAGE_KERNELS = {"indexer": ("indexer_",), "topk": ("topk_",), "attention": ("sfa_",)}
+STAGE_KERNELS = {"indexer": ("indexer_f32_kernel", "indexer_decode_kernel", "indexer_prefill_kernel"),
+                 "topk": ("topk_",), "attention": ("sfa_",), "prolog": ("indexer_prolog_kernel",)}
 COPY_KERNEL = "neg_kernel"  # the plain copy used to calibrate the byte counters
 
 KERNEL_SOURCES = {
@@ -76,6 +77,8 @@ KERNEL_SOURCES = {
              "sparse_attention_lightningindexer_amd/csrc/common.hpp"],
     "attention": ["sparse_attention_lightningindexer_amd/csrc/sfa.hip",
                   "sparse_attention_lightningindexer_amd/csrc/common.hpp"],
+    "prolog": ["sparse_attention_lightningindexer_amd/csrc/prolog.hip",
+               "sparse_attention_lightningindexer_amd/csrc/common.hpp"],
 }
 
 
@@ -175,7 +178,8 @@ def time_prolog(wl0, args, stream):
     nb = prolog_bytes(wl0.rows, PROLOG["d_x"], wl0.H_I, wl0.d_I, fmt == "mxfp8")
     ach = nb / (us * 1e-6) / 1e9
     return {"us": us, "rows": wl0.rows, "d_x": PROLOG["d_x"], "q_format": fmt, "algorithmic_bytes": nb,
-            "achieved_GBs": ach, "frac_hbm": ach / HBM_PEAK_GBS}
+            "achieved_GBs": ach, "frac_hbm": ach / HBM_PEAK_GBS,
+            "traffic": measured_traffic("prolog", args.workload)}
 
 
 def cpu_baseline(wl, budget_s: float):

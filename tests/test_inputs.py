@@ -66,3 +66,21 @@ def test_mxfp8_quantizer_error_bound_and_scale_rule():
     assert (amax / scale >= 256).all() and (amax / scale < 512).all()   # e = floor(log2 amax) - 8
     bound = np.abs(x) * 2.0 ** -4 + np.repeat(scale, 32, -1) * 2.0 ** -9 + np.maximum(np.abs(x) - 448 * np.repeat(scale, 32, -1), 0)
     assert (np.abs(deq - x) <= bound + 1e-15).all()
+
+
+def test_prolog_inputs_are_seeded_and_shaped():
+    """make_prolog: same seed and rotation give the same bits, another rotation other
+    bits; shapes, dtypes and the stated variances (projections with the indexer
+    inputs' variances: var(W_q x) = 1/d_I, var(W_h x) = 1/H_I)."""
+    from sparse_attention_lightningindexer_amd.inputs import make_prolog
+    a, b, c = make_prolog(8, 1024, seed=3), make_prolog(8, 1024, seed=3), make_prolog(8, 1024, seed=3, rotation=1)
+    for name in ("x", "w_q", "w_h", "k", "gain"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+        assert not np.array_equal(getattr(a, name), getattr(c, name)), name
+    assert a.x.shape == (8, 1024) and a.x.dtype == np.uint16
+    assert a.w_q.shape == (64 * 128, 1024) and a.w_h.shape == (64, 1024) and a.k.shape == (8, 128)
+    assert a.gain.shape == (128,) and a.gain.dtype == np.float32
+    f = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    wq = f(a.w_q)
+    assert abs(wq.var() * 1024 * 128 - 1) < 0.02
+    assert abs(f(a.x).var() - 1) < 0.05 and abs(a.gain.mean() - 1) < 0.03
