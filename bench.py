@@ -182,6 +182,23 @@ def time_prolog(wl0, args, stream):
             "traffic": measured_traffic("prolog", args.workload)}
 
 
+def cpu_baseline_prolog(wl0, budget_s: float):
+    """The oracle's prolog (fp64 projections and normalization) on the host's cores,
+    on the same inputs as the GPU prolog, repeated for about budget_s seconds."""
+    from oracle import oracle as O
+    from sparse_attention_lightningindexer_amd.inputs import PROLOG, make_prolog
+    p = make_prolog(wl0.rows, PROLOG["d_x"], wl0.H_I, wl0.d_I, seed=PROLOG["seed"], eps=PROLOG["eps"])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.indexer_prolog(p)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": p.rows * reps / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"all {p.rows} rows of one prolog x {reps}; {dt:.1f} s"}
+
+
 def cpu_baseline(wl, budget_s: float):
     """The oracle as it stands, on the host's cores, over a bounded sample of rows."""
     import numpy as np
@@ -381,6 +398,8 @@ def main():
     res["append_us"] = a0.elapsed_time(a1) / args.steps * 1e3
     if wl0.rows <= 256:
         res["prolog"] = time_prolog(wl0, args, stream)
+        if not args.no_cpu:
+            res["prolog"]["cpu_baseline"] = cpu_baseline_prolog(wl0, min(args.cpu_budget, 5.0))
     if args.copy_calib:
         src = torch.randn(args.copy_calib * 2 ** 18, device="cuda")
         dst = torch.empty_like(src)
