@@ -176,6 +176,13 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     int vid[kStRows];  // pool row of chunk row srow0 + r of chunk c, in lane c
     auto compact = [&]() __attribute__((always_inline)) {
         constexpr int kSlotIters = kAttnMaxSplitSlots / kThreads;
+        // The sequence's block-table row goes to LDS beside the slot list
+        // (when it fits), loaded together with the indices: then the
+        // compaction costs one memory round trip instead of two.
+        constexpr int kTabMax = (kTileB - kAttnMaxSplitSlots * 4) / 4;
+        int32_t* const tab_s = prow + kAttnMaxSplitSlots;
+        const int nb = (L + kBlock - 1) / kBlock;  // blocks of the history (<= max_blocks)
+        const bool tab_lds = nb <= kTabMax;        // workgroup-uniform
         int pr_[kSlotIters];
         {
             // reads are unconditional (clamped to in-range slots and blocks) so
@@ -187,10 +194,16 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                 const int v = indices[(int64_t)row * top_k + min(t, top_k - 1)];
                 sv[k] = t < slot1 && v >= 0 && v < L ? v : -1;
             }
+            if (tab_lds) {
+                for (int jb = tid; jb < nb; jb += kThreads)
+                    tab_s[jb] = (int)phys_block(table, max_blocks, b, jb, num_blocks);
+                __syncthreads();
+            }
 #pragma unroll
             for (int k = 0; k < kSlotIters; ++k) {
                 const int sk = sv[k];
-                const int64_t p = phys_block(table, max_blocks, b, sk < 0 ? 0 : sk / kBlock, num_blocks);
+                const int jb = sk < 0 ? 0 : sk / kBlock;
+                const int64_t p = tab_lds ? (int64_t)tab_s[jb] : phys_block(table, max_blocks, b, jb, num_blocks);
                 pr_[k] = (sk >= 0 && p >= 0) ? (int)(p * kBlock + (sk % kBlock)) : -1;
             }
         }
