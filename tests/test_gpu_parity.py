@@ -295,14 +295,15 @@ def test_cache_append_matches_oracle(case):
 # (rows, d_x, H_I, d_I, query format): one row and one k stage; ragged row tiles
 # of every tile height (16, 32, 64 rows); fewer stages than the LDS ring holds;
 # few heads (H_I 4, so few workgroups share out the normalized rows) and heads
-# of 64 and 32 channels; the decode prolog workload (32 rows, d_x 7168) in both
-# formats.
+# of 32, 64 and 256 channels (four values per lane in the normalization); four
+# row tiles; the decode prolog workload (32 rows, d_x 7168) in both formats.
 PROLOG = {
     "r1_dx256_mx": (1, 256, 64, 128, "mxfp8"),
     "r5_dx1024_bf16": (5, 1024, 64, 128, "bf16"),
     "r17_dx768_mx": (17, 768, 64, 128, "mxfp8"),
     "r70_dx1280_h4_mx": (70, 1280, 4, 32, "mxfp8"),
     "r130_dx256_h40_bf16": (130, 256, 40, 64, "bf16"),
+    "r200_dx512_h8d256_mx": (200, 512, 8, 256, "mxfp8"),
     "decode_b32_dx7168_mx": (32, 7168, 64, 128, "mxfp8"),
     "decode_b32_dx7168_bf16": (32, 7168, 64, 128, "bf16"),
 }
