@@ -583,47 +583,50 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const uint16_t* __rest
     const int row = blockIdx.x;
     const int h = 4 * blockIdx.y + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (h >= H) return;
-    // the splits' LSEs, then the partial rows four splits at a time (the
-    // decode split count), each group loaded before any of it is used, so
-    // the loads issue back to back
+    // up to kBatch splits (the decode split count) in one round trip: their
+    // LSEs and partial rows are all loaded before any is used; more splits
+    // take further batches, merged in order with the running maximum fixed
+    // by a first pass over the LSEs
     constexpr int kBatch = 4;
     float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_lse[((int64_t)row * splits + s) * H + h]);
-    float W = 0.f;
-    for (int s = 0; s < splits; ++s) {
-        const float ls = ws_lse[((int64_t)row * splits + s) * H + h];
-        W += (M == -INFINITY || ls == -INFINITY) ? 0.f : expf(ls - M);
-    }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
+    if (splits > kBatch)
+        for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_lse[((int64_t)row * splits + s) * H + h]);
     for (int d = 8 * lane; d < Dv; d += 8 * 64) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float W = 0.f;
         for (int s0 = 0; s0 < splits; s0 += kBatch) {
             uint4 v[kBatch];
-            float wgt[kBatch];
+            float ls[kBatch];
 #pragma unroll
             for (int k = 0; k < kBatch; ++k) {
                 const int s = min(s0 + k, splits - 1);  // in range; weight 0 past the last split
-                const float ls = ws_lse[((int64_t)row * splits + s) * H + h];
-                wgt[k] = (s0 + k >= splits || M == -INFINITY || ls == -INFINITY) ? 0.f : expf(ls - M);
+                ls[k] = s0 + k < splits ? ws_lse[((int64_t)row * splits + s) * H + h] : -INFINITY;
                 v[k] = *reinterpret_cast<const uint4*>(ws_o + (((int64_t)row * splits + s) * H + h) * Dv + d);
+            }
+            if (splits <= kBatch) {
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) M = fmaxf(M, ls[k]);
             }
 #pragma unroll
             for (int k = 0; k < kBatch; ++k) {
+                const float wgt = (M == -INFINITY || ls[k] == -INFINITY) ? 0.f : expf(ls[k] - M);
+                W += wgt;
                 const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    acc[2 * i] = fmaf(wgt[k], __uint_as_float(w4[i] << 16), acc[2 * i]);
-                    acc[2 * i + 1] = fmaf(wgt[k], __uint_as_float(w4[i] & 0xffff0000u), acc[2 * i + 1]);
+                    acc[2 * i] = fmaf(wgt, __uint_as_float(w4[i] << 16), acc[2 * i]);
+                    acc[2 * i + 1] = fmaf(wgt, __uint_as_float(w4[i] & 0xffff0000u), acc[2 * i + 1]);
                 }
             }
         }
+        const float inv = W > 0.f ? 1.f / W : 0.f;
         uint16_t* o = out + ((int64_t)row * H + h) * Dv + d;
         uint32_t w4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) w4[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
         *reinterpret_cast<uint4*>(o) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        if (lse != nullptr && lane == 0 && d == 0) lse[(int64_t)row * H + h] = W > 0.f ? M + logf(W) : -INFINITY;
     }
-    if (lse != nullptr && lane == 0) lse[(int64_t)row * H + h] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
 // fp32 attention for small shapes: one wave per (head, row); logits of the
