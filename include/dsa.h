@@ -250,7 +250,7 @@ dsa_status dsa_cache_append(const dsa_batch* batch, const void* k_new, const voi
  * preparation"): what the indexer of one step needs, made from each query
  * token's hidden state. */
 typedef struct {
-    int32_t rows;               /* query tokens (0: nothing to do)                 */
+    int32_t rows;               /* query tokens, at most 4194240 (0: nothing to do) */
     int32_t d_x;                /* hidden width: a positive multiple of 256        */
     int32_t n_heads;            /* H_I >= 1                                        */
     int32_t head_dim;           /* d_I: a multiple of 32, at most 256              */

@@ -305,8 +305,8 @@ dsa_status dsa_indexer_prolog(const dsa_prolog_args* p, void* stream) {
     if (p->rows < 0 || p->d_x < kPrologChunk || p->d_x % kPrologChunk != 0 || p->n_heads < 1 || p->head_dim < 32 ||
         p->head_dim % 32 != 0 || p->head_dim > 256 || !(p->eps >= 0.f) || p->eps > 3.0e38f)
         return DSA_ERR_SHAPE;
-    if ((int64_t)p->n_heads * p->head_dim > (int64_t)INT_MAX / 2 || (int64_t)p->rows * p->d_x > (int64_t)INT_MAX * 64)
-        return DSA_ERR_SHAPE;
+    // row tiles of up to 64 rows form the grid's second dimension (at most 65535)
+    if ((int64_t)p->n_heads * p->head_dim > (int64_t)INT_MAX / 2 || p->rows > 65535 * 64) return DSA_ERR_SHAPE;
     if (p->q_dtype != DSA_BF16 && p->q_dtype != DSA_E4M3) return DSA_ERR_UNSUPPORTED;
     if (p->rows == 0) return DSA_OK;
     if (p->x == nullptr || p->w_q == nullptr || p->w_h == nullptr || p->k == nullptr || p->k_gain == nullptr ||

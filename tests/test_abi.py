@@ -126,7 +126,7 @@ def test_prolog_validation_errors_are_returned_before_any_launch():
 
     assert lib.dsa_indexer_prolog(None, None) == B.DSA_ERR_NULL
     assert call(rows=0) == B.DSA_OK                       # nothing to do, nothing launched
-    for bad in (dict(rows=-1), dict(d_x=0), dict(d_x=7168 + 64), dict(d_x=7168 + 128), dict(head_dim=48), dict(head_dim=288),
+    for bad in (dict(rows=-1), dict(rows=65535 * 64 + 1), dict(d_x=0), dict(d_x=7168 + 64), dict(d_x=7168 + 128), dict(head_dim=48), dict(head_dim=288),
                 dict(n_heads=0), dict(eps=-1.0), dict(eps=float("nan")), dict(eps=float("inf")),
                 dict(x=fake + 8), dict(w_q=fake + 2), dict(q_out=fake + 4), dict(head_w_out=fake + 2),
                 dict(k_out=fake + 1)):
