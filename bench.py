@@ -304,6 +304,23 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)",
           file=sys.stderr, flush=True)
 
+    # the spread of single steps: a separate loop (not the timed region) with an
+    # event between consecutive steps; each step's time is the span between its
+    # two events on the launch stream, after a spin that lets the host queue
+    # the loop ahead of the GPU
+    n_one = min(args.steps, 100)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_one + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(600_000 * n_one)
+    evs[0].record(stream)
+    for i in range(n_one):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    one = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_one)])
+    step_us = {"p10": float(np.percentile(one, 10)), "p50": float(np.percentile(one, 50)),
+               "p90": float(np.percentile(one, 90)), "steps": n_one}
+
     # per-stage durations: the same kernels through the three unfused calls.
     # Each stage runs K times back to back (input sets rotating) between two
     # HIP events on the launch stream, so an event's own cost is spread over K
@@ -365,6 +382,7 @@ def main():
                    "index_dim": wl0.d_I, "heads": wl0.H, "d_qk": wl0.d_qk, "d_v": wl0.d_v,
                    "paging": wl0.cfg["paging"], "input_sets": nsets},
         "roofline": roof,
+        "step_us": step_us,
         "stages_us": stage_us,
     }
     if wl0.idx_dtype in ("e4m3", "mxfp8"):
