@@ -283,7 +283,7 @@ typedef struct {
  * quotient clamped to +-448 (nearest, ties to even), scale byte e + 127 --
  * the layout dsa_indexer_args takes for an E4M3 query with E8M0 scales.
  * k_out is rounded nearest-even to BF16 and is what dsa_cache_append stores
- * as the index key.  All branches run in one launch on `stream`.  Alignment
+ * as the index key (with eps = 0, an all-zero key gives NaN, 0/0).  All branches run in one launch on `stream`.  Alignment
  * (else SHAPE): x, w_q and w_h 16 bytes, q_out 8, head_w_out and k_gain 4,
  * k and k_out 2.  Errors: NULL, SHAPE, UNSUPPORTED, HIP.
  */

@@ -359,3 +359,40 @@ def test_indexer_prolog_zero_inputs_and_feeds_the_indexer():
     torch.cuda.synchronize()
     rows = np.arange(wl.rows, dtype=np.int32)
     check_scores(wl, sc.cpu().numpy().astype(np.float64), O.indexer_scores(wl, rows), rows)
+
+
+@pytest.mark.parametrize("case", ["fp8_mx_kv", "mx_idx_fp32_kv"])
+def test_cache_append_edge_values_match_oracle(case):
+    """Quantized appends of rows built from edge values: all-zero rows, -0.0, bf16
+    subnormals, tiny and huge magnitudes in one group, and values a hair under the
+    saturation point of their group; codes and scales bit-exact against the oracle."""
+    cfg, kw = APPEND[case]
+    wl = make_workload(cfg, **kw)
+    say(f"[parity] append edge values {case}")
+    dev = B.DeviceInputs(wl)
+    rng = np.random.default_rng(12)
+    specials = np.array([0.0, -0.0, 1e-39, -3e-39, 1e-30, 2.5e-20, 1.0, -1.0, 448.0, -447.0, 1e20, -3e30,
+                         0.0625, 0.09375, 65504.0, 7.0e-3], np.float32)
+
+    def rows(width):
+        x = rng.choice(specials, size=(wl.rows, width)).astype(np.float32)
+        x[0] = 0.0                                 # an all-zero row
+        x[1] = -0.0
+        x[2] = rng.standard_normal(width).astype(np.float32) * 1e-36  # subnormal-range row
+        return torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+
+    k_new, kv_new = rows(wl.d_I), rows(wl.d_qk)
+    B.dsa_cache_append(dev, torch.from_numpy(k_new).to(torch.bfloat16).cuda(),
+                       torch.from_numpy(kv_new).to(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    kp, kvp = wl.k_pool.copy(), wl.kv_pool.copy()
+    ks = None if wl.k_scale is None else wl.k_scale.copy()
+    kvs = None if wl.kv_scale is None else wl.kv_scale.copy()
+    O.cache_append(wl, k_new, wl.idx_dtype, kp, ks)
+    O.cache_append(wl, kv_new, wl.kv_dtype, kvp, kvs)
+    for name, got, ref in [("k_pool", dev.k_pool, kp), ("kv_pool", dev.kv_pool, kvp),
+                           ("k_scale", dev.k_scale, ks), ("kv_scale", dev.kv_scale, kvs)]:
+        if ref is None:
+            continue
+        g = got.cpu().numpy().reshape(ref.shape)
+        assert np.array_equal(g.view(np.uint8), np.ascontiguousarray(ref).view(np.uint8)), f"{case}: {name} differs"
