@@ -396,3 +396,34 @@ def test_cache_append_edge_values_match_oracle(case):
             continue
         g = got.cpu().numpy().reshape(ref.shape)
         assert np.array_equal(g.view(np.uint8), np.ascontiguousarray(ref).view(np.uint8)), f"{case}: {name} differs"
+
+
+def test_late_large_logit_takes_the_exact_second_pass():
+    """A logit in a late chunk above its work item's first-chunk maximum by far more
+    than the no-rescale slack (2^32 in probability): the work item runs again with
+    the exact maximum.  One latent row's rope channels are aligned with head 0's
+    query so that head's logit there is about 120 nats (173 in log2 units: without
+    the second pass its probability would overflow fp32 and bf16); its value
+    channels stay ordinary.  Output and lse match the oracle: 128 rows of 8 chunks
+    (no split, the row in the last chunk) and 2 rows split 32 ways (the row in the
+    second chunk of the last split)."""
+    for batch, lens, top_k in ((128, 300, 256), (2, [3000, 2500], 2048)):
+        wl = make_workload(2, batch=batch, lens=lens, top_k=top_k)
+        say(f"[parity] late large logit: batch {batch}, top_k {top_k}")
+        q = torch.from_numpy(wl.q.view(np.int16)).view(torch.bfloat16).double().numpy()
+        s_star = top_k - 7
+        marked = [0, batch - 1] + ([batch // 2] if batch > 2 else [])
+        for b in marked:
+            q0 = q[b, 0, 512:]                      # head 0 of row b (n_q = 1), rope channels
+            beta = 120.0 / (wl.sm_scale * float(q0 @ q0))
+            row = (beta * q0).astype(np.float32)
+            blk = int(wl.block_table[b, s_star // 64])
+            wl.kv_pool[blk, s_star % 64, 512:] = torch.from_numpy(row).to(torch.bfloat16).view(
+                torch.int16).numpy().view(np.uint16)
+        idx = np.tile(np.arange(top_k, dtype=np.int32), (wl.rows, 1))
+        dev = B.DeviceInputs(wl)
+        out, lse = B.dsa_sparse_attn(dev, torch.from_numpy(idx).cuda())
+        torch.cuda.synchronize()
+        ref_o, ref_l = O.sparse_attn(wl, idx)
+        assert (ref_l[marked, 0] > 110).all()       # the late logit dominates head 0
+        check_attention(wl, f64(out), f64(lse), ref_o, ref_l, f"late logit k={top_k}")
