@@ -427,3 +427,34 @@ def test_late_large_logit_takes_the_exact_second_pass():
         ref_o, ref_l = O.sparse_attn(wl, idx)
         assert (ref_l[marked, 0] > 110).all()       # the late logit dominates head 0
         check_attention(wl, f64(out), f64(lse), ref_o, ref_l, f"late logit k={top_k}")
+
+
+def test_side_stream_and_no_indices_out_give_the_same_bytes():
+    """Every call runs on the stream it is given: dsa_forward on a second stream
+    (default priority), with and without indices_out, gives the same output and lse
+    bytes as on the current stream; the side stream's work is ordered after the
+    inputs' copies by an event."""
+    wl = make_workload(2, batch=4, lens=[5000, 700, 2049, 64])
+    say("[parity] side stream, indices_out NULL")
+    dev = B.DeviceInputs(wl)
+    out0, lse0, idx0 = B.dsa_forward(dev)
+    torch.cuda.synchronize()
+    ref = (out0.clone(), lse0.clone(), idx0.clone())
+    side = torch.cuda.Stream()
+    ready = torch.cuda.Event()
+    ready.record(torch.cuda.current_stream())
+    side.wait_event(ready)
+    out_s = torch.empty_like(ref[0])
+    lse_s = torch.empty_like(ref[1])
+    dev.set_outputs(out_s, lse_s)
+    with torch.cuda.stream(side):
+        B.dsa_forward(dev, indices_out=None, want_indices=False, stream=side)
+    side.synchronize()
+    assert torch.equal(out_s, ref[0]) and torch.equal(lse_s, ref[1])
+    # attention alone on the side stream, from the first call's indices
+    out_a = torch.empty_like(ref[0])
+    dev.set_outputs(out_a, None)
+    with torch.cuda.stream(side):
+        B.dsa_sparse_attn(dev, ref[2], stream=side)
+    side.synchronize()
+    assert torch.equal(out_a, ref[0])
