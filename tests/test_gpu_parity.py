@@ -458,3 +458,35 @@ def test_side_stream_and_no_indices_out_give_the_same_bytes():
         B.dsa_sparse_attn(dev, ref[2], stream=side)
     side.synchronize()
     assert torch.equal(out_a, ref[0])
+
+
+def test_forward_replays_from_a_captured_graph():
+    """dsa_forward captured into a HIP graph (workspace and outputs allocated
+    beforehand; the library allocates nothing) replays to the eager bytes, three
+    times, with eager work that clears the outputs between the replays."""
+    wl = make_workload(2, batch=4, lens=[5000, 700, 2049, 64])
+    say("[parity] graph capture and replay of dsa_forward")
+    dev = B.DeviceInputs(wl)
+    ws = torch.empty(max(1, B.dsa_forward_workspace_bytes(dev)), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((wl.rows, wl.top_k), dtype=torch.int32, device="cuda")
+    B.dsa_forward(dev, indices_out=idx, ws=ws)
+    torch.cuda.synchronize()
+    ref = (dev.out.clone(), dev.lse.clone(), idx.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # a warm call on the capture's side stream
+        B.dsa_forward(dev, indices_out=idx, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.dsa_forward(dev, indices_out=idx, ws=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        dev.out.zero_()
+        dev.lse.zero_()
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dev.out, ref[0]) and torch.equal(dev.lse, ref[1]) and torch.equal(idx, ref[2]), rep
