@@ -252,7 +252,7 @@ def main():
         print(json.dumps({k: rec[k] for k in ("hbm_bytes_per_launch", "fetch_factor", "write_factor")}))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the stage shards by sequence with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
 
