@@ -28,7 +28,7 @@ BF16_PEAK_TFLOPS = 2500.0
 
 
 def algorithmic(wl):
-    """Bytes and flops the method must move/compute per step, per stage (see the design notes).
+    """Bytes and flops the method must move/compute per step, per stage.
 
     The scores intermediate is not counted; gathers count one latent row per
     selected (row, position); the attention counts QK^T over d_qk and PV over d_v.
@@ -253,7 +253,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the stage shards by sequence with no exchange; see the design notes)", file=sys.stderr)
+              "(decode shards by sequence, with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -20,7 +20,7 @@
  *       Fusion to Multi-Dimensional Parallelism"
  *
  * What is computed (the pages give prose, no formulas; where they are silent
- * the plainest reading is taken and listed in the design notes):
+ * the plainest reading is taken):
  *  1. dequantize every input to fp64 (value(code) * scale) -- exact;
  *  2. indexer: I[r,s] = sum_j w[r,j] * max(0, sum_c qI[r,j,c] * kI[s,c])
  *     for every causal history position s < L_r  ([A] §2 "Sparse Attention

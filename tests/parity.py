@@ -9,7 +9,9 @@ Tolerances:
 * indices -- bit-exact when the oracle selects from the GPU's own fp32 scores
   (both sides then take the decision in the kernel's precision); against the
   oracle's fp64 scores, a position may differ only if its score is within
-  1e-3 relative of the k-th score (R8 of the readings in the design notes);
+  1e-3 relative of the k-th score, where the k-th score is the oracle's
+  k_r-th largest fp64 score of the row (1e-3 of the row's largest magnitude
+  when that score is 0);
 * attention -- bf16 outputs: max |d| <= 2e-2 and ||d||_2 <= 1e-2 ||ref||_2;
   fp32 outputs: max |d| <= 1e-4 max |ref|; lse: |d| <= 1e-3 (+ 1e-4 relative
   for fp32).
