@@ -35,8 +35,9 @@
  *     sparse core reads only the selected KV entries);
  *  5. dense causal attention over all s < L_r (used only by invariants);
  *  6. cache append: this step's index keys and latent rows written into the
- *     paged pools, quantized in fp32 when the pool is (the quantizer's
- *     decisions are integer codes, so they are taken in the kernel's fp32);
+ *     paged pools, copied when the pool has the input's format, quantized in
+ *     fp32 when the pool is e4m3 (the quantizer's decisions are integer
+ *     codes, so they are taken in the kernel's fp32);
  *  7. indexer prolog: the index query and head weights projected from the
  *     hidden state and the new index key RMS-normalized, exactly in fp64
  *     ([D] §4.2 "Three-Stream Coordination for Indexer Preprocessing").
@@ -351,7 +352,6 @@ int oracle_dense_attn(int batch, int n_q, const int32_t* seq_lens, const int32_t
                           kv_scale_kind, kv_group, NULL, 0, sm_scale, rows, n_rows, out, lse);
 }
 
-/* Number of OpenMP threads a parallel region of the oracle will use. */
 /* ------------------------------------------------------------ cache append */
 
 /* Nearest-even rounding of a non-negative double to an integer. */
@@ -420,37 +420,47 @@ static void quantize_vector(const float* x, int width, int kind, int group, uint
 
 /* Cache append: row r = b*n_q + i is this step's token at position
  * s = L_b - n_q + i of sequence b; its `width` values x_new[r] are written to
- * the pool row of s (skipped when s < 0 or its block is absent), as fp32
- * (ORC_F32), nearest-even bf16 (ORC_BF16), or e4m3 codes plus scales
- * (ORC_E4M3, scale kind and group as above).  scales: [pool rows][ceil(width/group)]. */
+ * the pool row of s (skipped when s < 0 or its block is absent).  The pool
+ * formats and the input each one takes:
+ *   ORC_F32 pool,  fp32 input (x_dtype ORC_F32): the values, copied;
+ *   ORC_BF16 pool, bf16 input (x_dtype ORC_BF16): the 16-bit codes, copied
+ *                  bit for bit (NaN payloads included);
+ *   ORC_E4M3 pool, bf16 input: each code decoded to fp32 (exact), then e4m3
+ *                  codes plus scales (scale kind and group as above).
+ * Any other pairing returns -1 and writes nothing.  x_new: [rows][width] of
+ * x_dtype; scales: [pool rows][ceil(width/group)]. */
 int oracle_cache_append(int batch, int n_q, const int32_t* seq_lens, const int32_t* block_table,
-                        int max_blocks, int64_t num_blocks, const float* x_new, int width,
-                        int dtype, int scale_kind, int group, void* pool, void* scales) {
-    orc_batch B = {batch, n_q, seq_lens, block_table, max_blocks, 64, num_blocks};
+                        int max_blocks, int block_size, int64_t num_blocks, const void* x_new, int x_dtype,
+                        int width, int dtype, int scale_kind, int group, void* pool, void* scales) {
+    if (!((dtype == ORC_F32 && x_dtype == ORC_F32) || (dtype == ORC_BF16 && x_dtype == ORC_BF16) ||
+          (dtype == ORC_E4M3 && x_dtype == ORC_BF16)))
+        return -1;
+    orc_batch B = {batch, n_q, seq_lens, block_table, max_blocks, block_size, num_blocks};
     int ng = scale_kind == ORC_SCALE_NONE ? 0 : (width + group - 1) / group;
+    float* row = (float*)malloc(sizeof(float) * (size_t)width);
+    if (row == NULL) return -1;
     for (int r = 0; r < batch * n_q; ++r) {
         int b = r / n_q;
         int s = history_len(&B, r) - 1;
         if (s < 0) continue;
         int64_t pr = pool_row(&B, b, s);
         if (pr < 0) continue;
-        const float* x = x_new + (int64_t)r * width;
         if (dtype == ORC_F32) {
-            memcpy((float*)pool + pr * width, x, sizeof(float) * (size_t)width);
+            memcpy((float*)pool + pr * width, (const float*)x_new + (int64_t)r * width,
+                   sizeof(float) * (size_t)width);
         } else if (dtype == ORC_BF16) {
-            for (int c = 0; c < width; ++c) {   /* nearest-even to the upper 16 bits */
-                uint32_t u;
-                memcpy(&u, &x[c], sizeof u);
-                uint32_t lsb = (u >> 16) & 1u;
-                ((uint16_t*)pool)[pr * width + c] = (uint16_t)((u + 0x7FFFu + lsb) >> 16);
-            }
+            memcpy((uint16_t*)pool + pr * width, (const uint16_t*)x_new + (int64_t)r * width,
+                   sizeof(uint16_t) * (size_t)width);
         } else {
+            const uint16_t* xb = (const uint16_t*)x_new + (int64_t)r * width;
+            for (int c = 0; c < width; ++c) row[c] = (float)oracle_bf16_to_f64(xb[c]);  /* exact */
             uint8_t* codes = (uint8_t*)pool + pr * width;
             void* sc = scale_kind == ORC_SCALE_F32 ? (void*)((float*)scales + pr * ng)
                                                    : (void*)((uint8_t*)scales + pr * ng);
-            quantize_vector(x, width, scale_kind, group, codes, sc);
+            quantize_vector(row, width, scale_kind, group, codes, sc);
         }
     }
+    free(row);
     return 0;
 }
 
@@ -514,6 +524,7 @@ int oracle_indexer_prolog(int rows, int d_x, const uint16_t* x, const uint16_t* 
     return 0;
 }
 
+/* Number of OpenMP threads a parallel region of the oracle will use. */
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

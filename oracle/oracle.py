@@ -45,7 +45,8 @@ def lib():
         L.oracle_dense_attn.argtypes = attn + [d, p, i32, p, p]
         L.oracle_f32_to_e4m3.restype = C.c_uint8
         L.oracle_f32_to_e4m3.argtypes = [C.c_float]
-        L.oracle_cache_append.argtypes = [i32, i32, p, p, i32, i64, p, i32, i32, i32, i32, p, p]
+        L.oracle_cache_append.argtypes = [i32, i32, p, p, i32, i32, i64, p, i32, i32, i32, i32, i32, p, p]
+        L.oracle_cache_append.restype = i32
         L.oracle_e4m3_encode.argtypes = [p, i64, p]
         L.oracle_indexer_prolog.argtypes = [i32, i32, p, p, p, p, p, d, i32, i32, p, p, p]
         L.oracle_num_threads.restype = i32
@@ -177,14 +178,23 @@ def f32_to_e4m3(x: float) -> int:
 
 
 def cache_append(wl, x_new, fmt: str, pool, scales):
-    """Write rows x_new [rows, width] (fp32 values) into `pool` (and `scales`) in place, as
-    storage format `fmt` ("f32", "bf16", "e4m3" = fp32 per 128, "e4m3_128", "mxfp8")."""
-    x = _c(x_new, np.float32)
+    """Write rows x_new [rows, width] into `pool` (and `scales`) in place, as storage
+    format `fmt` ("f32", "bf16", "e4m3" = fp32 per 128, "e4m3_128", "mxfp8").  An f32
+    pool takes float32 rows; every other pool takes bf16 rows, as uint16 bit patterns
+    (a bf16 pool copies them bit for bit)."""
     kind, grp = _SCALES[fmt]
+    if fmt == "f32":
+        x, xdt = _c(x_new, np.float32), _DT["f32"]
+    else:
+        x = np.ascontiguousarray(x_new)
+        assert x.dtype == np.uint16, "bf16 rows as uint16 bit patterns"
+        xdt = _DT["bf16"]
     seq, tab = _c(wl.seq_lens, np.int32), _c(wl.block_table, np.int32)
     assert pool.flags.c_contiguous and (scales is None or scales.flags.c_contiguous)
-    lib().oracle_cache_append(wl.batch, wl.n_q, _ptr(seq), _ptr(tab), wl.max_blocks, wl.num_blocks,
-                              _ptr(x), x.shape[1], _DT[fmt], kind, grp, _ptr(pool), _ptr(scales))
+    st = lib().oracle_cache_append(wl.batch, wl.n_q, _ptr(seq), _ptr(tab), wl.max_blocks, 64, wl.num_blocks,
+                                   _ptr(x), xdt, x.shape[1], _DT[fmt], kind, grp, _ptr(pool), _ptr(scales))
+    if st != 0:
+        raise ValueError(f"oracle_cache_append: unsupported pairing of {fmt} pool and {x.dtype} rows")
 
 
 def e4m3_encode(x):

@@ -15,7 +15,8 @@
 //   E8M0 scale:  e = floor(log2 amax) - 8 (-127 when amax = 0), clamped to
 //                [-127, 127], code = e4m3(x * 2^-e), byte e + 127
 // The quotient is clamped to +-448 and rounded to the nearest e4m3 (ties to
-// even) by the hardware conversion.  bf16 and fp32 pools are plain copies.
+// even) by the hardware conversion.  bf16 and fp32 pools are plain copies of
+// their input, bit for bit (NaN payloads included).
 //
 // One workgroup of 256 threads per token: threads 0..63 take the index key,
 // threads 64..255 the latent row, four values per thread, so a group of G
@@ -46,12 +47,12 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
 
 // Writes this thread's four values x[0..3] (elements 4t .. 4t+3 of a width-wide
-// vector) into pool row `prow`.  kind: 0 fp32 copy, 1 bf16 copy, 2 e4m3 with an
-// fp32 scale per `group`, 3 e4m3 with an E8M0 scale per `group`.  Every lane
-// of the wave calls this (the reductions are wave-wide); `active` says whether
-// the thread holds values.
-__device__ __forceinline__ void store_vector(const float (&x)[4], bool active, int t, int width, int kind,
-                                             int group, void* pool, void* scales, int64_t prow) {
+// vector) into pool row `prow`.  kind: 0 fp32 copy, 1 bf16 copy (of the input
+// codes `raw`, not of x), 2 e4m3 with an fp32 scale per `group`, 3 e4m3 with
+// an E8M0 scale per `group`.  Every lane of the wave calls this (the
+// reductions are wave-wide); `active` says whether the thread holds values.
+__device__ __forceinline__ void store_vector(const float (&x)[4], uint2 raw, bool active, int t, int width,
+                                             int kind, int group, void* pool, void* scales, int64_t prow) {
     if (kind == 0) {
         if (active)
             *reinterpret_cast<float4*>(static_cast<float*>(pool) + prow * width + 4 * t) =
@@ -59,11 +60,7 @@ __device__ __forceinline__ void store_vector(const float (&x)[4], bool active, i
         return;
     }
     if (kind == 1) {
-        if (active) {
-            const uint32_t lo = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
-            const uint32_t hi = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(pool) + prow * width + 4 * t) = make_uint2(lo, hi);
-        }
+        if (active) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(pool) + prow * width + 4 * t) = raw;
         return;
     }
     float a = active ? fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))) : 0.f;
@@ -106,10 +103,12 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
     if (pb < 0) return;  // absent block: nothing is written (uniform per pool, hence per wave)
     const int64_t prow = pb * kBlock + s % kBlock;
     float x[4] = {0.f, 0.f, 0.f, 0.f};
+    uint2 raw = make_uint2(0u, 0u);  // bf16 input codes, stored as they are into a bf16 pool
     if (active) {
         const In* src = (key ? k_new + (int64_t)r * k_width : kv_new + (int64_t)r * kv_width) + 4 * t;
         if constexpr (sizeof(In) == 2) {
             const uint2 v = *reinterpret_cast<const uint2*>(src);
+            raw = v;
             x[0] = bf16_bits_to_f32((uint16_t)(v.x & 0xffffu));
             x[1] = bf16_bits_to_f32((uint16_t)(v.x >> 16));
             x[2] = bf16_bits_to_f32((uint16_t)(v.y & 0xffffu));
@@ -120,9 +119,9 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
         }
     }
     if (key)
-        store_vector(x, active, t, k_width, k_kind, k_group, k_pool, k_scales, prow);
+        store_vector(x, raw, active, t, k_width, k_kind, k_group, k_pool, k_scales, prow);
     else
-        store_vector(x, active, t, kv_width, kv_kind, kv_group, kv_pool, kv_scales, prow);
+        store_vector(x, raw, active, t, kv_width, kv_kind, kv_group, kv_pool, kv_scales, prow);
 }
 
 }  // namespace

@@ -469,11 +469,12 @@ def test_cache_append_quantizes_like_the_input_generator(fmt):
     from sparse_attention_lightningindexer_amd.inputs import quantize_e4m3_f32scale, quantize_mxfp8
     wl = make_workload(2, batch=3, n_q=2, lens=[300, 130, 65])
     x = (np.random.default_rng(5).standard_normal((wl.rows, 576)).astype(np.float32) / 24)
-    x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()          # bf16 inputs
+    xb = torch.from_numpy(x).to(torch.bfloat16)                          # bf16 inputs
+    x = xb.float().numpy()
     nrows = wl.num_blocks * 64
     pool = np.zeros((nrows, 576), np.uint8)
     scl = np.zeros((nrows, 5), np.float32) if fmt == "e4m3_128" else np.zeros((nrows, 18), np.uint8)
-    O.cache_append(wl, x, fmt, pool, scl)
+    O.cache_append(wl, xb.view(torch.int16).numpy().view(np.uint16), fmt, pool, scl)
     codes, sref = quantize_e4m3_f32scale(x, 128) if fmt == "e4m3_128" else quantize_mxfp8(x, 32)
     touched = np.zeros(nrows, bool)
     for r in range(wl.rows):
@@ -483,6 +484,42 @@ def test_cache_append_quantizes_like_the_input_generator(fmt):
         assert np.array_equal(pool[pr], codes[r]) and np.array_equal(scl[pr], sref[r])
         touched[pr] = True
     assert not pool[~touched].any() and not scl[~touched].any()
+
+
+def test_cache_append_bf16_pool_copies_every_code():
+    """A bf16 pool takes bf16 rows and stores their codes unchanged: every one of the
+    65536 bf16 codes (NaN payloads, signalling and quiet, both infinities, -0 and the
+    subnormals included) lands at its row's pool position, and nothing else is
+    written; an fp32 pool copies fp32 rows, NaN payloads included."""
+    wl = make_workload(2, batch=2, n_q=128, lens=[300, 700])  # 256 rows
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(wl.rows, 256)
+    nrows = wl.num_blocks * 64
+    pool = np.full((nrows, 256), 0x1234, np.uint16)
+    O.cache_append(wl, codes, "bf16", pool, None)
+    touched = np.zeros(nrows, bool)
+    for r in range(wl.rows):
+        b, s = r // wl.n_q, int(wl.row_lens()[r]) - 1
+        pr = int(wl.block_table[b, s // 64]) * 64 + s % 64
+        assert np.array_equal(pool[pr], codes[r])
+        touched[pr] = True
+    assert (pool[~touched] == 0x1234).all()
+    # fp32: quiet and signalling NaN payloads and infinities survive the copy
+    bits = np.array([0x7F800001, 0xFF800001, 0x7FC00000, 0x7FFFFFFF, 0x7F800000, 0xFF800000, 0x00000001,
+                     0x80000000], np.uint32)
+    x = np.tile(bits, (wl.rows, 32)).view(np.float32)
+    pool32 = np.zeros((nrows, 256), np.float32)
+    O.cache_append(wl, x, "f32", pool32, None)
+    s0 = int(wl.row_lens()[0]) - 1                      # row 0's own position
+    pr = int(wl.block_table[0, s0 // 64]) * 64 + s0 % 64
+    assert np.array_equal(pool32[pr].view(np.uint32), np.tile(bits, 32))
+
+
+def test_cache_append_rejects_unsupported_pairings():
+    """The append takes fp32 rows into an fp32 pool and bf16 rows into every other pool."""
+    wl = make_workload(2, batch=1, lens=[10])
+    pool = np.zeros((wl.num_blocks * 64, 8), np.uint16)
+    with pytest.raises(AssertionError):
+        O.cache_append(wl, np.zeros((1, 8), np.float32), "bf16", pool, None)
 
 
 # ------------------------------------------------------------ indexer prolog pins
