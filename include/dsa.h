@@ -50,8 +50,9 @@
  *               last covers the 64 rope channels) KV:
  *               n_heads 128, d_qk 576, d_v 512
  *               F32 q and KV: n_heads <= 16, d_qk <= 128, d_v <= d_qk
- *      block_size 64, 1 <= top_k <= 4096, n_q <= 8 unless n_q == L_b
- *      (prefill: one sequence, one query per position).
+ *      block_size 64, 1 <= top_k <= 4096, any n_q >= 1 (decode, speculative
+ *      verification, chunked prefill and whole-sequence prefill alike),
+ *      batch <= 65535 and batch * n_q <= 2^24 (else DSA_ERR_SHAPE).
  */
 #ifndef DSA_H
 #define DSA_H
@@ -229,7 +230,8 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_indexer_args* idx,
  * (the last position row r sees).  k_new[r][0:k->width] is stored at the
  * index-K pool row of s and kv_new[r][0:kv->width] at the latent pool row of
  * s; a row with s < 0 or an absent block is skipped.  Per pool format:
- *   BF16 or F32 (no scales): a copy (k_new/kv_new in the same dtype);
+ *   BF16 or F32 (no scales): a bit-for-bit copy of k_new/kv_new, which have
+ *       the pool's dtype (NaN payloads are kept as they are);
  *   E4M3 + F32 scale per `group` (a power of two, 4 to 256): scale =
  *       amax/448 (1 when amax = 0), code = e4m3(x/scale);
  *   E4M3 + E8M0 scale per `group` (32): e = floor(log2 amax) - 8 (-127 when

@@ -14,6 +14,8 @@
 namespace {
 
 constexpr int kMaxTopK = 4096;
+constexpr int kMaxBatch = 65535;       // sequences form a grid dimension of the indexer
+constexpr int64_t kMaxRows = 1 << 24;  // query rows (batch * n_q)
 constexpr size_t kAlign = 256;
 constexpr int kPrologChunk = 256;  // the prolog's hidden width must be a multiple of this
 
@@ -24,7 +26,7 @@ dsa_status check_batch(const dsa_batch* b) {
     if (b->batch < 0 || b->n_q < 1 || b->block_size != 64 || b->max_blocks < 1 || b->max_seq_len < 0)
         return DSA_ERR_SHAPE;
     if ((int64_t)b->max_seq_len > (int64_t)b->max_blocks * 64) return DSA_ERR_SHAPE;
-    if ((int64_t)b->batch * b->n_q > INT_MAX / 2) return DSA_ERR_SHAPE;
+    if (b->batch > kMaxBatch || (int64_t)b->batch * b->n_q > kMaxRows) return DSA_ERR_SHAPE;
     if (b->batch > 0 && (b->seq_lens == nullptr || b->block_table == nullptr)) return DSA_ERR_NULL;
     return DSA_OK;
 }

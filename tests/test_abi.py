@@ -62,6 +62,10 @@ def test_validation_errors_are_returned_before_any_launch():
     bad = B.dsa_batch.from_buffer_copy(batch)
     bad.block_size = 32
     assert lib.dsa_indexer_scores(ref(bad), ref(idx), 0x10000, 128, None) == B.DSA_ERR_SHAPE
+    for nb, nq in ((65536, 1), (1 << 12, (1 << 12) + 1)):  # more sequences than a grid dimension; too many rows
+        bad = B.dsa_batch.from_buffer_copy(batch)
+        bad.batch, bad.n_q = nb, nq
+        assert lib.dsa_indexer_scores(ref(bad), ref(idx), 0x10000, 128, None) == B.DSA_ERR_SHAPE
     bad = B.dsa_batch.from_buffer_copy(batch)
     bad.max_seq_len = bad.max_blocks * 64 + 1
     assert lib.dsa_topk(ref(bad), 0x10000, 10**6, 16, 0x10000, None, 0, None) == B.DSA_ERR_SHAPE

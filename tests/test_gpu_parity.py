@@ -36,6 +36,17 @@ SMALL = {
     "fp8_pages_decode": (6, dict(batch=3, lens=[500, 900, 130], top_k=256, poison=True)),
     "fp8_pages_nq2": (6, dict(batch=2, n_q=2, lens=[700, 66], top_k=256, poison=True)),
     "prefill_bf16": (3, dict(lens=333, top_k=96, poison=True)),
+    # several query tokens per sequence with batch > 1: the multi-row indexer
+    # kernel then spans several sequences, each row with its own causal length
+    "nq3_bf16": (2, dict(batch=2, n_q=3, lens=[300, 130], top_k=128, poison=True)),
+    "nq4_mxfp8": (6, dict(batch=3, n_q=4, lens=[500, 64, 261], top_k=128, poison=True)),
+    "nq8_bf16": (2, dict(batch=2, n_q=8, lens=[1000, 77], top_k=256, poison=True)),
+    "nq8_mxfp8": (6, dict(batch=2, n_q=8, lens=[1000, 77], top_k=256, poison=True)),
+    # the fp32-per-128 indexer with two query tokens per sequence
+    "fp8_nq2": (5, dict(batch=3, n_q=2, lens=[700, 66, 1500], top_k=256, poison=True)),
+    # chunked prefill: 100 new tokens on top of a longer history, and a sequence
+    # shorter than the chunk (its first rows see nothing)
+    "chunked_prefill_nq100": (2, dict(batch=2, n_q=100, lens=[700, 60], top_k=128, poison=True)),
 }
 
 
@@ -65,12 +76,9 @@ def test_small_all_stages_match_oracle(case):
     assert np.array_equal(f64(out2), out) and np.array_equal(f64(lse2), lse)
 
 
-@pytest.mark.parametrize("case", ["decode_bf16", "skewed_nq2", "fp8_decode", "prefill_bf16"])
+@pytest.mark.parametrize("case", ["decode_bf16", "skewed_nq2", "fp8_decode", "nq4_mxfp8"])
 def test_identity_and_permuted_paging_give_identical_outputs(case):
     cfg, kw = SMALL[case]
-    kw = dict(kw)
-    if cfg == 3:
-        pytest.skip("prefill workloads are identity-paged by definition; covered by the permuted cases")
     a = make_workload(cfg, **kw)
     b = make_workload(cfg, paging="identity", **kw)
     _, sa, ia, oa, la = gpu_all(a)
@@ -150,6 +158,20 @@ def test_topk_extreme_k_and_long_rows(top_k):
     check_indices_exact(idx, O.topk(s.astype(np.float64), wl.row_lens(), top_k))
 
 
+def test_topk_without_workspace_on_rows_beyond_the_segment_merge():
+    """Rows whose segment candidates exceed what the merge keeps (9 segments of
+    16384 positions x top_k 4096 > 32768) take the selection that re-reads the
+    scores from memory; it needs no workspace and matches the oracle exactly."""
+    wl = make_workload(4, batch=2, lens=[140000, 5000], top_k=4096)
+    dev = B.DeviceInputs(wl)
+    assert B.dsa_topk_workspace_bytes(dev) == 0
+    rng = np.random.default_rng(140000)
+    s = rng.standard_normal((wl.rows, 140000)).astype(np.float32)
+    s[:, ::101] = s[:, 7:8]                               # ties across the row
+    idx = B.dsa_topk(dev, torch.from_numpy(s).cuda()).cpu().numpy()
+    check_indices_exact(idx, O.topk(s.astype(np.float64), wl.row_lens(), 4096))
+
+
 @pytest.mark.parametrize("long_len,top_k", [(32768, 1), (32768, 2048), (20000, 4096), (16384, 7),
                                              (16384, 2048), (8192, 2047), (8192, 1)])
 def test_topk_register_resident_lengths_with_ties(long_len, top_k):
@@ -167,37 +189,32 @@ def test_topk_register_resident_lengths_with_ties(long_len, top_k):
 
 # ------------------------------------------------------- full workload sizes
 
-FULL_SAMPLES = {
-    2: [0, 7, 31],
-    4: [0, 5, 15],
-    5: [0, 33, 63],
-    6: [0, 33, 63],
-    1: None,
-}
-
-
 @pytest.mark.parametrize("cfg", [1, 2, 4, 5, 6])
-def test_full_size_sampled_rows(cfg):
+def test_full_size_every_row(cfg):
+    """Every workload at its full size, in the launch configuration the benchmark
+    times (dsa_forward into a workspace), checked on every row: scores within the
+    fp32 bound, indices exact on the GPU's own scores and within the tie band on
+    the oracle's fp64 scores, attention within the output tolerance."""
     say(f"[parity] full cfg {cfg}: generating")
     wl = make_workload(cfg)
     dev = B.DeviceInputs(wl)
     say(f"[parity] full cfg {cfg}: forward on GPU")
-    out, lse, idx = B.dsa_forward(dev)
-    sc = B.dsa_indexer_scores(dev)
+    ws = torch.empty(max(1, B.dsa_forward_workspace_bytes(dev)), dtype=torch.uint8, device="cuda")
+    out, lse, idx = B.dsa_forward(dev, ws=ws)
     torch.cuda.synchronize()
-    rows = FULL_SAMPLES[cfg] or list(range(wl.rows))
-    sc_h = sc[rows].cpu().numpy().astype(np.float64)
+    rows = list(range(wl.rows))
+    ld = (wl.max_seq_len + 63) // 64 * 64
+    sc_h = ws[: wl.rows * ld * 4].view(torch.float32).view(wl.rows, ld).cpu().numpy().astype(np.float64)
     idx_h = idx.cpu().numpy()
-    say(f"[parity] full cfg {cfg}: oracle on rows {rows if len(rows) < 10 else len(rows)}")
-    ref_sc = O.indexer_scores(wl, rows, ld=sc.shape[1])
+    say(f"[parity] full cfg {cfg}: oracle on all {len(rows)} rows")
+    ref_sc = O.indexer_scores(wl, rows, ld=ld)
     check_scores(wl, sc_h, ref_sc, rows)
-    check_indices_exact(idx_h[rows], O.topk(sc_h, wl.row_lens()[rows], wl.top_k))
-    ref_idx = O.topk(ref_sc, wl.row_lens()[rows], wl.top_k)
-    nd = sum(check_indices_band(idx_h[r], ref_idx[i], ref_sc[i], int(wl.row_lens()[r]), wl.top_k)
-             for i, r in enumerate(rows))
+    check_indices_exact(idx_h, O.topk(sc_h, wl.row_lens(), wl.top_k))
+    ref_idx = O.topk(ref_sc, wl.row_lens(), wl.top_k)
+    nd = sum(check_indices_band(idx_h[r], ref_idx[r], ref_sc[r], int(wl.row_lens()[r]), wl.top_k) for r in rows)
     say(f"[parity] full cfg {cfg}: {nd} band swaps")
-    ref_o, ref_l = O.sparse_attn(wl, idx_h, rows)
-    check_attention(wl, f64(out[rows]), f64(lse[rows]), ref_o, ref_l, f"full cfg {cfg}")
+    ref_o, ref_l = O.sparse_attn(wl, idx_h)
+    check_attention(wl, f64(out), f64(lse), ref_o, ref_l, f"full cfg {cfg}")
 
 
 @pytest.mark.parametrize("cfg", [3, 5, 6])
@@ -223,7 +240,20 @@ def test_prefill_permuted_paging_across_table_windows(cfg):
     check_attention(wl, f64(out[rows]), f64(lse[rows]), ref_o, ref_l, f"prefill windows cfg {cfg}")
 
 
-def test_full_prefill_sampled_rows():
+def prefill_check_rows(T, n_spread=200):
+    """Rows of the full prefill checked against the oracle: n_spread rows evenly
+    spread over the positions, the rows around the top_k boundary (2046..2049) and
+    the last 64 rows."""
+    return sorted(set(np.linspace(0, T - 1, n_spread).astype(int).tolist()) | {2046, 2047, 2048, 2049}
+                  | set(range(T - 64, T)))
+
+
+def test_full_prefill_rows_spread_over_positions():
+    """The full prefill (32768 causal rows) in the benchmark's launch configuration:
+    on 260+ rows spread over every position range, the scores are within the fp32
+    bound, the indices exact on the GPU's own scores and within the tie band on the
+    oracle's fp64 scores, and the attention within tolerance; on every row, the
+    index list has k_r = min(2048, t+1) ascending unique positions < t+1."""
     say("[parity] full prefill: generating 32768 x 128 x 576 queries")
     wl = make_workload(3)
     dev = B.DeviceInputs(wl)
@@ -231,14 +261,18 @@ def test_full_prefill_sampled_rows():
     ws = torch.empty(B.dsa_forward_workspace_bytes(dev), dtype=torch.uint8, device="cuda")
     out, lse, idx = B.dsa_forward(dev, ws=ws)
     torch.cuda.synchronize()
-    rows = [0, 1, 2046, 2047, 2048, 9999, 16384, 32767]
+    rows = prefill_check_rows(wl.rows)
     ld = (wl.max_seq_len + 63) // 64 * 64
     sc_h = ws[: wl.rows * ld * 4].view(torch.float32).view(wl.rows, ld)[rows].cpu().numpy().astype(np.float64)
     idx_h = idx.cpu().numpy()
-    say("[parity] full prefill: oracle")
+    say(f"[parity] full prefill: oracle on {len(rows)} rows")
     ref_sc = O.indexer_scores(wl, rows, ld=ld)
     check_scores(wl, sc_h, ref_sc, rows)
-    check_indices_exact(idx_h[rows], O.topk(sc_h, wl.row_lens()[rows], wl.top_k))
+    Lr = wl.row_lens()[rows]
+    check_indices_exact(idx_h[rows], O.topk(sc_h, Lr, wl.top_k))
+    ref_idx = O.topk(ref_sc, Lr, wl.top_k)
+    nd = sum(check_indices_band(idx_h[r], ref_idx[i], ref_sc[i], int(Lr[i]), wl.top_k) for i, r in enumerate(rows))
+    say(f"[parity] full prefill: {nd} band swaps")
     ref_o, ref_l = O.sparse_attn(wl, idx_h, rows)
     check_attention(wl, f64(out[rows]), f64(lse[rows]), ref_o, ref_l, "full prefill")
     # property at every row: k_r = min(2048, t+1) ascending unique positions < t+1
@@ -247,6 +281,10 @@ def test_full_prefill_sampled_rows():
     valid = idx_h >= 0
     assert (valid.sum(1) == k).all()
     assert (np.where(valid, idx_h, -1).max(1) < L).all()
+    col = np.arange(idx_h.shape[1])[None, :]
+    assert np.array_equal(valid, col < k[:, None])           # the k_r positions first, then -1
+    inner = (col[:, 1:] < k[:, None])                        # consecutive pairs inside the prefix
+    assert (np.diff(idx_h.astype(np.int64), axis=1)[inner] > 0).all()  # strictly ascending
     assert bool(torch.isfinite(out).all())
 
 
@@ -257,6 +295,37 @@ APPEND = {
     "fp8_mx_kv": (5, dict(batch=3, lens=[300, 1000, 453])),
     "mx_idx_fp32_kv": (6, dict(batch=2, n_q=2, lens=[700, 66])),
 }
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(
+        np.uint16)
+
+
+def _append_both(wl, dev, k_new, kv_new):
+    """The GPU's append (from device copies of the rows) and the oracle's (on host copies
+    of the pools): (gpu pools and scales, oracle pools and scales).  Rows are float32
+    for fp32 pools, bf16 bit patterns (uint16) otherwise."""
+    def to_dev(a):
+        return torch.from_numpy(a).cuda() if a.dtype == np.float32 else torch.from_numpy(a.view(np.int16)).view(
+            torch.bfloat16).cuda()
+    B.dsa_cache_append(dev, to_dev(k_new), to_dev(kv_new))
+    torch.cuda.synchronize()
+    kp, kvp = wl.k_pool.copy(), wl.kv_pool.copy()
+    ks = None if wl.k_scale is None else wl.k_scale.copy()
+    kvs = None if wl.kv_scale is None else wl.kv_scale.copy()
+    O.cache_append(wl, k_new, wl.idx_dtype, kp, ks)
+    O.cache_append(wl, kv_new, wl.kv_dtype, kvp, kvs)
+    return [("k_pool", dev.k_pool, kp), ("kv_pool", dev.kv_pool, kvp), ("k_scale", dev.k_scale, ks),
+            ("kv_scale", dev.kv_scale, kvs)]
+
+
+def _assert_same_bytes(case, pairs):
+    for name, got, ref in pairs:
+        if ref is None:
+            continue
+        g = got.cpu().numpy().reshape(ref.shape)
+        assert np.array_equal(g.view(np.uint8), np.ascontiguousarray(ref).view(np.uint8)), f"{case}: {name} differs"
 
 
 @pytest.mark.parametrize("case", list(APPEND))
@@ -272,24 +341,28 @@ def test_cache_append_matches_oracle(case):
     k_new = (rng.standard_normal((wl.rows, wl.d_I)) / np.sqrt(wl.d_I)).astype(np.float32)
     kv_new = (rng.standard_normal((wl.rows, wl.d_qk)) / np.sqrt(wl.d_qk)).astype(np.float32)
     if not f32:  # the new rows arrive in bf16
-        k_new = torch.from_numpy(k_new).to(torch.bfloat16).float().numpy()
-        kv_new = torch.from_numpy(kv_new).to(torch.bfloat16).float().numpy()
-    dt = torch.float32 if f32 else torch.bfloat16
-    B.dsa_cache_append(dev, torch.from_numpy(k_new).to(dt).cuda(), torch.from_numpy(kv_new).to(dt).cuda())
-    torch.cuda.synchronize()
-    # the oracle on host copies of the same pools
-    kp, kvp = wl.k_pool.copy(), wl.kv_pool.copy()
-    ks = None if wl.k_scale is None else wl.k_scale.copy()
-    kvs = None if wl.kv_scale is None else wl.kv_scale.copy()
-    O.cache_append(wl, k_new, wl.idx_dtype, kp, ks)
-    O.cache_append(wl, kv_new, wl.kv_dtype, kvp, kvs)
-    assert not np.array_equal(kvp, wl.kv_pool)  # the append changed something
-    for name, got, ref in [("k_pool", dev.k_pool, kp), ("kv_pool", dev.kv_pool, kvp),
-                           ("k_scale", dev.k_scale, ks), ("kv_scale", dev.kv_scale, kvs)]:
-        if ref is None:
-            continue
-        g = got.cpu().numpy().reshape(ref.shape)
-        assert np.array_equal(g.view(np.uint8), np.ascontiguousarray(ref).view(np.uint8)), f"{case}: {name} differs"
+        k_new, kv_new = _bf16_bits(k_new), _bf16_bits(kv_new)
+    pairs = _append_both(wl, dev, k_new, kv_new)
+    assert not np.array_equal(pairs[1][2], wl.kv_pool)  # the append changed something
+    _assert_same_bytes(case, pairs)
+
+
+@pytest.mark.parametrize("case", ["f32", "bf16"])
+def test_cache_append_copies_nan_payloads(case):
+    """Unquantized pools are copies: rows of NaN payloads (signalling and quiet, both
+    signs), infinities, -0 and subnormals land in the pools bit for bit."""
+    cfg, kw = APPEND[case]
+    wl = make_workload(cfg, **kw)
+    say(f"[parity] append NaN payloads {case}")
+    dev = B.DeviceInputs(wl)
+    if case == "f32":
+        pat = np.array([0x7F800001, 0xFF800001, 0x7FC00000, 0xFFC12345, 0x7FBFFFFF, 0x7F800000, 0xFF800000,
+                        0x00000001, 0x80000000, 0x3F800000], np.uint32)
+        mk = lambda w: np.resize(pat, (wl.rows, w)).view(np.float32)  # noqa: E731
+    else:
+        pat = np.array([0x7F81, 0xFF81, 0x7FC0, 0xFFC1, 0x7FBF, 0x7F80, 0xFF80, 0x0001, 0x8000, 0x3F80], np.uint16)
+        mk = lambda w: np.ascontiguousarray(np.resize(pat, (wl.rows, w)))  # noqa: E731
+    _assert_same_bytes(case, _append_both(wl, dev, mk(wl.d_I), mk(wl.d_qk)))
 
 
 # (rows, d_x, H_I, d_I, query format): one row and one k stage; ragged row tiles
@@ -381,21 +454,8 @@ def test_cache_append_edge_values_match_oracle(case):
         x[2] = rng.standard_normal(width).astype(np.float32) * 1e-36  # subnormal-range row
         return torch.from_numpy(x).to(torch.bfloat16).float().numpy()
 
-    k_new, kv_new = rows(wl.d_I), rows(wl.d_qk)
-    B.dsa_cache_append(dev, torch.from_numpy(k_new).to(torch.bfloat16).cuda(),
-                       torch.from_numpy(kv_new).to(torch.bfloat16).cuda())
-    torch.cuda.synchronize()
-    kp, kvp = wl.k_pool.copy(), wl.kv_pool.copy()
-    ks = None if wl.k_scale is None else wl.k_scale.copy()
-    kvs = None if wl.kv_scale is None else wl.kv_scale.copy()
-    O.cache_append(wl, k_new, wl.idx_dtype, kp, ks)
-    O.cache_append(wl, kv_new, wl.kv_dtype, kvp, kvs)
-    for name, got, ref in [("k_pool", dev.k_pool, kp), ("kv_pool", dev.kv_pool, kvp),
-                           ("k_scale", dev.k_scale, ks), ("kv_scale", dev.kv_scale, kvs)]:
-        if ref is None:
-            continue
-        g = got.cpu().numpy().reshape(ref.shape)
-        assert np.array_equal(g.view(np.uint8), np.ascontiguousarray(ref).view(np.uint8)), f"{case}: {name} differs"
+    k_new, kv_new = _bf16_bits(rows(wl.d_I)), _bf16_bits(rows(wl.d_qk))
+    _assert_same_bytes(case, _append_both(wl, dev, k_new, kv_new))
 
 
 def test_late_large_logit_takes_the_exact_second_pass():
