@@ -1,0 +1,61 @@
+"""The build's resource guard (CPU only): hipcc's per-kernel resource remarks are
+parsed, and a kernel that uses scratch memory or spills vector registers fails
+the build, since the hand-counted vmcnt waits of the LDS-ring kernels are exact
+only without compiler-issued memory operations in their loops."""
+import json
+import os
+
+import pytest
+
+from sparse_attention_lightningindexer_amd import build as Bld
+
+REMARKS = """\
+x.hip:10:1: remark: Function Name: _Z6kernelPf [-Rpass-analysis=kernel-resource-usage]
+x.hip:10:1: remark:     VGPRs: 40 [-Rpass-analysis=kernel-resource-usage]
+x.hip:10:1: remark:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis=kernel-resource-usage]
+x.hip:10:1: remark:     SGPRs Spill: 3 [-Rpass-analysis=kernel-resource-usage]
+x.hip:10:1: remark:     VGPRs Spill: 4 [-Rpass-analysis=kernel-resource-usage]
+x.hip:20:1: remark: Function Name: _Z5cleanPf [-Rpass-analysis=kernel-resource-usage]
+x.hip:20:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]
+x.hip:20:1: remark:     SGPRs Spill: 12 [-Rpass-analysis=kernel-resource-usage]
+x.hip:20:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+"""
+
+SPILLING_KERNEL = r"""
+#include <hip/hip_runtime.h>
+__global__ void spills(float* out, const int* idx) {
+    float a[256];  // dynamically indexed private array: lives in scratch memory
+    for (int i = 0; i < 256; ++i) a[i] = out[i * 64 + threadIdx.x];
+    out[threadIdx.x] = a[idx[threadIdx.x] & 255];
+}
+"""
+
+
+def test_parser_reads_every_kernel_and_flags_scratch_and_vgpr_spills():
+    u = Bld.resource_usage(REMARKS)
+    assert u["_Z6kernelPf"] == {"vgprs": 40, "scratch_bytes": 16, "sgpr_spill": 3, "vgpr_spill": 4}
+    assert u["_Z5cleanPf"]["sgpr_spill"] == 12
+    bad = Bld.resource_violations(u)
+    assert len(bad) == 1 and bad[0].startswith("_Z6kernelPf")   # SGPR spills go to VGPR lanes: allowed
+
+
+def test_a_kernel_using_scratch_fails_the_build(tmp_path):
+    if not os.path.exists(Bld.HIPCC):
+        pytest.skip("hipcc not installed")
+    src = tmp_path / "spills.hip"
+    src.write_text(SPILLING_KERNEL)
+    with pytest.raises(RuntimeError, match="scratch"):
+        Bld.compile_source(str(src), str(tmp_path / "spills.o"))
+
+
+def test_the_library_kernels_use_no_scratch():
+    """The last build's report lists the LDS-ring kernels (hand-counted waits) and
+    every kernel in it is free of scratch use and VGPR spills."""
+    path = os.path.join(Bld.OUT, "resource_usage.json")
+    if not os.path.exists(path):
+        pytest.skip("library not built")
+    report = json.load(open(path))
+    kernels = {k: v for per in report.values() for k, v in per.items()}
+    assert any("indexer_prefill_kernel" in k for k in kernels)
+    assert any("indexer_prolog_kernel" in k for k in kernels)
+    assert not Bld.resource_violations(kernels)
