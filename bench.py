@@ -3,11 +3,15 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skewed|fp8|tiny]
 
 A step is one dsa_forward over one batch of synthetic inputs already resident
-in HBM; several independent input sets rotate so that each step's cache rows
-come from HBM rather than the 256 MB Infinity Cache.  Prints one JSON line:
-whole-step throughput (query tokens/s), the roofline of the dominant kernel
-(timed with HIP events on the launch stream), and the CPU oracle timed on the
-host's cores over a bounded sample of the same workload.
+in HBM; for decode, eight independent input sets rotate (about 1.2 GB touched
+per cycle of sets) so that each step's cache rows come from HBM rather than
+the 256 MB Infinity Cache.  Prints one JSON line: whole-step throughput (query
+tokens/s), the roofline of the dominant kernel (timed with HIP events on the
+launch stream), and the CPU oracle timed on the host's cores over a bounded
+sample of the same workload.  The metric is quoted on decode B32 x 8k and
+prefill 32k: with the default decode workload, the line also carries a
+"prefill" record of the same form, whose roofline is the indexer and
+attention contractions against the bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -23,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "DSA tokens/s (LI+TopK+SFA), decode B32@8k & prefill 32k; % HBM/MFMA peak"
 WORKLOADS = {"tiny": 1, "decode": 2, "prefill": 3, "skewed": 4, "fp8": 5, "fp8pages": 6}
+WORKLOAD_NAMES = {v: k for k, v in WORKLOADS.items()}
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -200,31 +205,200 @@ def cpu_baseline_prolog(wl0, budget_s: float):
 
 
 def cpu_baseline(wl, budget_s: float):
-    """The oracle as it stands, on the host's cores, over a bounded sample of rows."""
+    """The oracle as it stands, on the host's cores, over a bounded sample of rows,
+    repeated for about budget_s seconds."""
     import numpy as np
     from oracle import oracle as O
-    rows_all = np.arange(wl.rows, dtype=np.int32)
     if wl.rows > 64:  # prefill: rows spread evenly over the causal range
-        sample = np.linspace(0, wl.rows - 1, 16).astype(np.int32)
-        what = f"16 of {wl.rows} query rows, evenly spaced over positions (whole stage per row)"
+        sample = np.linspace(0, wl.rows - 1, 64).astype(np.int32)
+        what = f"64 of {wl.rows} query rows, evenly spaced over positions (whole stage per row)"
     else:
-        sample = rows_all
+        sample = np.arange(wl.rows, dtype=np.int32)
         what = f"all {wl.rows} query rows of one step (whole stage)"
-    done, t0 = 0, time.perf_counter()
-    reps = 0
+    done, reps, t0 = 0, 0, time.perf_counter()
     while True:
         O.forward(wl, rows=sample)
         done += len(sample)
         reps += 1
-        if time.perf_counter() - t0 >= budget_s or wl.rows > 64:
+        if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    rate = done / dt
-    if wl.rows > 64:  # scale: the sampled rows' mean cost stands for all rows
-        what += f"; {dt:.1f} s"
+    return {"value": done / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": what + f" x {reps}; {dt:.1f} s"}
+
+
+def spin_then_time(call, n, stream):
+    """n calls back to back between two HIP events on `stream`, after a GPU spin of
+    ~0.6 ms per call so that the host has queued them all before the first runs;
+    returns microseconds per call."""
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda._sleep(600_000 * n)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3
+
+
+def measure(cfg, args, steps, warmup, nsets, extras):
+    """One workload: the timed dsa_forward steps, their spread, the per-stage
+    durations and the roofline of the dominant kernel (both stages of the indexer
+    + attention contraction for prefill); with `extras`, also the quantized
+    indexer's recall, the cache append and the indexer prolog."""
+    import numpy as np
+    import torch
+    from sparse_attention_lightningindexer_amd import binding as B
+    from sparse_attention_lightningindexer_amd.inputs import make_workload
+
+    print(f"[bench] generating {nsets} input set(s) of workload {cfg}", file=sys.stderr, flush=True)
+    sets = []
+    for s in range(nsets):
+        wl = make_workload(cfg, rotation=s)
+        dev = B.DeviceInputs(wl)
+        ws = torch.empty(max(1, B.dsa_forward_workspace_bytes(dev)), dtype=torch.uint8, device="cuda")
+        idx = torch.empty((wl.rows, wl.top_k), dtype=torch.int32, device="cuda")
+        sets.append((wl, dev, ws, idx))
+        if s == 0:
+            wl0 = wl
+    del wl
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        _, dev, ws, idx = sets[i % nsets]
+        B.dsa_forward(dev, indices_out=idx, ws=ws, stream=stream)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps of the whole stage
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = gpu_ms / steps
+    value = wl0.rows * steps / (gpu_ms / 1e3)
+    print(f"[bench] {wl0.cfg['name']}: {steps} steps, {ms_per_step * 1e3:.1f} us/step "
+          f"(wall {wall / steps * 1e6:.1f} us)", file=sys.stderr, flush=True)
+
+    # the spread of single steps: a separate loop (not the timed region) with an
+    # event between consecutive steps, after a spin that lets the host queue
+    # the loop ahead of the GPU
+    n_one = min(steps, 100)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_one + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(600_000 * n_one)
+    evs[0].record(stream)
+    for i in range(n_one):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    one = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_one)])
+    step_us = {"p10": float(np.percentile(one, 10)), "p50": float(np.percentile(one, 50)),
+               "p90": float(np.percentile(one, 90)), "steps": n_one}
+
+    # per-stage durations: the same kernels through the three unfused calls,
+    # each stage `steps` times back to back with the input sets rotating
+    scores = [torch.empty((s[0].rows, max(1, s[0].max_seq_len)), dtype=torch.float32, device="cuda")
+              for s in sets]
+    attn_ws = [torch.empty(max(1, B.dsa_sparse_attn_workspace_bytes(s[1])), dtype=torch.uint8, device="cuda")
+               for s in sets]
+    for i in range(nsets):  # every set's scores and indices, for the loops below
+        _, dev, _, idx = sets[i]
+        B.dsa_indexer_scores(dev, scores[i], stream=stream)
+        B.dsa_topk(dev, scores[i], indices=idx, stream=stream)
+    calls = {
+        "indexer": lambda i: B.dsa_indexer_scores(sets[i % nsets][1], scores[i % nsets], stream=stream),
+        "topk": lambda i: B.dsa_topk(sets[i % nsets][1], scores[i % nsets], indices=sets[i % nsets][3],
+                                     stream=stream),
+        "attention": lambda i: B.dsa_sparse_attn(sets[i % nsets][1], sets[i % nsets][3], ws=attn_ws[i % nsets],
+                                                 stream=stream),
+    }
+    stage_us = {name: spin_then_time(call, steps, stream) for name, call in calls.items()}
+    del scores, attn_ws
+    algo = algorithmic(wl0)
+    if cfg == 3:
+        # prefill: the indexer and attention contractions together against the
+        # bf16 MFMA peak (their flops over their kernel time)
+        nflops = algo["indexer"][1] + algo["attention"][1]
+        dur_us = stage_us["indexer"] + stage_us["attention"]
+        ach = nflops / (dur_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
+                "kernel": "indexer scoring + sparse attention (indexer_prefill_kernel, sfa_mla_kernel)",
+                "algorithmic_flops": nflops, "avg_us": dur_us,
+                "stage_frac": {k: algo[k][1] / (stage_us[k] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS
+                               for k in ("indexer", "attention")}}
     else:
-        what += f" x {reps}; {dt:.1f} s"
-    return {"value": rate, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle", "sample": what}
+        dom = max(stage_us, key=stage_us.get)
+        nbytes, nflops = algo[dom]
+        ach = nbytes / (stage_us[dom] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                "traffic": measured_traffic(dom, WORKLOAD_NAMES[cfg]),
+                "kernel": {"indexer": "indexer scoring (indexer_*_kernel)",
+                           "topk": "top-k (topk_reg_kernel or topk_kernel)",
+                           "attention": "sparse attention (sfa_mla_kernel, plus sfa_combine_kernel when split)"}[dom],
+                "algorithmic_bytes": nbytes, "algorithmic_flops": nflops, "avg_us": stage_us[dom],
+                "mfma_frac": nflops / (stage_us[dom] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "fp8e4m3+bf16", "mxfp8": "fp8e4m3+bf16"}[wl0.idx_dtype],
+        "data": "synthetic",
+        "config": {"workload": wl0.cfg["name"], "batch": wl0.batch, "n_q": wl0.n_q,
+                   "context": int(wl0.max_seq_len), "top_k": wl0.top_k, "index_heads": wl0.H_I,
+                   "index_dim": wl0.d_I, "heads": wl0.H, "d_qk": wl0.d_qk, "d_v": wl0.d_v,
+                   "paging": wl0.cfg["paging"], "input_sets": nsets},
+        "roofline": roof,
+        "step_us": step_us,
+        "stages_us": stage_us,
+    }
+    if extras and wl0.idx_dtype in ("e4m3", "mxfp8"):
+        # reported, not a parity bound: how much of the quantized indexer's
+        # Top-K the bf16 indexer (same drawn values, rounded to bf16) also
+        # selects, over every row of the first input set
+        wl_b = make_workload(cfg, rotation=0, idx_dtype="bf16")
+        dev_b = B.DeviceInputs(wl_b)
+        idx_b = B.dsa_topk(dev_b, B.dsa_indexer_scores(dev_b)).cpu().numpy()
+        idx_q = sets[0][3].cpu().numpy()
+        rec = [len(set(a[a >= 0].tolist()) & set(c[c >= 0].tolist())) / max(1, int((c >= 0).sum()))
+               for a, c in zip(idx_q, idx_b)]
+        res["topk_recall_vs_bf16"] = {"mean": float(np.mean(rec)), "min": float(np.min(rec)), "rows": len(rec)}
+        del dev_b
+    if extras:
+        # cache append (the step before the indexer): this step's index keys and
+        # latent rows written into the first input set's pools, quantized when
+        # the pool is; after every other measurement (it overwrites pool rows)
+        _, dev0, _, _ = sets[0]
+        dt = torch.bfloat16 if wl0.idx_dtype != "f32" else torch.float32
+        k_new = torch.randn(wl0.rows, wl0.d_I, device="cuda").to(dt)
+        kv_new = torch.randn(wl0.rows, wl0.d_qk, device="cuda").to(dt)
+        B.dsa_cache_append(dev0, k_new, kv_new, stream=stream)
+        res["append_us"] = spin_then_time(lambda i: B.dsa_cache_append(dev0, k_new, kv_new, stream=stream),
+                                          steps, stream)
+        if wl0.rows <= 256:
+            res["prolog"] = time_prolog(wl0, args, stream)
+            if not args.no_cpu:
+                res["prolog"]["cpu_baseline"] = cpu_baseline_prolog(wl0, min(args.cpu_budget, 5.0))
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl0, args.cpu_budget)
+    return res
 
 
 def main():
@@ -233,9 +407,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=list(WORKLOADS))
-    ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
+    ap.add_argument("--sets", type=int, default=8, help="rotating input sets (decode workloads)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="with the decode workload, skip the nested prefill 32k record")
+    ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB three times (byte-counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -256,168 +433,18 @@ def main():
               "(decode shards by sequence, with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from sparse_attention_lightningindexer_amd import binding as B
-    from sparse_attention_lightningindexer_amd.inputs import make_workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.lib()  # fail loudly when the HIP library is missing
     cfg = WORKLOADS[args.workload]
     nsets = 1 if cfg == 3 else args.sets  # prefill: one set already exceeds the caches many times over
-    print(f"[bench] generating {nsets} input set(s) of workload {args.workload}", file=sys.stderr, flush=True)
-    sets = []
-    for s in range(nsets):
-        wl = make_workload(cfg, rotation=s)
-        dev = B.DeviceInputs(wl)
-        ws = torch.empty(max(1, B.dsa_forward_workspace_bytes(dev)), dtype=torch.uint8, device="cuda")
-        idx = torch.empty((wl.rows, wl.top_k), dtype=torch.int32, device="cuda")
-        sets.append((wl, dev, ws, idx))
-        if s == 0:
-            wl0 = wl
-    del wl
-    stream = torch.cuda.current_stream()
-
-    def step(i):
-        _, dev, ws, idx = sets[i % nsets]
-        B.dsa_forward(dev, indices_out=idx, ws=ws, stream=stream)
-
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # timed region: exactly K steps of the whole stage
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
-    ms_per_step = gpu_ms / args.steps
-    rows = wl0.rows
-    value = rows * args.steps / (gpu_ms / 1e3)
-    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)",
-          file=sys.stderr, flush=True)
-
-    # the spread of single steps: a separate loop (not the timed region) with an
-    # event between consecutive steps; each step's time is the span between its
-    # two events on the launch stream, after a spin that lets the host queue
-    # the loop ahead of the GPU
-    n_one = min(args.steps, 100)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_one + 1)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(600_000 * n_one)
-    evs[0].record(stream)
-    for i in range(n_one):
-        step(i)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    one = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_one)])
-    step_us = {"p10": float(np.percentile(one, 10)), "p50": float(np.percentile(one, 50)),
-               "p90": float(np.percentile(one, 90)), "steps": n_one}
-
-    # per-stage durations: the same kernels through the three unfused calls.
-    # Each stage runs K times back to back (input sets rotating) between two
-    # HIP events on the launch stream, so an event's own cost is spread over K
-    # launches.  Before each loop the GPU spins (~0.25 ms per launch) so that
-    # the host has queued every call before the first one runs.
-    acc = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
-    scores = [torch.empty((s[0].rows, max(1, s[0].max_seq_len)), dtype=torch.float32, device="cuda")
-              for s in sets]
-    attn_ws = [torch.empty(max(1, B.dsa_sparse_attn_workspace_bytes(s[1])), dtype=torch.uint8, device="cuda")
-               for s in sets]
-    for i in range(nsets):  # every set's scores and indices, for the loops below
-        _, dev, _, idx = sets[i]
-        B.dsa_indexer_scores(dev, scores[i], stream=stream)
-        B.dsa_topk(dev, scores[i], indices=idx, stream=stream)
-    calls = {
-        "indexer": lambda i: B.dsa_indexer_scores(sets[i % nsets][1], scores[i % nsets], stream=stream),
-        "topk": lambda i: B.dsa_topk(sets[i % nsets][1], scores[i % nsets], indices=sets[i % nsets][3],
-                                     stream=stream),
-        "attention": lambda i: B.dsa_sparse_attn(sets[i % nsets][1], sets[i % nsets][3], ws=attn_ws[i % nsets],
-                                                 stream=stream),
-    }
-    for name, call in calls.items():
-        torch.cuda.synchronize()
-        torch.cuda._sleep(600_000 * args.steps)
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        for i in range(args.steps):
-            call(i)
-        s1.record(stream)
-        torch.cuda.synchronize()
-        acc[name] = s0.elapsed_time(s1)
-    stage_us = {k: v / args.steps * 1e3 for k, v in acc.items()}
-    algo = algorithmic(wl0)
-    dom = max(stage_us, key=stage_us.get)
-    nbytes, nflops = algo[dom]
-    dur_s = stage_us[dom] * 1e-6
-    if cfg == 3 and dom != "topk":
-        ach = nflops / dur_s / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / BF16_PEAK_TFLOPS}
-    else:
-        ach = nbytes / dur_s / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS}
-    roof["traffic"] = measured_traffic(dom, args.workload)
-    roof["kernel"] = {"indexer": "indexer scoring (indexer_*_kernel)", "topk": "top-k (topk_reg_kernel or topk_kernel)",
-                      "attention": "sparse attention (sfa_mla_kernel, plus sfa_combine_kernel when split)"}[dom]
-    roof["algorithmic_bytes"] = nbytes
-    roof["algorithmic_flops"] = nflops
-    roof["avg_us"] = stage_us[dom]
-
-    res = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "fp8e4m3+bf16", "mxfp8": "fp8e4m3+bf16"}[wl0.idx_dtype],
-        "data": "synthetic",
-        "config": {"workload": wl0.cfg["name"], "batch": wl0.batch, "n_q": wl0.n_q,
-                   "context": int(wl0.max_seq_len), "top_k": wl0.top_k, "index_heads": wl0.H_I,
-                   "index_dim": wl0.d_I, "heads": wl0.H, "d_qk": wl0.d_qk, "d_v": wl0.d_v,
-                   "paging": wl0.cfg["paging"], "input_sets": nsets},
-        "roofline": roof,
-        "step_us": step_us,
-        "stages_us": stage_us,
-    }
-    if wl0.idx_dtype in ("e4m3", "mxfp8"):
-        # reported, not a parity bound: how much of the quantized indexer's
-        # Top-K the bf16 indexer (same drawn values, rounded to bf16) also
-        # selects, over every row of the first input set
-        wl_b = make_workload(cfg, rotation=0, idx_dtype="bf16")
-        dev_b = B.DeviceInputs(wl_b)
-        idx_b = B.dsa_topk(dev_b, B.dsa_indexer_scores(dev_b)).cpu().numpy()
-        idx_q = sets[0][3].cpu().numpy()
-        rec = [len(set(a[a >= 0].tolist()) & set(c[c >= 0].tolist())) / max(1, int((c >= 0).sum()))
-               for a, c in zip(idx_q, idx_b)]
-        res["topk_recall_vs_bf16"] = {"mean": float(np.mean(rec)), "min": float(np.min(rec)), "rows": len(rec)}
-        del dev_b
-    # cache append (the step before the indexer): this step's index keys and
-    # latent rows written into the first input set's pools, quantized when the
-    # pool is; timed like the stages, after every other measurement (it
-    # overwrites those pool rows)
-    _, dev0, _, _ = sets[0]
-    k_new = torch.randn(wl0.rows, wl0.d_I, device="cuda").to(torch.bfloat16 if wl0.idx_dtype != "f32" else torch.float32)
-    kv_new = torch.randn(wl0.rows, wl0.d_qk, device="cuda").to(k_new.dtype)
-    B.dsa_cache_append(dev0, k_new, kv_new, stream=stream)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(600_000 * args.steps)
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
-    for _ in range(args.steps):
-        B.dsa_cache_append(dev0, k_new, kv_new, stream=stream)
-    a1.record(stream)
-    torch.cuda.synchronize()
-    res["append_us"] = a0.elapsed_time(a1) / args.steps * 1e3
-    if wl0.rows <= 256:
-        res["prolog"] = time_prolog(wl0, args, stream)
-        if not args.no_cpu:
-            res["prolog"]["cpu_baseline"] = cpu_baseline_prolog(wl0, min(args.cpu_budget, 5.0))
+    res = measure(cfg, args, args.steps, args.warmup, nsets, extras=True)
+    if cfg == 2 and not args.no_prefill:
+        # the metric is quoted on decode B32 x 8k and prefill 32k: the prefill
+        # record rides in the same line, with its own roofline and CPU baseline
+        res["prefill"] = measure(3, args, args.prefill_steps, min(args.warmup, 3), 1, extras=False)
     if args.copy_calib:
         src = torch.randn(args.copy_calib * 2 ** 18, device="cuda")
         dst = torch.empty_like(src)
@@ -425,9 +452,6 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    if not args.no_cpu:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl0, args.cpu_budget)
     print(json.dumps(res))
 
 
