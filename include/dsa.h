@@ -24,6 +24,8 @@
  *  - Ownership: the caller owns every buffer, workspaces included.  The
  *    library allocates no memory and keeps no state between calls; calls on
  *    different streams are independent when each has its own workspace.
+ *    The one exception is dsa_forward_noalloc, which works in a fixed
+ *    per-GPU scratch array of the library (see there).
  *  - Asynchrony: all device work is enqueued on `stream` (a hipStream_t, or
  *    NULL for the null stream); nothing synchronizes the device.
  *  - Layout: row-major, innermost dimension contiguous.  A query row is a
@@ -219,6 +221,30 @@ size_t dsa_forward_workspace_bytes(const dsa_batch* batch, const dsa_indexer_arg
 dsa_status dsa_forward(const dsa_batch* batch, const dsa_indexer_args* idx,
                        const dsa_attn_args* attn, int32_t top_k, int32_t* indices_out,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_forward_noalloc -- dsa_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The same computation as dsa_forward (bit for bit), with
+ * the workspace taken from the library's own per-GPU scratch array instead of
+ * a caller buffer; the caller still passes every input and output.
+ *
+ * The array holds dsa_forward_noalloc_max_bytes() bytes (32 MiB) on every GPU
+ * the library runs on, from the first call on that GPU until the process
+ * ends.  A batch whose dsa_forward_workspace_bytes exceeds it returns
+ * DSA_ERR_WORKSPACE before anything is launched (the decode workloads fit;
+ * long prefills do not).  Calls on one GPU share its array, so calls that
+ * overlap on one GPU (different streams, different host threads) race; calls
+ * on one stream are ordered and safe.  Nothing here allocates: no hipMalloc,
+ * no hipFree, no allocating library routine.  Errors: as dsa_forward, plus
+ * HIP when the array's device address cannot be obtained.
+ */
+dsa_status dsa_forward_noalloc(const dsa_batch* batch, const dsa_indexer_args* idx,
+                               const dsa_attn_args* attn, int32_t top_k, int32_t* indices_out,
+                               void* stream);
+
+/* Bytes of the per-GPU scratch array dsa_forward_noalloc works in. */
+size_t dsa_forward_noalloc_max_bytes(void);
 
 /*
  * dsa_cache_append -- write this step's index keys and latent KV rows into the

@@ -10,6 +10,7 @@ Functions with the C names:
     dsa_topk(dev, scores, top_k=None)             -> indices int32 [rows, top_k]
     dsa_sparse_attn(dev, indices, top_k=None)     -> (out, lse)
     dsa_forward(dev, top_k=None, indices_out=...) -> (out, lse, indices)
+    dsa_forward_noalloc(dev, top_k=None, indices_out=None) -> (out, lse, indices_out)
     dsa_cache_append(dev, k_new, kv_new)
     dsa_indexer_prolog(pd, q_fmt)                 -> (q, q_scale, head_w, k_norm)
 and their *_workspace_bytes queries, where `dev` is a DeviceInputs (device
@@ -72,7 +73,8 @@ _lib = None
 #: every entry point include/dsa.h declares
 EXPORTS = ("dsa_status_string", "dsa_version", "dsa_indexer_scores", "dsa_topk_workspace_bytes",
            "dsa_topk", "dsa_sparse_attn_workspace_bytes", "dsa_sparse_attn",
-           "dsa_forward_workspace_bytes", "dsa_forward", "dsa_cache_append", "dsa_indexer_prolog")
+           "dsa_forward_workspace_bytes", "dsa_forward", "dsa_forward_noalloc", "dsa_forward_noalloc_max_bytes",
+           "dsa_cache_append", "dsa_indexer_prolog")
 
 
 def lib():
@@ -109,6 +111,11 @@ def lib():
         L.dsa_forward.restype = C.c_int
         L.dsa_forward.argtypes = [P(dsa_batch), P(dsa_indexer_args), P(dsa_attn_args), C.c_int32, C.c_void_p,
                                   C.c_void_p, S, C.c_void_p]
+        L.dsa_forward_noalloc.restype = C.c_int
+        L.dsa_forward_noalloc.argtypes = [P(dsa_batch), P(dsa_indexer_args), P(dsa_attn_args), C.c_int32,
+                                          C.c_void_p, C.c_void_p]
+        L.dsa_forward_noalloc_max_bytes.restype = S
+        L.dsa_forward_noalloc_max_bytes.argtypes = []
         _lib = L
     return _lib
 
@@ -246,6 +253,15 @@ def dsa_forward(dev: DeviceInputs, top_k=None, indices_out=None, ws=None, stream
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev.q.device)
     _check(lib().dsa_forward(C.byref(dev.batch), C.byref(dev.idx), C.byref(dev.attn), top_k, _ptr(indices_out),
                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "dsa_forward")
+    return dev.out, dev.lse, indices_out
+
+
+def dsa_forward_noalloc(dev: DeviceInputs, top_k=None, indices_out=None, stream=None):
+    """dsa_forward in the library's per-GPU scratch array (no workspace argument);
+    indices_out may be None."""
+    top_k = dev.top_k if top_k is None else top_k
+    _check(lib().dsa_forward_noalloc(C.byref(dev.batch), C.byref(dev.idx), C.byref(dev.attn), top_k,
+                                     _ptr(indices_out), _stream(stream)), "dsa_forward_noalloc")
     return dev.out, dev.lse, indices_out
 
 

@@ -25,7 +25,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["indexer.hip", "topk.hip", "sfa.hip", "append.hip", "prolog.hip", "dsa_api.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "sfa.hip", "append.hip", "prolog.hip", "scratch.hip", "dsa_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

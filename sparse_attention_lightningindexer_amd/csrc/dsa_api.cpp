@@ -148,6 +148,9 @@ int64_t forward_ld(const dsa_batch* b) { return ((int64_t)b->max_seq_len + 63) /
 
 dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
+dsa_status forward_impl(const dsa_batch* batch, const dsa_indexer_args* idx, const dsa_attn_args* attn,
+                        int32_t top_k, int32_t* indices_out, void* ws, size_t ws_bytes, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -224,6 +227,30 @@ size_t dsa_forward_workspace_bytes(const dsa_batch* batch, const dsa_indexer_arg
 
 dsa_status dsa_forward(const dsa_batch* batch, const dsa_indexer_args* idx, const dsa_attn_args* attn,
                        int32_t top_k, int32_t* indices_out, void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl(batch, idx, attn, top_k, indices_out, ws, ws_bytes, stream);
+}
+
+dsa_status dsa_forward_noalloc(const dsa_batch* batch, const dsa_indexer_args* idx, const dsa_attn_args* attn,
+                               int32_t top_k, int32_t* indices_out, void* stream) {
+    dsa_status s = check_batch(batch);
+    if (s != DSA_OK) return s;
+    if ((s = check_indexer(batch, idx)) != DSA_OK) return s;
+    if ((s = check_attn(batch, attn)) != DSA_OK) return s;
+    if (top_k < 1 || top_k > kMaxTopK) return DSA_ERR_SHAPE;
+    if (dsa_forward_workspace_bytes(batch, idx, attn, top_k) > dsa::kScratchBytes) return DSA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (dsa::scratch_for_current_device(&ws) != hipSuccess) return DSA_ERR_HIP;
+    return forward_impl(batch, idx, attn, top_k, indices_out, ws, dsa::kScratchBytes, stream);
+}
+
+size_t dsa_forward_noalloc_max_bytes(void) { return dsa::kScratchBytes; }
+
+}  // extern "C"
+
+namespace {
+
+dsa_status forward_impl(const dsa_batch* batch, const dsa_indexer_args* idx, const dsa_attn_args* attn,
+                        int32_t top_k, int32_t* indices_out, void* ws, size_t ws_bytes, void* stream) {
     dsa_status s = check_batch(batch);
     if (s != DSA_OK) return s;
     if ((s = check_indexer(batch, idx)) != DSA_OK) return s;
@@ -250,6 +277,10 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_indexer_args* idx, cons
     if ((e = dsa::launch_topk(T, st)) != hipSuccess) return DSA_ERR_HIP;
     return hip_status(dsa::launch_sparse_attn(attn_launch(batch, attn, indices, top_k, attn_ws_p), st));
 }
+
+}  // namespace
+
+extern "C" {
 
 dsa_status dsa_cache_append(const dsa_batch* batch, const void* k_new, const void* kv_new, dsa_dtype new_dtype,
                             const dsa_cache* k, const dsa_cache* kv, void* stream) {

@@ -87,6 +87,12 @@ struct PrologLaunch {
     uint16_t* k_norm;          // bf16 [rows][d_I]
 };
 
+// The no-allocation entry point's device workspace: a file-scope array of
+// this many bytes per GPU (scratch.hip); its device address for the current
+// device, looked up once per device.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t scratch_for_current_device(void** ptr);
+
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st);
 hipError_t launch_indexer_prolog(const PrologLaunch& a, hipStream_t st);
 hipError_t launch_cache_append(const AppendLaunch& a, hipStream_t st);

@@ -96,6 +96,20 @@ def test_validation_errors_are_returned_before_any_launch():
     assert lib.dsa_sparse_attn(ref(batch), ref(kv_mx), 0x10000, 16, 0x10000, need, None) == B.DSA_ERR_NULL
 
 
+def test_noalloc_forward_refuses_batches_beyond_its_scratch_before_any_launch():
+    """dsa_forward_noalloc checks the batch's workspace against its fixed per-GPU
+    array on the host: a 4096-row prefill needs more and is refused without any
+    HIP call (this runs without a GPU)."""
+    lib = B.lib()
+    assert lib.dsa_forward_noalloc_max_bytes() == 32 << 20
+    wl = make_workload(2, batch=1, n_q=4096, lens=[4096], top_k=2048)
+    batch, idx, attn = _fake_structs(wl)
+    ref = C.byref
+    assert lib.dsa_forward_workspace_bytes(ref(batch), ref(idx), ref(attn), 2048) > (32 << 20)
+    assert lib.dsa_forward_noalloc(ref(batch), ref(idx), ref(attn), 2048, None, None) == B.DSA_ERR_WORKSPACE
+    assert lib.dsa_forward_noalloc(None, ref(idx), ref(attn), 2048, None, None) == B.DSA_ERR_NULL
+
+
 def test_workspace_sizes_follow_the_split_rule():
     lib = B.lib()
     for cfg, kw in ((2, {}), (4, dict(lens=[5000] * 8)), (5, dict(batch=64, lens=100))):
