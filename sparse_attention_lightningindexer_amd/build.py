@@ -9,9 +9,10 @@ over loads issued outside the compiler's bookkeeping (global_load_lds into an
 LDS ring).  Those counts are exact only while the compiler adds no vector
 memory operation of its own to the loops, and register spills to scratch are
 such operations.  Every source is therefore compiled with the compiler's
-per-kernel resource remarks, and the build fails if any kernel uses scratch
-memory or spills vector registers.  The per-kernel figures are written to
-_build/resource_usage.json.
+per-kernel resource remarks, and the build fails if a kernel of a source that
+issues such loads (one that calls wait_vmcnt) uses scratch memory or spills
+vector registers.  In the other sources a spill costs only time; it is
+reported.  The per-kernel figures are written to _build/resource_usage.json.
 """
 import json
 import os
@@ -78,10 +79,18 @@ def compile_source(path: str, obj: str, verbose: bool = False) -> dict:
         print(msgs)
     usage = resource_usage(text)
     bad = resource_violations(usage)
-    if bad:
+    if bad and uses_counted_waits(path):
         raise RuntimeError(f"{name}: kernels using scratch memory or spilling vector registers "
                            "(hand-counted vmcnt waits would be wrong):\n  " + "\n  ".join(bad))
+    if bad and verbose:
+        print(f"{name}: spills (no hand-counted waits in this source):\n  " + "\n  ".join(bad))
     return usage
+
+
+def uses_counted_waits(path: str) -> bool:
+    """Whether a source waits on hand-counted vmcnt values (calls wait_vmcnt)."""
+    with open(path) as fh:
+        return "wait_vmcnt" in fh.read()
 
 
 def build(verbose: bool = False) -> str:

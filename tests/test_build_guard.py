@@ -23,6 +23,7 @@ x.hip:20:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
 
 SPILLING_KERNEL = r"""
 #include <hip/hip_runtime.h>
+// this source stands for one with hand-counted waits: wait_vmcnt
 __global__ void spills(float* out, const int* idx) {
     float a[256];  // dynamically indexed private array: lives in scratch memory
     for (int i = 0; i < 256; ++i) a[i] = out[i * 64 + threadIdx.x];
@@ -39,23 +40,30 @@ def test_parser_reads_every_kernel_and_flags_scratch_and_vgpr_spills():
     assert len(bad) == 1 and bad[0].startswith("_Z6kernelPf")   # SGPR spills go to VGPR lanes: allowed
 
 
-def test_a_kernel_using_scratch_fails_the_build(tmp_path):
+def test_a_kernel_using_scratch_fails_the_build_where_waits_are_counted(tmp_path):
     if not os.path.exists(Bld.HIPCC):
         pytest.skip("hipcc not installed")
     src = tmp_path / "spills.hip"
     src.write_text(SPILLING_KERNEL)
     with pytest.raises(RuntimeError, match="scratch"):
         Bld.compile_source(str(src), str(tmp_path / "spills.o"))
+    # the same kernel in a source without counted waits builds (the spill is reported)
+    src2 = tmp_path / "spills_plain.hip"
+    src2.write_text(SPILLING_KERNEL.replace("wait_vmcnt", "no counted waits"))
+    usage = Bld.compile_source(str(src2), str(tmp_path / "spills_plain.o"))
+    assert Bld.resource_violations(usage)
 
 
-def test_the_library_kernels_use_no_scratch():
-    """The last build's report lists the LDS-ring kernels (hand-counted waits) and
-    every kernel in it is free of scratch use and VGPR spills."""
+def test_the_library_kernels_with_counted_waits_use_no_scratch():
+    """The last build's report lists the LDS-ring kernels (hand-counted waits), and
+    every kernel of their sources is free of scratch use and VGPR spills."""
     path = os.path.join(Bld.OUT, "resource_usage.json")
     if not os.path.exists(path):
         pytest.skip("library not built")
     report = json.load(open(path))
-    kernels = {k: v for per in report.values() for k, v in per.items()}
+    strict = [s for s in report if Bld.uses_counted_waits(os.path.join(Bld.CSRC, s))]
+    assert sorted(strict) == ["indexer.hip", "prolog.hip"]
+    kernels = {k: v for s in strict for k, v in report[s].items()}
     assert any("indexer_prefill_kernel" in k for k in kernels)
     assert any("indexer_prolog_kernel" in k for k in kernels)
     assert not Bld.resource_violations(kernels)
