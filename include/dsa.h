@@ -87,14 +87,23 @@ typedef enum {
     DSA_SCALE_E8M0 = 2        /* one OCP MX E8M0 byte, 2^(b-127), per `group`      */
 } dsa_scale_kind;
 
-/* A paged cache pool: [num_blocks][block_size][width] elements of `dtype`.
- * Index-K pool ([B] §2.1: the indexer reads the paged K cache directly) and
- * MLA latent KV pool ([D] §2.2: KV compressed into a low-rank latent row
- * per position, shared by all heads).  For quantized pools ([A] §5
- * "Layered Quantization") `scales` holds [num_blocks][block_size]
- * [ceil(width/group)] factors; the element value is value(code) * factor,
- * element c using factor c/group (a last, shorter group when group does not
- * divide width). */
+/* A paged cache pool of num_blocks blocks of block_size (64) positions, each
+ * position a row of `width` elements of `dtype`.  Index-K pool ([B] §2.1: the
+ * indexer reads the paged K cache directly) and MLA latent KV pool ([D] §2.2:
+ * KV compressed into a low-rank latent row per position, shared by all
+ * heads).  Element c of row o of block p is at
+ *     data + p*block_stride + o*row_stride + c        (in elements of dtype)
+ * and, for quantized pools ([A] §5 "Layered Quantization"), its factor at
+ *     scales + p*scale_block_stride + o*scale_row_stride + c/group
+ * (in scale elements: fp32 or E8M0 bytes); the element value is value(code) *
+ * factor, with a last, shorter group when group does not divide width.  A
+ * stride of 0 means the dense layout: row_stride = width, block_stride =
+ * 64*row_stride, scale_row_stride = ceil(width/group), scale_block_stride =
+ * 64*scale_row_stride.  Strides are >= 0 and row_stride >= width; for BF16
+ * and E4M3 pools the data pointer and both data strides (in bytes) must be
+ * multiples of 16 (rows are read in 16-byte pieces), for F32 pools of 4; an
+ * E8M0 index-K scale row (its four bytes) must be 4-byte aligned.  Distinct
+ * positions must not overlap (the caller's layout; it is not checked). */
 typedef struct {
     const void* data;           /* device, see above                               */
     const void* scales;         /* device, fp32 or E8M0 bytes; NULL when NONE      */
@@ -103,6 +112,10 @@ typedef struct {
     int32_t group;              /* elements per scale: 128 (F32 kind), 32 (E8M0)   */
     int32_t width;              /* elements per position: d_I or d_qk              */
     int64_t num_blocks;         /* blocks in the pool                              */
+    int64_t block_stride;       /* elements between blocks, 0: dense               */
+    int64_t row_stride;         /* elements between positions of a block, 0: dense */
+    int64_t scale_block_stride; /* scale elements between blocks, 0: dense         */
+    int64_t scale_row_stride;   /* scale elements between positions, 0: dense      */
 } dsa_cache;
 
 /* The batch: sequences, their lengths and the shared block table ([D] §8:

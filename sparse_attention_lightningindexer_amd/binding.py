@@ -45,9 +45,11 @@ class dsa_batch(C.Structure):
 
 
 class dsa_cache(C.Structure):
+    """A paged pool; strides are in elements (of the data, then of the scales), 0 = dense."""
     _fields_ = [("data", C.c_void_p), ("scales", C.c_void_p), ("dtype", C.c_int),
                 ("scale_kind", C.c_int), ("group", C.c_int32), ("width", C.c_int32),
-                ("num_blocks", C.c_int64)]
+                ("num_blocks", C.c_int64), ("block_stride", C.c_int64), ("row_stride", C.c_int64),
+                ("scale_block_stride", C.c_int64), ("scale_row_stride", C.c_int64)]
 
 
 class dsa_indexer_args(C.Structure):

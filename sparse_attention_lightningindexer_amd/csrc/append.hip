@@ -52,20 +52,19 @@ __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.
 // an E8M0 scale per `group`.  Every lane of the wave calls this (the
 // reductions are wave-wide); `active` says whether the thread holds values.
 __device__ __forceinline__ void store_vector(const float (&x)[4], uint2 raw, bool active, int t, int width,
-                                             int kind, int group, void* pool, void* scales, int64_t prow) {
+                                             int kind, int group, void* pool_row, void* scale_row) {
     if (kind == 0) {
         if (active)
-            *reinterpret_cast<float4*>(static_cast<float*>(pool) + prow * width + 4 * t) =
+            *reinterpret_cast<float4*>(static_cast<float*>(pool_row) + 4 * t) =
                 make_float4(x[0], x[1], x[2], x[3]);
         return;
     }
     if (kind == 1) {
-        if (active) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(pool) + prow * width + 4 * t) = raw;
+        if (active) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(pool_row) + 4 * t) = raw;
         return;
     }
     float a = active ? fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))) : 0.f;
     a = lane_max(a, group / 4);
-    const int ng = (width + group - 1) / group;
     const int gidx = (4 * t) / group;
     const bool first = active && (4 * t) % group == 0;
     uint32_t codes;
@@ -73,7 +72,7 @@ __device__ __forceinline__ void store_vector(const float (&x)[4], uint2 raw, boo
         const float scale = a > 0.f ? a / 448.f : 1.f;
         codes = e4m3x4(clamp448(x[0] / scale), clamp448(x[1] / scale), clamp448(x[2] / scale),
                        clamp448(x[3] / scale));
-        if (first) static_cast<float*>(scales)[prow * ng + gidx] = scale;
+        if (first) static_cast<float*>(scale_row)[gidx] = scale;
     } else {
         int e2 = 0;
         (void)frexpf(a, &e2);
@@ -81,17 +80,17 @@ __device__ __forceinline__ void store_vector(const float (&x)[4], uint2 raw, boo
         e = min(max(e, -127), 127);
         codes = e4m3x4(clamp448(ldexpf(x[0], -e)), clamp448(ldexpf(x[1], -e)), clamp448(ldexpf(x[2], -e)),
                        clamp448(ldexpf(x[3], -e)));
-        if (first) static_cast<uint8_t*>(scales)[prow * ng + gidx] = (uint8_t)(e + 127);
+        if (first) static_cast<uint8_t*>(scale_row)[gidx] = (uint8_t)(e + 127);
     }
-    if (active) *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(pool) + prow * width + 4 * t) = codes;
+    if (active) *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(pool_row) + 4 * t) = codes;
 }
 
 template <class In>
 __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
     const In* __restrict__ k_new, const In* __restrict__ kv_new, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ table, int max_blocks, int n_q, int max_seq_len, int k_width, int k_kind,
-    int k_group, int64_t k_blocks, void* k_pool, void* k_scales, int kv_width, int kv_kind, int kv_group,
-    int64_t kv_blocks, void* kv_pool, void* kv_scales) {
+    int k_group, int64_t k_blocks, PoolLayout k_l, void* k_pool, void* k_scales, int kv_width, int kv_kind,
+    int kv_group, int64_t kv_blocks, PoolLayout kv_l, void* kv_pool, void* kv_scales) {
     const int r = blockIdx.x, b = r / n_q, i = r % n_q;
     const int s = clamp_len(seq_lens, b, max_seq_len) - n_q + i;  // this token's position
     if (s < 0) return;  // block-uniform
@@ -101,7 +100,9 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
     const bool active = 4 * t < width;
     const int64_t pb = phys_block(table, max_blocks, b, s / kBlock, key ? k_blocks : kv_blocks);
     if (pb < 0) return;  // absent block: nothing is written (uniform per pool, hence per wave)
-    const int64_t prow = pb * kBlock + s % kBlock;
+    const PoolLayout& Lp = key ? k_l : kv_l;
+    const int64_t roff = pb * Lp.bs + (s % kBlock) * Lp.rs;    // this token's row, in bytes
+    const int64_t soff = pb * Lp.sbs + (s % kBlock) * Lp.srs;  // and its scales
     float x[4] = {0.f, 0.f, 0.f, 0.f};
     uint2 raw = make_uint2(0u, 0u);  // bf16 input codes, stored as they are into a bf16 pool
     if (active) {
@@ -119,9 +120,11 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
         }
     }
     if (key)
-        store_vector(x, raw, active, t, k_width, k_kind, k_group, k_pool, k_scales, prow);
+        store_vector(x, raw, active, t, k_width, k_kind, k_group, static_cast<uint8_t*>(k_pool) + roff,
+                     static_cast<uint8_t*>(k_scales) + soff);
     else
-        store_vector(x, raw, active, t, kv_width, kv_kind, kv_group, kv_pool, kv_scales, prow);
+        store_vector(x, raw, active, t, kv_width, kv_kind, kv_group, static_cast<uint8_t*>(kv_pool) + roff,
+                     static_cast<uint8_t*>(kv_scales) + soff);
 }
 
 }  // namespace
@@ -132,14 +135,15 @@ hipError_t launch_cache_append(const AppendLaunch& a, hipStream_t st) {
     if (a.in_f32)
         hipLaunchKernelGGL(cache_append_kernel<float>, dim3(rows), dim3(kAppendThreads), 0, st,
                            (const float*)a.k_new, (const float*)a.kv_new, a.seq_lens, a.table, a.max_blocks,
-                           a.n_q, a.max_seq_len, a.k_width, a.k_kind, a.k_group, a.k_blocks, a.k_pool,
-                           a.k_scales, a.kv_width, a.kv_kind, a.kv_group, a.kv_blocks, a.kv_pool, a.kv_scales);
+                           a.n_q, a.max_seq_len, a.k_width, a.k_kind, a.k_group, a.k_blocks, a.k_l, a.k_pool,
+                           a.k_scales, a.kv_width, a.kv_kind, a.kv_group, a.kv_blocks, a.kv_l, a.kv_pool,
+                           a.kv_scales);
     else
         hipLaunchKernelGGL(cache_append_kernel<uint16_t>, dim3(rows), dim3(kAppendThreads), 0, st,
                            (const uint16_t*)a.k_new, (const uint16_t*)a.kv_new, a.seq_lens, a.table,
                            a.max_blocks, a.n_q, a.max_seq_len, a.k_width, a.k_kind, a.k_group, a.k_blocks,
-                           a.k_pool, a.k_scales, a.kv_width, a.kv_kind, a.kv_group, a.kv_blocks, a.kv_pool,
-                           a.kv_scales);
+                           a.k_l, a.k_pool, a.k_scales, a.kv_width, a.kv_kind, a.kv_group, a.kv_blocks, a.kv_l,
+                           a.kv_pool, a.kv_scales);
     return hipGetLastError();
 }
 

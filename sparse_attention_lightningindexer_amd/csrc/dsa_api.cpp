@@ -31,11 +31,47 @@ dsa_status check_batch(const dsa_batch* b) {
     return DSA_OK;
 }
 
+// A pool's byte layout from its element strides (0: the dense layout).
+// SHAPE when a stride is negative or too large, a row is narrower than the
+// width, or an alignment the kernels rely on does not hold: rows of BF16 and
+// E4M3 pools are read in 16-byte pieces, F32 rows and fp32 scales in 4 bytes.
+dsa_status pool_layout(const dsa_cache* c, dsa::PoolLayout* L) {
+    const int esz = c->dtype == DSA_F32 ? 4 : c->dtype == DSA_BF16 ? 2 : 1;
+    const bool scaled = c->scale_kind != DSA_SCALE_NONE;
+    const int ng = scaled && c->group > 0 ? (c->width + c->group - 1) / c->group : 0;
+    const int ssz = c->scale_kind == DSA_SCALE_F32 ? 4 : 1;
+    constexpr int64_t kMaxStride = int64_t(1) << 40;
+    const int64_t in[4] = {c->block_stride, c->row_stride, c->scale_block_stride, c->scale_row_stride};
+    for (int64_t v : in)
+        if (v < 0 || v > kMaxStride) return DSA_ERR_SHAPE;
+    const int64_t rs = c->row_stride != 0 ? c->row_stride : c->width;
+    if (rs < c->width) return DSA_ERR_SHAPE;
+    const int64_t bs = c->block_stride != 0 ? c->block_stride : 64 * rs;
+    const int64_t srs = c->scale_row_stride != 0 ? c->scale_row_stride : ng;
+    if (scaled && srs < ng) return DSA_ERR_SHAPE;
+    const int64_t sbs = c->scale_block_stride != 0 ? c->scale_block_stride : 64 * srs;
+    const int64_t align = esz == 4 ? 4 : 16;
+    if ((uintptr_t)c->data % align != 0 || (rs * esz) % align != 0 || (bs * esz) % align != 0) return DSA_ERR_SHAPE;
+    if (scaled && ssz == 4 && ((uintptr_t)c->scales % 4 != 0)) return DSA_ERR_SHAPE;
+    L->bs = bs * esz;
+    L->rs = rs * esz;
+    L->sbs = sbs * ssz;
+    L->srs = srs * ssz;
+    return DSA_OK;
+}
+
+dsa::PoolLayout layout_of(const dsa_cache* c) {
+    dsa::PoolLayout L{};
+    (void)pool_layout(c, &L);  // validated before any launch
+    return L;
+}
+
 dsa_status check_pool(const dsa_cache* c, int width) {
     if (c->data == nullptr) return DSA_ERR_NULL;
     if (c->num_blocks < 1 || c->width != width) return DSA_ERR_SHAPE;
     if (c->num_blocks * 64 > (int64_t)INT_MAX) return DSA_ERR_UNSUPPORTED;  // pool rows are int32
-    return DSA_OK;
+    dsa::PoolLayout L;
+    return pool_layout(c, &L);
 }
 
 dsa_status check_indexer(const dsa_batch* b, const dsa_indexer_args* a) {
@@ -59,6 +95,10 @@ dsa_status check_indexer(const dsa_batch* b, const dsa_indexer_args* a) {
               (a->k.scale_kind == DSA_SCALE_E8M0 && a->k.group == 32)))
             return DSA_ERR_UNSUPPORTED;
         if (a->k.scales == nullptr || (b->batch > 0 && a->q_scale == nullptr)) return DSA_ERR_NULL;
+        if (a->k.scale_kind == DSA_SCALE_E8M0) {  // a position's four E8M0 bytes are read as one dword
+            const dsa::PoolLayout L = layout_of(&a->k);
+            if ((uintptr_t)a->k.scales % 4 != 0 || L.srs % 4 != 0 || L.sbs % 4 != 0) return DSA_ERR_SHAPE;
+        }
         return DSA_OK;
     default:
         return DSA_ERR_UNSUPPORTED;
@@ -94,6 +134,7 @@ dsa::IndexerLaunch indexer_launch(const dsa_batch* b, const dsa_indexer_args* a,
     L.w = a->head_w;
     L.kpool = a->k.data;
     L.kscale = a->k.scales;
+    L.kl = layout_of(&a->k);
     L.seq_lens = b->seq_lens;
     L.table = b->block_table;
     L.max_blocks = b->max_blocks;
@@ -119,6 +160,7 @@ dsa::AttnLaunch attn_launch(const dsa_batch* b, const dsa_attn_args* a, const in
     L.q = a->q;
     L.kv = a->kv.data;
     L.kvscale = a->kv.scales;
+    L.kvl = layout_of(&a->kv);
     L.seq_lens = b->seq_lens;
     L.table = b->block_table;
     L.max_blocks = b->max_blocks;
@@ -309,6 +351,13 @@ dsa_status dsa_cache_append(const dsa_batch* batch, const void* k_new, const voi
     if (k->data == nullptr || kv->data == nullptr) return DSA_ERR_NULL;
     if ((kk >= 2 && k->scales == nullptr) || (kvk >= 2 && kv->scales == nullptr)) return DSA_ERR_NULL;
     dsa::AppendLaunch L{};
+    if ((s = pool_layout(k, &L.k_l)) != DSA_OK || (s = pool_layout(kv, &L.kv_l)) != DSA_OK) return s;
+    // fp32 rows are written 16 bytes at a time
+    for (const dsa_cache* c : {k, kv}) {
+        const dsa::PoolLayout& Lc = c == k ? L.k_l : L.kv_l;
+        if (c->dtype == DSA_F32 && ((uintptr_t)c->data % 16 != 0 || Lc.rs % 16 != 0 || Lc.bs % 16 != 0))
+            return DSA_ERR_SHAPE;
+    }
     L.in_f32 = new_dtype == DSA_F32;
     L.k_new = k_new;
     L.kv_new = kv_new;

@@ -22,7 +22,7 @@ namespace dsa {
 // --------------------------------------------------------------- fp32 path
 // Small fp32 shapes: one thread per (row, position); q and w of the row in LDS.
 __global__ __launch_bounds__(64) void indexer_f32_kernel(
-    const float* __restrict__ q, const float* __restrict__ w, const float* __restrict__ kpool,
+    const float* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ kpool, PoolLayout kl,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
     int64_t num_blocks, int n_q, int max_seq_len, int H, int D, float* __restrict__ scores,
     int64_t ld) {
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(64) void indexer_f32_kernel(
         scores[(int64_t)r * ld + s] = -INFINITY;
         return;
     }
-    const float* k = kpool + (p * kBlock + s % kBlock) * D;
+    const float* k = reinterpret_cast<const float*>(kpool + p * kl.bs + (s % kBlock) * kl.rs);
     float acc = 0.f;
     for (int j = 0; j < H; ++j) {
         float d = 0.f;
@@ -162,7 +162,7 @@ __device__ __forceinline__ float head_weighted_relu_sum(const f32x4 (&acc)[4], c
 template <class T, int NQ, int TPW, int NW>
 __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ q_scale, const float* __restrict__ w,
-    const uint8_t* __restrict__ kpool, const void* __restrict__ kscale,
+    const uint8_t* __restrict__ kpool, const void* __restrict__ kscale, PoolLayout kl,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
     int64_t num_blocks, int n_q, int max_seq_len, float* __restrict__ scores, int64_t ld) {
     static_assert(NQ <= 2, "decode rows per sequence");
@@ -201,12 +201,12 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
         const int64_t p = pt[u] < 0 ? 0 : pt[u];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {  // an absent block reads block 0 (its scores are -inf)
-            const uint8_t* v = kpool + (p * kBlock + 16 * nt + j) * (int64_t)T::ROW;
+            const uint8_t* v = kpool + p * kl.bs + (16 * nt + j) * kl.rs;
 #pragma unroll
             for (int ks = 0; ks < T::KSTEPS; ++ks) f[nt][ks] = load_frag<T>(v, ks, g);
-            if constexpr (T::SCALED) sc[nt] = static_cast<const float*>(kscale)[p * kBlock + 16 * nt + j];
-            if constexpr (T::MX)
-                sc[nt] = __int_as_float(static_cast<const uint8_t*>(kscale)[(p * kBlock + 16 * nt + j) * 4 + g]);
+            const uint8_t* sp = static_cast<const uint8_t*>(kscale) + p * kl.sbs + (16 * nt + j) * kl.srs;
+            if constexpr (T::SCALED) sc[nt] = *reinterpret_cast<const float*>(sp);
+            if constexpr (T::MX) sc[nt] = __int_as_float(sp[g]);
         }
     };
     load_tile(0, kf[0], ksc[0]);
@@ -284,7 +284,7 @@ constexpr int kIdxRing = 4;
 template <class T>
 __global__ __launch_bounds__(512) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ q_scale, const float* __restrict__ w,
-    const uint8_t* __restrict__ kpool, const void* __restrict__ kscale,
+    const uint8_t* __restrict__ kpool, const void* __restrict__ kscale, PoolLayout kl,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
     int64_t num_blocks, int n_q, int max_seq_len, float* __restrict__ scores, int64_t ld) {
     constexpr int UNITS = T::ROW / 16;              // 16-byte units per K row
@@ -331,16 +331,17 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
         if (t >= max_blocks || p < 0 || p >= num_blocks) p = -1;  // absent block
         if (threadIdx.x == 0) tile_ok[buf] = p >= 0;
         if (p < 0) p = 0;
-        const uint8_t* base = kpool + p * TILE_BYTES;
+        const uint8_t* base = kpool + p * kl.bs;
         const uint32_t dst = lds_addr(&ktile[buf][0]);
         for (int k = wave; k < TILE_K; k += 8) {
             const int U = k * kWave + lane;
             const int row = U / UNITS, col = (U % UNITS) ^ (row % UNITS);
-            lds_gather16(base + row * T::ROW + col * 16, dst + k * kWave * 16);
+            lds_gather16(base + row * kl.rs + col * 16, dst + k * kWave * 16);
         }
         if constexpr (kScaleLine) {  // one dword per position: the fp32 scale or the four E8M0 bytes
             if (wave == 0)
-                lds_gather4(static_cast<const uint32_t*>(kscale) + p * kBlock + lane, lds_addr(&kst[buf][0]));
+                lds_gather4(static_cast<const uint8_t*>(kscale) + p * kl.sbs + lane * kl.srs,
+                            lds_addr(&kst[buf][0]));
         }
         issued += per_tile;
     };
@@ -478,7 +479,7 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
         dim3 grid((a.max_seq_len + 63) / 64, rows);
         size_t sh = sizeof(float) * (size_t)(a.H * a.D + a.H);
         hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(64), sh, st, (const float*)a.q, a.w,
-                           (const float*)a.kpool, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
+                           (const uint8_t*)a.kpool, a.kl, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
                            a.n_q, a.max_seq_len, a.H, a.D, a.scores, a.ld);
         return hipGetLastError();
     }
@@ -490,7 +491,7 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
     hipLaunchKernelGGL((indexer_decode_kernel<T, NQ, TPW, NW>),                                  \
                        dim3((tiles + NW * TPW - 1) / (NW * TPW), a.batch), dim3(64 * NW), 0, st, \
                        (const uint8_t*)a.q, a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale,   \
-                       a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len,   \
+                       a.kl, a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len, \
                        a.scores, a.ld)
         if (a.dtype == 2) {
             if (a.n_q == 1) DSA_DEC(IdxFp8, 1, 2, 8); else DSA_DEC(IdxFp8, 2, 4, 4);
@@ -506,7 +507,7 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
     dim3 grid((NB + 1) / 2, a.batch);
 #define DSA_PRE(T)                                                                                   \
     hipLaunchKernelGGL((indexer_prefill_kernel<T>), grid, dim3(512), 0, st, (const uint8_t*)a.q,    \
-                       a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale, a.seq_lens, a.table,      \
+                       a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale, a.kl, a.seq_lens, a.table, \
                        a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len, a.scores, a.ld)
     if (a.dtype == 2) DSA_PRE(IdxFp8);
     else if (a.dtype == 3) DSA_PRE(IdxMx);

@@ -11,6 +11,12 @@ constexpr int kTopkCacheMax = 16384;      // rows up to this length keep their k
 constexpr int kAttnMaxSplits = 32;        // split partials merged per row
 constexpr int kAttnMaxSplitSlots = 2048;  // index slots one attention workgroup compacts
 
+// A pool's layout in bytes: row (position o of block p) at p*bs + o*rs, its
+// scales at p*sbs + o*srs.
+struct PoolLayout {
+    int64_t bs, rs, sbs, srs;
+};
+
 struct IndexerLaunch {
     int dtype;                 // 0 f32, 1 bf16, 2 e4m3 + fp32 per 128, 3 MXFP8 (e4m3 + e8m0 per 32)
     const void* q;
@@ -18,6 +24,7 @@ struct IndexerLaunch {
     const float* w;
     const void* kpool;
     const void* kscale;        // fp32 [pool rows] (2) or e8m0 [pool rows][4] (3)
+    PoolLayout kl;             // index-K pool layout
     const int32_t* seq_lens;
     const int32_t* table;
     int max_blocks;
@@ -42,6 +49,7 @@ struct AttnLaunch {
     const void* q;
     const void* kv;
     const void* kvscale;       // e8m0 [pool rows][18] (2) or fp32 [pool rows][5] (3)
+    PoolLayout kvl;            // latent pool layout
     const int32_t* seq_lens;
     const int32_t* table;
     int max_blocks;
@@ -64,10 +72,12 @@ struct AppendLaunch {
     int max_blocks, batch, n_q, max_seq_len;
     int k_width, k_kind, k_group;     // kind: 0 fp32, 1 bf16, 2 e4m3 + fp32 scale, 3 e4m3 + E8M0 scale
     int64_t k_blocks;
+    PoolLayout k_l;
     void* k_pool;
     void* k_scales;
     int kv_width, kv_kind, kv_group;
     int64_t kv_blocks;
+    PoolLayout kv_l;
     void* kv_pool;
     void* kv_scales;
 };

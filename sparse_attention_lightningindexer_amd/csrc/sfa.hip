@@ -131,10 +131,12 @@ __device__ __forceinline__ void dequant_unit_rne(i32x4 codes, float scale, i32x4
 }
 
 // KV: 1 bf16, 2 MXFP8 (e4m3 + E8M0 per 32), 3 e4m3 + fp32 scale per 128.
-template <int KV>
+// DENSE: the pool has the dense layout, so a row's place is a constant
+// multiple of its number (no per-row stride arithmetic).
+template <int KV, bool DENSE>
 __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, const void* __restrict__ kvscale,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
+    PoolLayout kvl, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
     int64_t num_blocks, int n_q, int max_seq_len, int rows, const int32_t* __restrict__ indices,
     int top_k, int per_split, int splits, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, uint16_t* __restrict__ ws_o, float* __restrict__ ws_lse) {
@@ -251,6 +253,15 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     auto sid = [&](int c, int r) __attribute__((always_inline)) -> int {
         return __builtin_amdgcn_readlane(vid[r], c);
     };
+    // byte offsets of pool row pr (block pr/64, position pr%64) and of its scales
+    auto row_off = [&](int pr) __attribute__((always_inline)) -> int64_t {
+        if constexpr (DENSE) return (int64_t)pr * (MX ? kDqk : kRowB);
+        else return (int64_t)(pr >> 6) * kvl.bs + (int64_t)(pr & 63) * kvl.rs;
+    };
+    auto scale_off = [&](int pr) __attribute__((always_inline)) -> int64_t {
+        if constexpr (DENSE) return (int64_t)pr * (KV == 2 ? kDqk / 32 : 5 * 4);
+        else return (int64_t)(pr >> 6) * kvl.sbs + (int64_t)(pr & 63) * kvl.srs;
+    };
     const int rope_r = (lane & 31) >> 3;  // the row of the lane's rope unit
     auto load_chunk = [&](int c, Stage& st) __attribute__((always_inline)) {
         int rid[kStRows];
@@ -259,11 +270,11 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         if constexpr (!MX) {
 #pragma unroll
             for (int r = 0; r < kStRows; ++r)
-                st.v[r] = *reinterpret_cast<const i32x4*>(kv + (int64_t)rid[r] * kRowB + lane * 16);
+                st.v[r] = *reinterpret_cast<const i32x4*>(kv + row_off(rid[r]) + lane * 16);
             int id = rid[0];
 #pragma unroll
             for (int m = 1; m < kStRows; ++m) id = rope_r == m ? rid[m] : id;
-            st.v[kStRows] = *reinterpret_cast<const i32x4*>(kv + (int64_t)id * kRowB + 16 * (64 + (lane & 7)));
+            st.v[kStRows] = *reinterpret_cast<const i32x4*>(kv + row_off(id) + 16 * (64 + (lane & 7)));
         } else {
 #pragma unroll
             for (int i = 0; i < kMxPer; ++i) {
@@ -272,11 +283,12 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                 int id = rid[0];
 #pragma unroll
                 for (int m = 1; m < kStRows; ++m) id = r == m ? rid[m] : id;
-                st.v[i] = *reinterpret_cast<const i32x4*>(kv + (int64_t)id * kDqk + u * 16);
+                st.v[i] = *reinterpret_cast<const i32x4*>(kv + row_off(id) + u * 16);
+                const uint8_t* sp = static_cast<const uint8_t*>(kvscale) + scale_off(id);
                 if constexpr (KV == 2)  // E8M0 of the 32-code group u/2
-                    st.sc[i] = static_cast<const uint8_t*>(kvscale)[(int64_t)id * (kDqk / 32) + (u >> 1)];
+                    st.sc[i] = sp[u >> 1];
                 else  // fp32 of the 128-code group u/8 (five per row, the last one the rope)
-                    st.sc[i] = __float_as_uint(static_cast<const float*>(kvscale)[(int64_t)id * 5 + (u >> 3)]);
+                    st.sc[i] = __float_as_uint(reinterpret_cast<const float*>(sp)[u >> 3]);
             }
         }
     };
@@ -632,7 +644,7 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(const uint16_t* __rest
 // fp32 attention for small shapes: one wave per (head, row); logits of the
 // row's valid positions in LDS, two-pass softmax, lanes over value channels.
 __global__ __launch_bounds__(64) void sfa_f32_kernel(
-    const float* __restrict__ q, const float* __restrict__ kv, const int32_t* __restrict__ seq_lens,
+    const float* __restrict__ q, const uint8_t* __restrict__ kv, PoolLayout kvl, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ table, int max_blocks, int64_t num_blocks, int n_q, int max_seq_len,
     const int32_t* __restrict__ indices, int top_k, int H, int Dqk, int Dv, float sm_scale,
     float* __restrict__ out, float* __restrict__ lse) {
@@ -659,7 +671,7 @@ __global__ __launch_bounds__(64) void sfa_f32_kernel(
     const float* qh = q + ((int64_t)row * H + h) * Dqk;
     float mx = -INFINITY;
     for (int t = lane; t < n; t += 64) {
-        const float* k = kv + (int64_t)pr[t] * Dqk;
+        const float* k = reinterpret_cast<const float*>(kv + (int64_t)(pr[t] >> 6) * kvl.bs + (pr[t] & 63) * kvl.rs);
         float acc = 0.f;
         for (int c = 0; c < Dqk; ++c) acc = fmaf(qh[c], k[c], acc);
         z[t] = acc * sm_scale;
@@ -677,7 +689,9 @@ __global__ __launch_bounds__(64) void sfa_f32_kernel(
     float* oh = out + ((int64_t)row * H + h) * Dv;
     for (int d = lane; d < Dv; d += 64) {
         float acc = 0.f;
-        for (int t = 0; t < n; ++t) acc = fmaf(z[t], kv[(int64_t)pr[t] * Dqk + d], acc);
+        for (int t = 0; t < n; ++t)
+            acc = fmaf(z[t], reinterpret_cast<const float*>(kv + (int64_t)(pr[t] >> 6) * kvl.bs +
+                                                            (pr[t] & 63) * kvl.rs)[d], acc);
         oh[d] = acc * inv;
     }
     if (lse != nullptr && lane == 0) lse[(int64_t)row * H + h] = n > 0 ? mx + logf(sum) : -INFINITY;
@@ -708,7 +722,7 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st) {
     if (a.q_dtype == 0) {
         const size_t sh = (size_t)a.top_k * (sizeof(float) + sizeof(int));
         hipLaunchKernelGGL(sfa_f32_kernel, dim3(a.H, rows), dim3(64), sh, st, (const float*)a.q,
-                           (const float*)a.kv, a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q,
+                           (const uint8_t*)a.kv, a.kvl, a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q,
                            a.max_seq_len, a.indices, a.top_k, a.H, a.Dqk, a.Dv, a.sm_scale, (float*)a.out,
                            a.lse);
         return hipGetLastError();
@@ -719,21 +733,24 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st) {
     const float scale_log2 = a.sm_scale * kLog2e;
     uint16_t* ws_o = (uint16_t*)a.ws;
     float* ws_lse = splits == 1 ? nullptr : (float*)(ws_o + (size_t)rows * splits * kH * kDv);
-    if (a.kv_kind == 3)
-        hipLaunchKernelGGL((sfa_mla_kernel<3>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,
-                           (const uint8_t*)a.kv, a.kvscale, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
-                           a.n_q, a.max_seq_len, rows, a.indices, a.top_k, per, splits, scale_log2,
-                           (uint16_t*)a.out, a.lse, ws_o, ws_lse);
-    else if (a.kv_kind == 2)
-        hipLaunchKernelGGL((sfa_mla_kernel<2>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,
-                           (const uint8_t*)a.kv, a.kvscale, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
-                           a.n_q, a.max_seq_len, rows, a.indices, a.top_k, per, splits, scale_log2,
-                           (uint16_t*)a.out, a.lse, ws_o, ws_lse);
-    else
-        hipLaunchKernelGGL((sfa_mla_kernel<1>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,
-                           (const uint8_t*)a.kv, a.kvscale, a.seq_lens, a.table, a.max_blocks, a.num_blocks,
-                           a.n_q, a.max_seq_len, rows, a.indices, a.top_k, per, splits, scale_log2,
-                           (uint16_t*)a.out, a.lse, ws_o, ws_lse);
+    // the dense layout of each format, in bytes: rows, blocks, scale rows, scale blocks
+    const int64_t drow = a.kv_kind == 1 ? kRowB : kDqk;
+    const int64_t dsrow = a.kv_kind == 2 ? kDqk / 32 : a.kv_kind == 3 ? 5 * 4 : 0;
+    const bool dense = a.kvl.rs == drow && a.kvl.bs == 64 * drow &&
+                       (a.kv_kind == 1 || (a.kvl.srs == dsrow && a.kvl.sbs == 64 * dsrow));
+#define DSA_SFA(KV, D)                                                                                         \
+    hipLaunchKernelGGL((sfa_mla_kernel<KV, D>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,     \
+                       (const uint8_t*)a.kv, a.kvscale, a.kvl, a.seq_lens, a.table, a.max_blocks, a.num_blocks, \
+                       a.n_q, a.max_seq_len, rows, a.indices, a.top_k, per, splits, scale_log2,              \
+                       (uint16_t*)a.out, a.lse, ws_o, ws_lse)
+    if (a.kv_kind == 3) {
+        if (dense) DSA_SFA(3, true); else DSA_SFA(3, false);
+    } else if (a.kv_kind == 2) {
+        if (dense) DSA_SFA(2, true); else DSA_SFA(2, false);
+    } else {
+        if (dense) DSA_SFA(1, true); else DSA_SFA(1, false);
+    }
+#undef DSA_SFA
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     hipLaunchKernelGGL(sfa_combine_kernel, dim3(rows, kH / 4), dim3(256), 0, st, ws_o, ws_lse, splits, kH, kDv,

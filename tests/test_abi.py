@@ -96,6 +96,41 @@ def test_validation_errors_are_returned_before_any_launch():
     assert lib.dsa_sparse_attn(ref(batch), ref(kv_mx), 0x10000, 16, 0x10000, need, None) == B.DSA_ERR_NULL
 
 
+def test_pool_strides_are_validated_before_any_launch():
+    """Strides in elements, 0 meaning dense: negative strides, rows narrower than the
+    width, 16-byte misaligned BF16 rows or blocks, scale rows narrower than their
+    groups and misaligned E8M0 index-key scale rows are refused with DSA_ERR_SHAPE."""
+    lib = B.lib()
+    ref = C.byref
+    wl = make_workload(2, batch=2, lens=[100, 50])
+    batch, idx, attn = _fake_structs(wl)
+
+    def attn_status(**kv):
+        a2 = B.dsa_attn_args.from_buffer_copy(attn)
+        for k, v in kv.items():
+            setattr(a2.kv, k, v)
+        return lib.dsa_sparse_attn(ref(batch), ref(a2), 0x10000, 2048, None, 0, None)
+
+    for bad in (dict(row_stride=-1), dict(block_stride=-64), dict(row_stride=575), dict(row_stride=577),
+                dict(block_stride=64 * 576 + 4), dict(row_stride=1 << 41)):
+        assert attn_status(**bad) == B.DSA_ERR_SHAPE, bad
+    # a valid padded layout passes validation and reaches the workspace check
+    assert attn_status(row_stride=584, block_stride=64 * 584 + 128) == B.DSA_ERR_WORKSPACE
+    wl6 = make_workload(6, batch=2, lens=[100, 50])
+    batch6, idx6, _ = _fake_structs(wl6)
+
+    def idx_status(**kv):
+        i2 = B.dsa_indexer_args.from_buffer_copy(idx6)
+        i2.q_scale, i2.k.scales, i2.k.scale_kind, i2.k.group = 0x10000, 0x20000, B.DSA_SCALE_E8M0, 32
+        for k, v in kv.items():
+            setattr(i2.k, k, v)
+        return lib.dsa_indexer_scores(ref(batch6), ref(i2), None, 128, None)
+
+    assert idx_status(scale_row_stride=3) == B.DSA_ERR_SHAPE      # fewer than the 4 groups
+    assert idx_status(scale_row_stride=6) == B.DSA_ERR_SHAPE      # a row's 4 bytes not 4-byte aligned
+    assert idx_status(scale_row_stride=8, scale_block_stride=520) == B.DSA_ERR_NULL  # valid; scores NULL
+
+
 def test_noalloc_forward_refuses_batches_beyond_its_scratch_before_any_launch():
     """dsa_forward_noalloc checks the batch's workspace against its fixed per-GPU
     array on the host: a 4096-row prefill needs more and is refused without any

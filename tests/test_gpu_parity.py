@@ -550,3 +550,118 @@ def test_forward_replays_from_a_captured_graph():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(dev.out, ref[0]) and torch.equal(dev.lse, ref[1]) and torch.equal(idx, ref[2]), rep
+
+
+# ------------------------------------------------------------ strided pools
+
+def _strided(t, width, row_pad, block_pad, fill):
+    """Device copy of pool tensor t ([num_blocks, 64, width] or [num_blocks, 64]) in a
+    buffer whose rows are padded by row_pad elements and blocks by block_pad, the
+    padding filled with `fill`: (buffer, block stride, row stride) in elements."""
+    nb = t.shape[0]
+    rs = width + row_pad
+    bs = 64 * rs + block_pad
+    flat = t.reshape(nb, 64, width)
+    buf = torch.full((nb * bs,), 0, dtype=flat.dtype, device=flat.device)
+    buf.fill_(fill)
+    buf.as_strided((nb, 64, width), (bs, rs, 1)).copy_(flat)
+    return buf, bs, rs
+
+
+# pad sizes keep every row and block on the 16-byte grid the kernels read in
+_PADS = {"f32": (4, 16), "bf16": (8, 128), "e4m3": (16, 128), "mxfp8": (16, 128), "e4m3_128": (16, 128)}
+_FILL = {"f32": float("nan"), "bf16": 0x7FC0, "e4m3": 0x7F, "mxfp8": 0x7F, "e4m3_128": 0x7F}
+
+
+def _use_strided_pools(dev):
+    """Point dev's index-K and latent pools (and scales) at padded, NaN-filled copies
+    with explicit strides; returns the buffers (kept alive by the caller)."""
+    wl = dev.wl
+    keep = []
+
+    def fix(cache, data, scales, fmt, width):
+        rp, bp = _PADS[fmt]
+        buf, bs, rs = _strided(data, width, rp, bp, _FILL[fmt])
+        keep.append(buf)
+        cache.data, cache.block_stride, cache.row_stride = buf.data_ptr(), bs, rs
+        if scales is not None:
+            ng = 1 if scales.dim() == 2 else scales.shape[-1]
+            sbuf, sbs, srs = _strided(scales, ng, 4, 8, float("nan") if scales.dtype == torch.float32 else 0xFF)
+            keep.append(sbuf)
+            cache.scales, cache.scale_block_stride, cache.scale_row_stride = sbuf.data_ptr(), sbs, srs
+
+    fix(dev.idx.k, dev.k_pool, dev.k_scale, wl.idx_dtype, wl.d_I)
+    fix(dev.attn.kv, dev.kv_pool, dev.kv_scale, wl.kv_dtype, wl.d_qk)
+    return keep
+
+
+STRIDED = {
+    "tiny_fp32": (1, dict(poison=True)),
+    "decode_bf16": (2, dict(batch=3, lens=[300, 1000, 453], top_k=128, poison=True)),
+    "nq8_bf16_multirow_indexer": (2, dict(batch=2, n_q=8, lens=[1000, 77], top_k=256, poison=True)),
+    "fp8_decode": (5, dict(batch=3, lens=[500, 900, 130], top_k=256, poison=True)),
+    "fp8_pages_nq2": (6, dict(batch=2, n_q=2, lens=[700, 66], top_k=256, poison=True)),
+    "nq8_mxfp8_multirow_indexer": (6, dict(batch=2, n_q=8, lens=[1000, 77], top_k=256, poison=True)),
+}
+
+
+@pytest.mark.parametrize("case", list(STRIDED))
+def test_strided_pools_give_the_dense_results(case):
+    """Pools with padded rows and blocks (the padding NaN) and explicit strides, for the
+    data and the scales, give the same scores, indices, output and lse bytes as the
+    dense layout, through every kernel that reads a pool (decode and multi-row
+    indexers, every attention format)."""
+    cfg, kw = STRIDED[case]
+    wl = make_workload(cfg, **kw)
+    say(f"[parity] strided pools {case}")
+    _, sc, idx, out, lse = gpu_all(wl)
+    dev = B.DeviceInputs(wl)
+    keep = _use_strided_pools(dev)
+    _, sc2, idx2, out2, lse2 = gpu_all(wl, dev)
+    L = wl.row_lens()
+    for r in range(wl.rows):
+        assert np.array_equal(sc[r, :L[r]], sc2[r, :L[r]]), f"row {r}: scores differ"
+    assert np.array_equal(idx, idx2) and np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    del keep
+
+
+@pytest.mark.parametrize("case", list(APPEND))
+def test_cache_append_into_strided_pools(case):
+    """The append writes the same rows and scales into padded pools as into dense ones,
+    and leaves the padding untouched."""
+    cfg, kw = APPEND[case]
+    wl = make_workload(cfg, **kw)
+    say(f"[parity] append into strided pools {case}")
+    rng = np.random.default_rng(13)
+    f32 = wl.idx_dtype == "f32"
+    k_new = (rng.standard_normal((wl.rows, wl.d_I)) / np.sqrt(wl.d_I)).astype(np.float32)
+    kv_new = (rng.standard_normal((wl.rows, wl.d_qk)) / np.sqrt(wl.d_qk)).astype(np.float32)
+    dt = torch.float32 if f32 else torch.bfloat16
+    kt, kvt = torch.from_numpy(k_new).to(dt).cuda(), torch.from_numpy(kv_new).to(dt).cuda()
+    dense = B.DeviceInputs(wl)
+    B.dsa_cache_append(dense, kt, kvt)
+    dev = B.DeviceInputs(wl)
+    keep = _use_strided_pools(dev)
+    B.dsa_cache_append(dev, kt, kvt)
+    torch.cuda.synchronize()
+    # the strided buffers, viewed back as dense pools, equal the dense append
+    i = 0
+    for cache, ref, scales in ((dev.idx.k, dense.k_pool, dense.k_scale), (dev.attn.kv, dense.kv_pool, dense.kv_scale)):
+        for t, bs, rs in ((ref, cache.block_stride, cache.row_stride),
+                          (scales, cache.scale_block_stride, cache.scale_row_stride)):
+            if t is None:
+                continue
+            nb, width = t.shape[0], (1 if t.dim() == 2 else t.shape[-1])
+            buf = keep[i]
+            i += 1
+            view = buf.as_strided((nb, 64, width), (bs, rs, 1))
+            assert torch.equal(view.reshape(t.shape).view(torch.uint8) if t.dtype != torch.float32 else
+                               view.reshape(t.shape).view(torch.int32),
+                               t.view(torch.uint8) if t.dtype != torch.float32 else t.view(torch.int32)), case
+            mask = torch.ones(buf.numel(), dtype=torch.bool, device=buf.device)
+            mask.view(-1).as_strided((nb, 64, width), (bs, rs, 1)).fill_(False)
+            pad = buf[mask]
+            if pad.dtype == torch.float32:
+                assert bool(torch.isnan(pad).all()), f"{case}: padding written"
+            else:
+                assert bool((pad == pad.flatten()[0]).all()), f"{case}: padding written"
