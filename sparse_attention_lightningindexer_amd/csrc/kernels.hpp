@@ -102,6 +102,8 @@ struct PrologLaunch {
 // device, looked up once per device.
 constexpr size_t kScratchBytes = size_t(32) << 20;
 hipError_t scratch_for_current_device(void** ptr);
+// Compute units of the current device (asked of the runtime once per device).
+hipError_t compute_units(int* cus);
 
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st);
 hipError_t launch_indexer_prolog(const PrologLaunch& a, hipStream_t st);

@@ -1,6 +1,7 @@
-// scratch.hip -- the library's own device workspace for callers that cannot
-// allocate (HIP graph capture, tight serving loops, harnesses that forbid
-// hipMalloc): one file-scope device array per GPU, of a fixed maximum size.
+// scratch.hip -- per-device state of the library: its own device workspace
+// for callers that cannot allocate (HIP graph capture, tight serving loops,
+// harnesses that forbid hipMalloc), one file-scope device array per GPU of a
+// fixed maximum size; and each device's compute-unit count, asked once.
 //
 // In host code the array's name stands for a host-side shadow, not a device
 // address, so the array is only ever reached through the device pointer that
@@ -10,6 +11,7 @@
 // finds there what the last call left: calls that overlap on one GPU race.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "kernels.hpp"
@@ -38,6 +40,23 @@ hipError_t scratch_for_current_device(void** ptr) {
         g_scratch_ptr[dev] = p;
     }
     *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t compute_units(int* cus) {
+    static std::atomic<int> g_cus[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (n <= 0) return hipErrorInvalidDevice;
+        g_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    *cus = n;
     return hipSuccess;
 }
 

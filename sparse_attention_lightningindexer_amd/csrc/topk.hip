@@ -7,10 +7,12 @@
 // is ascending, padded with -1.
 //
 // Method: scores map to order-preserving 32-bit keys (-0.0 folded into
-// +0.0); an MSB-first radix select with LDS histograms finds the k-th
-// largest key T and how many keys equal to T are needed; every key > T and
-// the first needed keys == T are kept, in position order.  One workgroup per
-// row; rows are visited longest-first when the grid is larger than the GPU.
+// +0.0; key 0 marks an empty slot, see score_key); an MSB-first radix select
+// with LDS histograms finds the k-th largest key T and how many keys equal to
+// T are needed; every key > T and the first needed keys == T are kept, in
+// position order.  One workgroup per
+// row at a time, the rows taken from the last (in a causal prefill, the
+// longest) down.
 // Three forms:
 //   * rows up to 32768 positions: the keys stay in registers (8, 16 or 32
 //     per thread of a 1024-thread workgroup), three digit passes;
@@ -24,10 +26,16 @@
 
 namespace dsa {
 
+// Order-preserving key of a score, never 0: the one float that would map to 0
+// (the NaN with every bit set; NaN has no specified order) shares key 1 with
+// its neighbour, so 0 is free to mark an empty slot.  An empty slot's key is
+// below every score's, so as long as a row has top_k real keys, empty slots
+// never reach the k-th largest key and can sit in the histograms unnoticed.
 __device__ __forceinline__ uint32_t score_key(float f) {
     uint32_t u = __float_as_uint(f);
     if ((u << 1) == 0u) u = 0u;  // -0.0 == +0.0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return k > 1u ? k : 1u;
 }
 
 template <int NT, bool CACHE>
@@ -133,14 +141,15 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 
 // Register-resident selection by one 1024-thread workgroup over up to
 // 1024 * KPT slots: thread t holds the keys of slots KPT*t .. KPT*t + KPT - 1
-// (bit q of `valid` says whether slot KPT*t + q takes part), so the keys are
-// read from memory once.  The MSB-first radix select uses digits of 12, 10 and
+// (key 0 for an empty slot), so the keys are read from memory once.  The MSB-first radix select uses digits of 12, 10 and
 // 10 bits (one LDS histogram per pass, bins owned by threads for the suffix
 // scan); the k-th largest key T and the number of ties to keep follow, and one
 // block scan of the per-thread counts gives every kept slot its output place,
 // lowest slot first among equal keys.  emit(place, q) writes kept slot
 // KPT*t + q.  Exactly `top_k` slots are kept (callers guarantee that at least
-// top_k are valid).
+// top_k slots are not empty).  Empty slots are left out of the first
+// histogram only to spare one bin the atomic traffic; the later passes and
+// the final comparisons need no test, since key 0 lies below the cut.
 constexpr int kSelThreads = 1024;
 struct SelectShared {
     uint32_t hist[4096];
@@ -148,11 +157,15 @@ struct SelectShared {
     uint32_t cut_digit, cut_above;
 };
 
+// emit(place, q) takes a run-time q: a thread walks its kept slots as the set
+// bits of a mask, as many steps as it keeps.
 template <int KPT, class Emit>
-__device__ __forceinline__ void block_select(SelectShared& sh, const uint32_t (&key)[KPT], uint32_t valid,
-                                             int top_k, Emit&& emit) {
+__device__ __forceinline__ void block_select(SelectShared& sh, const uint32_t (&key)[KPT], int top_k,
+                                             Emit&& emit) {
     constexpr int NT = kSelThreads, NW = NT / kWave;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform across the wave; saying so keeps the per-wave
+    // comparisons below scalar instead of 64-bit lane masks held in registers
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     auto wsum_where = [&](auto pick) -> uint32_t {  // sum of the per-wave totals of the waves w with pick(w)
         uint32_t t = 0u;
 #pragma unroll
@@ -167,11 +180,11 @@ __device__ __forceinline__ void block_select(SelectShared& sh, const uint32_t (&
     __syncthreads();
 
     uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)top_k;
-    auto pass = [&](int shift, int bits) {
+    auto pass = [&](int shift, int bits, bool first) {
         const uint32_t nb = 1u << bits, dm = nb - 1u;
 #pragma unroll
         for (int q = 0; q < KPT; ++q)
-            if (((valid >> q) & 1u) && (key[q] & mask) == prefix) atomicAdd(&sh.hist[(key[q] >> shift) & dm], 1u);
+            if (first ? key[q] != 0u : (key[q] & mask) == prefix) atomicAdd(&sh.hist[(key[q] >> shift) & dm], 1u);
         __syncthreads();
         // thread t owns bins [per*t, per*t + per); its counts are read, cleared
         // for the next pass, and scanned from the top digit down.
@@ -205,19 +218,21 @@ __device__ __forceinline__ void block_select(SelectShared& sh, const uint32_t (&
         mask |= dm << shift;
         krem -= sh.cut_above;
     };
-    pass(20, 12);
-    pass(10, 10);
-    pass(0, 10);
+    pass(20, 12, true);
+    pass(10, 10, false);
+    pass(0, 10, false);
 
     // prefix is the k-th largest key; krem keys equal to it are taken, lowest first.
     const uint32_t T = prefix;
-    uint32_t gt = 0u, eq = 0u;
+    // this thread's slots above and at T, as bit masks (each comparison is
+    // made once: held as lane masks, they would not fit the scalar registers)
+    uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
-        const bool v = (valid >> q) & 1u;
-        gt += (v && key[q] > T) ? 1u : 0u;
-        eq += (v && key[q] == T) ? 1u : 0u;
+        gtm |= key[q] > T ? (1u << q) : 0u;
+        eqm |= key[q] == T ? (1u << q) : 0u;
     }
+    const uint32_t gt = (uint32_t)__builtin_popcount(gtm), eq = (uint32_t)__builtin_popcount(eqm);
     const uint32_t packed = (gt << 16) | eq;  // both totals stay below 2^16
     const uint32_t incl = wave_scan_incl(packed);
     if (lane == kWave - 1) sh.wsum[wave] = incl;
@@ -225,20 +240,22 @@ __device__ __forceinline__ void block_select(SelectShared& sh, const uint32_t (&
     const uint32_t excl = (incl - packed) + wsum_where([&](int w) { return w < wave; });
     const uint32_t gt_before = excl >> 16, eq_before = excl & 0xffffu;
     int place = (int)(gt_before + min(eq_before, krem));
-    uint32_t eq_seen = eq_before;
-#pragma unroll
-    for (int q = 0; q < KPT; ++q) {
-        if ((valid >> q) & 1u) {
-            const bool is_eq = key[q] == T;
-            const bool sel = key[q] > T || (is_eq && eq_seen < krem);
-            eq_seen += is_eq ? 1u : 0u;
-            if (sel) emit(place++, q);
-        }
+    // the lowest krem - eq_before of this thread's keys equal to T are kept
+    uint32_t take = eq_before < krem ? krem - eq_before : 0u;
+    uint32_t sel = gtm;
+    while (take > 0u && eqm != 0u) {
+        sel |= eqm & (0u - eqm);
+        eqm &= eqm - 1u;
+        --take;
+    }
+    while (sel != 0u) {  // ascending slot order
+        emit(place++, __builtin_ctz(sel));
+        sel &= sel - 1u;
     }
 }
 
-// Keys of `n` consecutive scores starting at row[base] (n <= KPT), vector
-// loads when the whole run is present and aligned.
+// Keys of `n` consecutive scores starting at row[base] (n <= KPT; the slots
+// from n on are empty), vector loads when the whole run is present and aligned.
 template <int KPT>
 __device__ __forceinline__ void load_keys(const float* row, int base, int n, bool vec, uint32_t (&key)[KPT]) {
     if (vec && n == KPT) {
@@ -256,29 +273,30 @@ __device__ __forceinline__ void load_keys(const float* row, int base, int n, boo
     }
 }
 
-__device__ __forceinline__ uint32_t prefix_mask(int n) { return n >= 32 ? 0xffffffffu : ((1u << max(n, 0)) - 1u); }
-
-// Rows up to 1024 * KPT positions, one workgroup per row (rows longest first).
+// Rows up to 1024 * KPT positions.  Workgroups are persistent: workgroup b
+// takes rows b, b + G, b + 2G, ... counted from the last (longest) row.
 template <int KPT>
 __global__ __launch_bounds__(kSelThreads) void topk_reg_kernel(const float* __restrict__ scores, int64_t ld,
                                                                const int32_t* __restrict__ seq_lens, int n_q,
                                                                int max_seq_len, int rows, int top_k, bool vec,
                                                                int32_t* __restrict__ indices) {
     __shared__ SelectShared sh;
-    const int r = rows - 1 - (int)blockIdx.x;
-    const int b = r / n_q, i0 = r % n_q;
-    const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, i0);
     const int tid = threadIdx.x;
-    int32_t* out = indices + (int64_t)r * top_k;
-    if (L <= top_k) {  // keep the whole history
-        for (int t = tid; t < top_k; t += kSelThreads) out[t] = t < L ? t : -1;
-        return;
-    }
     const int base = KPT * tid;
-    const int nv = min(max(L - base, 0), KPT);  // valid keys of this thread (a prefix)
-    uint32_t key[KPT];
-    load_keys<KPT>(scores + (int64_t)r * ld, base, nv, vec, key);
-    block_select<KPT>(sh, key, prefix_mask(nv), top_k, [&](int place, int q) { out[place] = base + q; });
+    for (int i = (int)blockIdx.x; i < rows; i += (int)gridDim.x) {
+        const int r = rows - 1 - i;
+        const int L = history_len(clamp_len(seq_lens, r / n_q, max_seq_len), n_q, r % n_q);
+        int32_t* out = indices + (int64_t)r * top_k;
+        if (L <= top_k) {  // keep the whole history
+            for (int t = tid; t < top_k; t += kSelThreads) out[t] = t < L ? t : -1;
+            continue;  // workgroup-uniform; no shared memory was touched
+        }
+        const int nv = min(max(L - base, 0), KPT);  // valid keys of this thread (a prefix)
+        uint32_t key[KPT];
+        load_keys<KPT>(scores + (int64_t)r * ld, base, nv, vec, key);
+        block_select<KPT>(sh, key, top_k, [&](int place, int q) { out[place] = base + q; });
+        __syncthreads();  // the shared histogram and scan words are reused by the next row
+    }
 }
 
 // Rows longer than the register-resident kernel takes: stage 1 keeps the top_k
@@ -310,7 +328,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_segment_kernel(const float* 
     const int nv = min(max(Ls - base, 0), 16);
     uint32_t key[16];
     load_keys<16>(scores + (int64_t)r * ld + s0, base, nv, vec, key);
-    block_select<16>(sh, key, prefix_mask(nv), top_k, [&](int place, int q) { out[place] = s0 + base + q; });
+    block_select<16>(sh, key, top_k, [&](int place, int q) { out[place] = s0 + base + q; });
 }
 
 template <int KPT>
@@ -334,15 +352,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(const float* __
     const float* row = scores + (int64_t)r * ld;
     const int base = KPT * tid;
     int pos[KPT];
-    uint32_t key[KPT], valid = 0u;
+    uint32_t key[KPT];
 #pragma unroll
     for (int q = 0; q < KPT; ++q) pos[q] = base + q < n ? cr[base + q] : -1;
 #pragma unroll
-    for (int q = 0; q < KPT; ++q) {
-        key[q] = score_key(row[pos[q] < 0 ? 0 : pos[q]]);
-        valid |= (pos[q] >= 0 ? 1u : 0u) << q;
-    }
-    block_select<KPT>(sh, key, valid, top_k, [&](int place, int q) { out[place] = pos[q]; });
+    for (int q = 0; q < KPT; ++q) key[q] = pos[q] < 0 ? 0u : score_key(row[pos[q]]);
+    // a kept slot's position is read again from the candidate list (a cached
+    // line) rather than held in registers through the selection
+    block_select<KPT>(sh, key, top_k, [&](int place, int q) { out[place] = cr[base + q]; });
 }
 
 int topk_segments(int max_seq_len) { return (max_seq_len + kSegLen - 1) / kSegLen; }
@@ -358,9 +375,15 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
     const int rows = a.batch * a.n_q;
     if (rows == 0) return hipSuccess;
     const bool vec = (a.ld % 4) == 0 && ((uintptr_t)a.scores % 16) == 0;
-#define DSA_REG(K)                                                                                        \
-    hipLaunchKernelGGL((topk_reg_kernel<K>), dim3(rows), dim3(kSelThreads), 0, st, a.scores, a.ld, a.seq_lens, \
-                       a.n_q, a.max_seq_len, rows, a.top_k, vec, a.indices)
+    // persistent workgroups for the register-resident kernel: at most two per
+    // compute unit
+    int cus = 0;
+    hipError_t e0 = compute_units(&cus);
+    if (e0 != hipSuccess) return e0;
+    const int reg_grid = rows < 2 * cus ? rows : 2 * cus;
+#define DSA_REG(K)                                                                                           \
+    hipLaunchKernelGGL((topk_reg_kernel<K>), dim3(reg_grid), dim3(kSelThreads), 0, st, a.scores, a.ld,      \
+                       a.seq_lens, a.n_q, a.max_seq_len, rows, a.top_k, vec, a.indices)
     if (a.max_seq_len <= 8 * 1024) DSA_REG(8);
     else if (a.max_seq_len <= 16 * 1024) DSA_REG(16);
     else if (a.max_seq_len <= 32 * 1024) DSA_REG(32);
