@@ -140,29 +140,43 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 }
 
 // Register-resident selection by one 1024-thread workgroup over up to
-// 1024 * KPT slots: thread t holds the keys of slots KPT*t .. KPT*t + KPT - 1
-// (key 0 for an empty slot), so the keys are read from memory once.  The MSB-first radix select uses digits of 12, 10 and
+// 1024 * KPT slots.  Slots are wave-strided: lane l of wave w holds in key[q]
+// slot 64 * (KPT * w + q) + l, so a column q of a wave is 64 consecutive
+// slots -- one coalesced load, and one ballot is the column's bit mask.  Key 0
+// marks an empty slot.  The MSB-first radix select uses digits of 12, 10 and
 // 10 bits (one LDS histogram per pass, bins owned by threads for the suffix
-// scan); the k-th largest key T and the number of ties to keep follow, and one
-// block scan of the per-thread counts gives every kept slot its output place,
-// lowest slot first among equal keys.  emit(place, q) writes kept slot
-// KPT*t + q.  Exactly `top_k` slots are kept (callers guarantee that at least
-// top_k slots are not empty).  Empty slots are left out of the first
-// histogram only to spare one bin the atomic traffic; the later passes and
-// the final comparisons need no test, since key 0 lies below the cut.
+// scan) and finds the k-th largest key T and the number of keys equal to T to
+// keep.  The histogram is all zero on entry (clear_hist, once per workgroup)
+// and is left so.  The column masks of the keys > T and == T go to LDS as 64-bit words
+// in slot order; thread t then takes slots KPT*t .. KPT*t + KPT - 1, and one
+// block scan of its counts gives every kept slot its output place, the lowest
+// slots first among equal keys.  emit(place, slot) writes a kept slot.  Exactly top_k slots
+// are kept (callers guarantee that at least top_k slots are not empty).  Empty
+// slots are left out of the first histogram only to spare one bin the atomic
+// traffic; the later passes and the final comparisons need no test, since
+// key 0 lies below the cut.
 constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+template <int KPT>
 struct SelectShared {
     uint32_t hist[4096];
-    uint32_t wsum[kSelThreads / 64] __attribute__((aligned(16)));
+    uint32_t wsum[kSelWaves] __attribute__((aligned(16)));
     uint32_t cut_digit, cut_above;
+    uint64_t gt_mask[kSelWaves * KPT];  // column q of wave w is word KPT * w + q
+    uint64_t eq_mask[kSelWaves * KPT];
 };
 
-// emit(place, q) takes a run-time q: a thread walks its kept slots as the set
-// bits of a mask, as many steps as it keeps.
+template <int KPT>
+__device__ __forceinline__ void clear_hist(SelectShared<KPT>& sh) {
+    for (int t = threadIdx.x; t < 4096; t += kSelThreads) sh.hist[t] = 0u;
+    __syncthreads();
+}
+
 template <int KPT, class Emit>
-__device__ __forceinline__ void block_select(SelectShared& sh, const uint32_t (&key)[KPT], int top_k,
+__device__ __forceinline__ void block_select(SelectShared<KPT>& sh, const uint32_t (&key)[KPT], int top_k,
                                              Emit&& emit) {
-    constexpr int NT = kSelThreads, NW = NT / kWave;
+    static_assert(KPT == 8 || KPT == 16 || KPT == 32, "a thread's KPT slots lie in one 64-bit column word");
+    constexpr int NT = kSelThreads, NW = kSelWaves;
     // the wave index is uniform across the wave; saying so keeps the per-wave
     // comparisons below scalar instead of 64-bit lane masks held in registers
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -176,10 +190,7 @@ __device__ __forceinline__ void block_select(SelectShared& sh, const uint32_t (&
         }
         return t;
     };
-    for (int t = tid; t < 4096; t += NT) sh.hist[t] = 0u;
-    __syncthreads();
-
-    uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)top_k;
+    uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)top_k;  // uniform
     auto pass = [&](int shift, int bits, bool first) {
         const uint32_t nb = 1u << bits, dm = nb - 1u;
 #pragma unroll
@@ -214,26 +225,33 @@ __device__ __forceinline__ void block_select(SelectShared& sh, const uint32_t (&
             }
         }
         __syncthreads();
-        prefix |= sh.cut_digit << shift;
+        prefix |= __builtin_amdgcn_readfirstlane(sh.cut_digit) << shift;
         mask |= dm << shift;
-        krem -= sh.cut_above;
+        krem -= __builtin_amdgcn_readfirstlane(sh.cut_above);
     };
     pass(20, 12, true);
     pass(10, 10, false);
     pass(0, 10, false);
 
-    // prefix is the k-th largest key; krem keys equal to it are taken, lowest first.
+    // prefix is the k-th largest key T; krem keys equal to it are taken, lowest first.
     const uint32_t T = prefix;
-    // this thread's slots above and at T, as bit masks (each comparison is
-    // made once: held as lane masks, they would not fit the scalar registers)
-    uint32_t gtm = 0u, eqm = 0u;
+    // the column masks of the keys > T and == T, written by the wave's lane 0
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
-        gtm |= key[q] > T ? (1u << q) : 0u;
-        eqm |= key[q] == T ? (1u << q) : 0u;
+        const uint64_t mg = ballot(key[q] > T), me = ballot(key[q] == T);
+        if (lane == 0) {
+            sh.gt_mask[KPT * wave + q] = mg;
+            sh.eq_mask[KPT * wave + q] = me;
+        }
     }
-    const uint32_t gt = (uint32_t)__builtin_popcount(gtm), eq = (uint32_t)__builtin_popcount(eqm);
-    const uint32_t packed = (gt << 16) | eq;  // both totals stay below 2^16
+    __syncthreads();
+    // thread t: slots KPT*t .. KPT*t + KPT - 1, bits (KPT*t) % 64 .. of word (KPT*t) / 64
+    constexpr uint32_t kBits = KPT == 32 ? 0xffffffffu : (1u << KPT) - 1u;
+    const int bit0 = (KPT * tid) & 63;
+    uint32_t gt32 = (uint32_t)(sh.gt_mask[(KPT * tid) >> 6] >> bit0) & kBits;
+    uint32_t eq32 = (uint32_t)(sh.eq_mask[(KPT * tid) >> 6] >> bit0) & kBits;
+    // both totals stay below 2^16 (at most 32768 slots)
+    const uint32_t packed = ((uint32_t)__builtin_popcount(gt32) << 16) | (uint32_t)__builtin_popcount(eq32);
     const uint32_t incl = wave_scan_incl(packed);
     if (lane == kWave - 1) sh.wsum[wave] = incl;
     __syncthreads();
@@ -242,34 +260,36 @@ __device__ __forceinline__ void block_select(SelectShared& sh, const uint32_t (&
     int place = (int)(gt_before + min(eq_before, krem));
     // the lowest krem - eq_before of this thread's keys equal to T are kept
     uint32_t take = eq_before < krem ? krem - eq_before : 0u;
-    uint32_t sel = gtm;
-    while (take > 0u && eqm != 0u) {
-        sel |= eqm & (0u - eqm);
-        eqm &= eqm - 1u;
+    uint32_t sel = gt32;
+    while (take > 0u && eq32 != 0u) {
+        sel |= eq32 & (0u - eq32);
+        eq32 &= eq32 - 1u;
         --take;
     }
     while (sel != 0u) {  // ascending slot order
-        emit(place++, __builtin_ctz(sel));
+        emit(place++, KPT * tid + __builtin_ctz(sel));
         sel &= sel - 1u;
     }
 }
 
-// Keys of `n` consecutive scores starting at row[base] (n <= KPT; the slots
-// from n on are empty), vector loads when the whole run is present and aligned.
+// Keys of the wave's slots wb + 64q + lane (q < KPT) of a run of n scores
+// (slots from n on are empty).  Loads are unconditional (a slot past the run
+// reads the last score) so that each column is one coalesced load and all of
+// them are in flight at once.
 template <int KPT>
-__device__ __forceinline__ void load_keys(const float* row, int base, int n, bool vec, uint32_t (&key)[KPT]) {
-    if (vec && n == KPT) {
+__device__ __forceinline__ void load_keys(const float* row, int wb, int n, int lane, uint32_t (&key)[KPT]) {
+    if (wb + kWave * KPT <= n) {  // wave-uniform
 #pragma unroll
-        for (int q = 0; q < KPT / 4; ++q) {
-            const float4 v = *reinterpret_cast<const float4*>(row + base + 4 * q);
-            key[4 * q] = score_key(v.x);
-            key[4 * q + 1] = score_key(v.y);
-            key[4 * q + 2] = score_key(v.z);
-            key[4 * q + 3] = score_key(v.w);
-        }
+        for (int q = 0; q < KPT; ++q) key[q] = score_key(row[wb + kWave * q + lane]);
+    } else if (wb < n) {
+        float v[KPT];
+#pragma unroll
+        for (int q = 0; q < KPT; ++q) v[q] = row[min(wb + kWave * q + lane, n - 1)];
+#pragma unroll
+        for (int q = 0; q < KPT; ++q) key[q] = wb + kWave * q + lane < n ? score_key(v[q]) : 0u;
     } else {
 #pragma unroll
-        for (int q = 0; q < KPT; ++q) key[q] = q < n ? score_key(row[base + q]) : 0u;
+        for (int q = 0; q < KPT; ++q) key[q] = 0u;
     }
 }
 
@@ -278,11 +298,12 @@ __device__ __forceinline__ void load_keys(const float* row, int base, int n, boo
 template <int KPT>
 __global__ __launch_bounds__(kSelThreads) void topk_reg_kernel(const float* __restrict__ scores, int64_t ld,
                                                                const int32_t* __restrict__ seq_lens, int n_q,
-                                                               int max_seq_len, int rows, int top_k, bool vec,
+                                                               int max_seq_len, int rows, int top_k,
                                                                int32_t* __restrict__ indices) {
-    __shared__ SelectShared sh;
-    const int tid = threadIdx.x;
-    const int base = KPT * tid;
+    __shared__ SelectShared<KPT> sh;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wb = KPT * kWave * __builtin_amdgcn_readfirstlane(tid >> 6);  // the wave's first slot
+    clear_hist(sh);
     for (int i = (int)blockIdx.x; i < rows; i += (int)gridDim.x) {
         const int r = rows - 1 - i;
         const int L = history_len(clamp_len(seq_lens, r / n_q, max_seq_len), n_q, r % n_q);
@@ -291,57 +312,72 @@ __global__ __launch_bounds__(kSelThreads) void topk_reg_kernel(const float* __re
             for (int t = tid; t < top_k; t += kSelThreads) out[t] = t < L ? t : -1;
             continue;  // workgroup-uniform; no shared memory was touched
         }
-        const int nv = min(max(L - base, 0), KPT);  // valid keys of this thread (a prefix)
         uint32_t key[KPT];
-        load_keys<KPT>(scores + (int64_t)r * ld, base, nv, vec, key);
-        block_select<KPT>(sh, key, top_k, [&](int place, int q) { out[place] = base + q; });
-        __syncthreads();  // the shared histogram and scan words are reused by the next row
+        load_keys<KPT>(scores + (int64_t)r * ld, wb, L, lane, key);
+        block_select<KPT>(sh, key, top_k, [&](int place, int slot) { out[place] = slot; });
+        __syncthreads();  // the scan words and column masks are reused by the next row
     }
 }
 
 // Rows longer than the register-resident kernel takes: stage 1 keeps the top_k
 // of every 16384-position segment (all of a shorter segment) as ascending
-// positions in cand[row][segment][top_k] (-1 padded); the row's top_k is
-// contained in the union.  Stage 2 selects from those candidates, which are
-// in ascending position order, so the lowest-position rule for equal scores
-// carries over.  grid (segments, rows) and (rows).
-constexpr int kSegLen = kSelThreads * 16;
+// positions in cand[row][segment][top_k] (-1 padded), with their keys in
+// ckey[row][segment][top_k] (0 for padding); the row's top_k is contained in
+// the union.  Stage 2 selects from those candidates, which are in ascending
+// position order, so the lowest-position rule for equal scores carries over.
+// grid (segments, rows) and (rows).  The workspace holds cand, then ckey.
+constexpr int kSegKpt = 16;
+constexpr int kSegLen = kSelThreads * kSegKpt;
 
 __global__ __launch_bounds__(kSelThreads) void topk_segment_kernel(const float* __restrict__ scores, int64_t ld,
                                                                    const int32_t* __restrict__ seq_lens, int n_q,
-                                                                   int max_seq_len, int rows, int top_k, bool vec,
-                                                                   int nseg, int32_t* __restrict__ cand) {
-    __shared__ SelectShared sh;
+                                                                   int max_seq_len, int rows, int top_k, int nseg,
+                                                                   int32_t* __restrict__ cand,
+                                                                   uint32_t* __restrict__ ckey) {
+    __shared__ SelectShared<kSegKpt> sh;
+    __shared__ uint32_t skey[kSegLen];  // the segment's keys by slot, for the emit
     const int seg = blockIdx.x, r = rows - 1 - (int)blockIdx.y;
     const int b = r / n_q, i0 = r % n_q;
     const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, i0);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     if (L <= top_k) return;  // stage 2 writes such rows itself
-    int32_t* out = cand + ((int64_t)r * nseg + seg) * top_k;
+    const int64_t o = ((int64_t)r * nseg + seg) * top_k;
+    int32_t* outp = cand + o;
+    uint32_t* outk = ckey + o;
     const int s0 = seg * kSegLen;
     const int Ls = min(max(L - s0, 0), kSegLen);  // positions of this segment in the history
+    const float* row = scores + (int64_t)r * ld + s0;
     if (Ls <= top_k) {
-        for (int t = tid; t < top_k; t += kSelThreads) out[t] = t < Ls ? s0 + t : -1;
+        for (int t = tid; t < top_k; t += kSelThreads) {
+            outp[t] = t < Ls ? s0 + t : -1;
+            outk[t] = t < Ls ? score_key(row[t]) : 0u;
+        }
         return;
     }
-    const int base = 16 * tid;
-    const int nv = min(max(Ls - base, 0), 16);
-    uint32_t key[16];
-    load_keys<16>(scores + (int64_t)r * ld + s0, base, nv, vec, key);
-    block_select<16>(sh, key, top_k, [&](int place, int q) { out[place] = s0 + base + q; });
+    const int wb = kSegKpt * kWave * __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t key[kSegKpt];
+    load_keys<kSegKpt>(row, wb, Ls, lane, key);
+#pragma unroll
+    for (int q = 0; q < kSegKpt; ++q) skey[wb + kWave * q + lane] = key[q];
+    clear_hist(sh);
+    block_select<kSegKpt>(sh, key, top_k, [&](int place, int slot) {
+        outp[place] = s0 + slot;
+        outk[place] = skey[slot];
+    });
 }
 
 template <int KPT>
-__global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(const float* __restrict__ scores, int64_t ld,
-                                                                 const int32_t* __restrict__ seq_lens, int n_q,
+__global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(const int32_t* __restrict__ seq_lens, int n_q,
                                                                  int max_seq_len, int rows, int top_k, int nseg,
                                                                  const int32_t* __restrict__ cand,
+                                                                 const uint32_t* __restrict__ ckey,
                                                                  int32_t* __restrict__ indices) {
-    __shared__ SelectShared sh;
+    __shared__ SelectShared<KPT> sh;
+    __shared__ int32_t spos[KPT * kSelThreads];  // candidate positions by slot, for the emit
     const int r = rows - 1 - (int)blockIdx.x;
     const int b = r / n_q, i0 = r % n_q;
     const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, i0);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     int32_t* out = indices + (int64_t)r * top_k;
     if (L <= top_k) {
         for (int t = tid; t < top_k; t += kSelThreads) out[t] = t < L ? t : -1;
@@ -349,17 +385,27 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(const float* __
     }
     const int n = nseg * top_k;  // candidate slots of the row
     const int32_t* cr = cand + (int64_t)r * n;
-    const float* row = scores + (int64_t)r * ld;
-    const int base = KPT * tid;
-    int pos[KPT];
+    const uint32_t* ck = ckey + (int64_t)r * n;
+    const int wb = KPT * kWave * __builtin_amdgcn_readfirstlane(tid >> 6);
+    // unconditional loads (clamped to the last slot): one batch in flight
+    int32_t pos[KPT];
     uint32_t key[KPT];
 #pragma unroll
-    for (int q = 0; q < KPT; ++q) pos[q] = base + q < n ? cr[base + q] : -1;
+    for (int q = 0; q < KPT; ++q) {
+        const int sl = min(wb + kWave * q + lane, n - 1);
+        pos[q] = cr[sl];
+        key[q] = ck[sl];
+    }
+    // slots past the list (n <= KPT * 1024) and -1 padding are empty; an empty
+    // slot's position is never read
 #pragma unroll
-    for (int q = 0; q < KPT; ++q) key[q] = pos[q] < 0 ? 0u : score_key(row[pos[q]]);
-    // a kept slot's position is read again from the candidate list (a cached
-    // line) rather than held in registers through the selection
-    block_select<KPT>(sh, key, top_k, [&](int place, int q) { out[place] = cr[base + q]; });
+    for (int q = 0; q < KPT; ++q) {
+        const int sl = wb + kWave * q + lane;
+        if (sl >= n || pos[q] < 0) key[q] = 0u;
+        spos[sl] = pos[q];
+    }
+    clear_hist(sh);
+    block_select<KPT>(sh, key, top_k, [&](int place, int slot) { out[place] = spos[slot]; });
 }
 
 int topk_segments(int max_seq_len) { return (max_seq_len + kSegLen - 1) / kSegLen; }
@@ -368,13 +414,12 @@ size_t topk_ws_bytes(int rows, int max_seq_len, int top_k) {
     if (max_seq_len <= 32 * 1024) return 0;
     const int64_t n = (int64_t)topk_segments(max_seq_len) * top_k;
     if (n > 32 * 1024) return 0;  // beyond the merge kernel: the global-memory kernel, no workspace
-    return sizeof(int32_t) * (size_t)rows * (size_t)n;
+    return 2 * sizeof(int32_t) * (size_t)rows * (size_t)n;  // positions, then their keys
 }
 
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
     const int rows = a.batch * a.n_q;
     if (rows == 0) return hipSuccess;
-    const bool vec = (a.ld % 4) == 0 && ((uintptr_t)a.scores % 16) == 0;
     // persistent workgroups for the register-resident kernel: at most two per
     // compute unit
     int cus = 0;
@@ -383,21 +428,23 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
     const int reg_grid = rows < 2 * cus ? rows : 2 * cus;
 #define DSA_REG(K)                                                                                           \
     hipLaunchKernelGGL((topk_reg_kernel<K>), dim3(reg_grid), dim3(kSelThreads), 0, st, a.scores, a.ld,      \
-                       a.seq_lens, a.n_q, a.max_seq_len, rows, a.top_k, vec, a.indices)
+                       a.seq_lens, a.n_q, a.max_seq_len, rows, a.top_k, a.indices)
     if (a.max_seq_len <= 8 * 1024) DSA_REG(8);
     else if (a.max_seq_len <= 16 * 1024) DSA_REG(16);
     else if (a.max_seq_len <= 32 * 1024) DSA_REG(32);
 #undef DSA_REG
     else if (topk_ws_bytes(rows, a.max_seq_len, a.top_k) > 0) {
         const int nseg = topk_segments(a.max_seq_len);
+        const int n = nseg * a.top_k;
+        int32_t* cand = a.ws;
+        uint32_t* ckey = reinterpret_cast<uint32_t*>(a.ws + (size_t)rows * n);
         hipLaunchKernelGGL(topk_segment_kernel, dim3(nseg, rows), dim3(kSelThreads), 0, st, a.scores, a.ld,
-                           a.seq_lens, a.n_q, a.max_seq_len, rows, a.top_k, vec, nseg, a.ws);
+                           a.seq_lens, a.n_q, a.max_seq_len, rows, a.top_k, nseg, cand, ckey);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const int n = nseg * a.top_k;
 #define DSA_MERGE(K)                                                                                         \
-    hipLaunchKernelGGL((topk_merge_kernel<K>), dim3(rows), dim3(kSelThreads), 0, st, a.scores, a.ld, a.seq_lens, \
-                       a.n_q, a.max_seq_len, rows, a.top_k, nseg, a.ws, a.indices)
+    hipLaunchKernelGGL((topk_merge_kernel<K>), dim3(rows), dim3(kSelThreads), 0, st, a.seq_lens, a.n_q,       \
+                       a.max_seq_len, rows, a.top_k, nseg, cand, ckey, a.indices)
         if (n <= 8 * 1024) DSA_MERGE(8);
         else if (n <= 16 * 1024) DSA_MERGE(16);
         else DSA_MERGE(32);
