@@ -167,33 +167,72 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
     int64_t num_blocks, int n_q, int max_seq_len, float* __restrict__ scores, int64_t ld) {
     static_assert(NQ <= 2, "decode rows per sequence");
     const int b = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: the table reads are scalar
     const int g = lane >> 4, j = lane & 15;
     const int Lb = clamp_len(seq_lens, b, max_seq_len);
     if ((int)blockIdx.x * NW * TPW * kBlock >= Lb) return;  // block-uniform
     const int tile0 = (blockIdx.x * NW + wave) * TPW;
 
-    // the sequence's query rows, staged once per workgroup (padded rows keep
-    // the 16-row fragment reads conflict free)
+    // Memory round trips before the first K tile: the block-table entries
+    // (the K addresses depend on them) are read first, then the query units
+    // are loaded into registers; the K loads issue as soon as the table
+    // entries arrive, and the query goes to LDS (padded rows keep the 16-row
+    // fragment reads conflict free) while the K tiles are in flight.
+    int32_t traw[TPW];  // raw table entries; checked once the later loads are issued
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int t = tile0 + u;
+        traw[u] = table[(int64_t)b * max_blocks + (t < max_blocks ? t : 0)];  // unconditional read
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the table reads issue first
     constexpr int QROW = T::ROW + 16;
+    constexpr int QUNITS = NQ * kIdxHeads * T::ROW / 16;
+    constexpr int QPER = (QUNITS + 64 * NW - 1) / (64 * NW);  // query units per thread
     __shared__ __attribute__((aligned(16))) uint8_t q_s[NQ * kIdxHeads * QROW];
-    {
-        constexpr int UNITS = NQ * kIdxHeads * T::ROW / 16;
-        for (int u = threadIdx.x; u < UNITS; u += 64 * NW) {
-            const int hr = u / (T::ROW / 16), c = u % (T::ROW / 16);  // head row (qi*64 + h), unit
-            const int qi = hr / kIdxHeads;
-            const int64_t rr = (int64_t)b * n_q + (qi < n_q ? qi : 0);
-            *reinterpret_cast<i32x4*>(q_s + hr * QROW + 16 * c) = *reinterpret_cast<const i32x4*>(
-                q + (rr * kIdxHeads + hr % kIdxHeads) * (int64_t)T::ROW + 16 * c);
+    i32x4 qunit[QPER];
+    auto q_unit = [&](int k, int& hr, int& c) {
+        const int u = min((int)threadIdx.x + 64 * NW * k, QUNITS - 1);  // unconditional: one batch of loads
+        hr = u / (T::ROW / 16);                                          // head row qi*64 + h
+        c = u % (T::ROW / 16);                                           // 16-byte unit of the row
+    };
+#pragma unroll
+    for (int k = 0; k < QPER; ++k) {
+        int hr, c;
+        q_unit(k, hr, c);
+        const int qi = hr / kIdxHeads;
+        const int64_t rr = (int64_t)b * n_q + (qi < n_q ? qi : 0);
+        qunit[k] = *reinterpret_cast<const i32x4*>(q + (rr * kIdxHeads + hr % kIdxHeads) * (int64_t)T::ROW + 16 * c);
+    }
+    // head weights (and query scales), also before the K tiles
+    float wr[NQ][4][4];
+    int qsx[NQ][4];  // MXFP8: E8M0 scale of head 16mt + j, k-block g
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) {
+        const bool valid = qi < n_q;
+        const int64_t rr = (int64_t)b * n_q + (valid ? qi : 0);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            qsx[qi][mt] = T::MX ? (int)static_cast<const uint8_t*>(q_scale)[(rr * kIdxHeads + 16 * mt + j) * 4 + g]
+                                : 127;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = 16 * mt + 4 * g + i;
+                float x = w[rr * kIdxHeads + h];
+                if constexpr (T::SCALED) x *= static_cast<const float*>(q_scale)[rr * kIdxHeads + h];
+                wr[qi][mt][i] = valid ? x : 0.f;
+            }
         }
     }
-
+    __builtin_amdgcn_sched_barrier(0);  // the loads above issue before the table entries are used
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) asm volatile("" ::"s"(traw[u]));  // all entries arrive in one round trip
     int64_t pt[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int t = tile0 + u;
-        const int64_t p = phys_block(table, max_blocks, b, t, num_blocks);  // unconditional read
-        pt[u] = t * kBlock < Lb ? p : -1;
+        const int64_t p = traw[u];
+        pt[u] = (t * kBlock < Lb && t < max_blocks && p >= 0 && p < num_blocks) ? p : -1;
     }
     typename T::frag kf[2][4][T::KSTEPS];
     float ksc[2][4];  // fp8: the position's scale; MXFP8: its E8M0 byte of k-block g (as bits)
@@ -211,31 +250,23 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
     };
     load_tile(0, kf[0], ksc[0]);
     if (TPW > 1) load_tile(1, kf[1], ksc[1]);
+#pragma unroll
+    for (int k = 0; k < QPER; ++k) {
+        int hr, c;
+        q_unit(k, hr, c);
+        *reinterpret_cast<i32x4*>(q_s + hr * QROW + 16 * c) = qunit[k];
+    }
 
     typename T::frag qa[NQ][4][T::KSTEPS];
-    float wr[NQ][4][4];
-    int qsx[NQ][4];  // MXFP8: E8M0 scale of head 16mt + j, k-block g
     __syncthreads();
 #pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
-        const bool valid = qi < n_q;
-        const int64_t rr = (int64_t)b * n_q + (valid ? qi : 0);
+    for (int qi = 0; qi < NQ; ++qi)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const uint8_t* v = q_s + (qi * kIdxHeads + 16 * mt + j) * QROW;
 #pragma unroll
             for (int ks = 0; ks < T::KSTEPS; ++ks) qa[qi][mt][ks] = load_frag<T>(v, ks, g);
-            qsx[qi][mt] = T::MX ? (int)static_cast<const uint8_t*>(q_scale)[(rr * kIdxHeads + 16 * mt + j) * 4 + g]
-                                : 127;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int h = 16 * mt + 4 * g + i;
-                float x = w[rr * kIdxHeads + h];
-                if constexpr (T::SCALED) x *= static_cast<const float*>(q_scale)[rr * kIdxHeads + h];
-                wr[qi][mt][i] = valid ? x : 0.f;
-            }
         }
-    }
 
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
