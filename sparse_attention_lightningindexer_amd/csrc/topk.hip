@@ -162,8 +162,6 @@ struct SelectShared {
     uint32_t hist[4096];
     uint32_t wsum[kSelWaves] __attribute__((aligned(16)));
     uint32_t cut_digit, cut_above;
-    uint64_t gt_mask[kSelWaves * KPT];  // column q of wave w is word KPT * w + q
-    uint64_t eq_mask[kSelWaves * KPT];
 };
 
 template <int KPT>
@@ -175,20 +173,20 @@ __device__ __forceinline__ void clear_hist(SelectShared<KPT>& sh) {
 template <int KPT, class Emit>
 __device__ __forceinline__ void block_select(SelectShared<KPT>& sh, const uint32_t (&key)[KPT], int top_k,
                                              Emit&& emit) {
-    static_assert(KPT == 8 || KPT == 16 || KPT == 32, "a thread's KPT slots lie in one 64-bit column word");
+    static_assert(KPT <= 32, "registers per thread");
     constexpr int NT = kSelThreads, NW = kSelWaves;
     // the wave index is uniform across the wave; saying so keeps the per-wave
     // comparisons below scalar instead of 64-bit lane masks held in registers
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    auto wsum_where = [&](auto pick) -> uint32_t {  // sum of the per-wave totals of the waves w with pick(w)
-        uint32_t t = 0u;
-#pragma unroll
-        for (int q = 0; q < NW / 4; ++q) {
-            const uint4 v = reinterpret_cast<const uint4*>(sh.wsum)[q];
-            t += (pick(4 * q) ? v.x : 0u) + (pick(4 * q + 1) ? v.y : 0u) + (pick(4 * q + 2) ? v.z : 0u) +
-                 (pick(4 * q + 3) ? v.w : 0u);
-        }
-        return t;
+    // sums of the per-wave totals in sh.wsum over the waves before this one
+    // and after it: lane w < NW reads wave w's total, one wave scan, two
+    // lane reads (no per-wave comparisons held in registers)
+    auto wsum_around = [&](uint32_t& before, uint32_t& after) {
+        const uint32_t v = lane < NW ? sh.wsum[lane] : 0u;
+        const uint32_t incl = wave_scan_incl(v);
+        const uint32_t upto = __builtin_amdgcn_readlane(incl, wave);
+        before = upto - __builtin_amdgcn_readlane(v, wave);
+        after = __builtin_amdgcn_readlane(incl, NW - 1) - upto;
     };
     uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)top_k;  // uniform
     auto pass = [&](int shift, int bits, bool first) {
@@ -211,7 +209,9 @@ __device__ __forceinline__ void block_select(SelectShared<KPT>& sh, const uint32
         if (lane == 0) sh.wsum[wave] = wtot;
         __syncthreads();
         // keys in higher bins: later lanes of this wave, then later waves
-        const uint32_t above = (wtot - P) + wsum_where([&](int w) { return w > wave; });
+        uint32_t wb_, wa_;
+        wsum_around(wb_, wa_);
+        const uint32_t above = (wtot - P) + wa_;
         // S(d) = keys with digit >= d; the cut digit D has S(D) >= krem > S(D+1)
         if (above < krem && above + own >= krem) {
             uint32_t sfx = above;
@@ -235,40 +235,37 @@ __device__ __forceinline__ void block_select(SelectShared<KPT>& sh, const uint32
 
     // prefix is the k-th largest key T; krem keys equal to it are taken, lowest first.
     const uint32_t T = prefix;
-    // the column masks of the keys > T and == T, written by the wave's lane 0
+    // Ordered emit, column by column.  A kept slot's place is the number of
+    // kept slots before it: the keys > T before it plus min(keys == T before
+    // it, krem).  The waves' totals go through one block scan; within a wave
+    // the running counts of the earlier columns are scalar and a column's own
+    // lanes count with mbcnt.  The comparisons are made again in the second
+    // loop (T passes through an opaque copy) rather than held as lane masks.
+    uint32_t wgt = 0u, weq = 0u;  // this wave's keys > T and == T (uniform)
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
-        const uint64_t mg = ballot(key[q] > T), me = ballot(key[q] == T);
-        if (lane == 0) {
-            sh.gt_mask[KPT * wave + q] = mg;
-            sh.eq_mask[KPT * wave + q] = me;
-        }
+        wgt += (uint32_t)__popcll(ballot(key[q] > T));
+        weq += (uint32_t)__popcll(ballot(key[q] == T));
+        asm volatile("" : "+s"(wgt), "+s"(weq));  // summed column by column, one column's masks live
     }
+    if (lane == 0) sh.wsum[wave] = (wgt << 16) | weq;  // both totals stay below 2^16
     __syncthreads();
-    // thread t: slots KPT*t .. KPT*t + KPT - 1, bits (KPT*t) % 64 .. of word (KPT*t) / 64
-    constexpr uint32_t kBits = KPT == 32 ? 0xffffffffu : (1u << KPT) - 1u;
-    const int bit0 = (KPT * tid) & 63;
-    uint32_t gt32 = (uint32_t)(sh.gt_mask[(KPT * tid) >> 6] >> bit0) & kBits;
-    uint32_t eq32 = (uint32_t)(sh.eq_mask[(KPT * tid) >> 6] >> bit0) & kBits;
-    // both totals stay below 2^16 (at most 32768 slots)
-    const uint32_t packed = ((uint32_t)__builtin_popcount(gt32) << 16) | (uint32_t)__builtin_popcount(eq32);
-    const uint32_t incl = wave_scan_incl(packed);
-    if (lane == kWave - 1) sh.wsum[wave] = incl;
-    __syncthreads();
-    const uint32_t excl = (incl - packed) + wsum_where([&](int w) { return w < wave; });
-    const uint32_t gt_before = excl >> 16, eq_before = excl & 0xffffu;
-    int place = (int)(gt_before + min(eq_before, krem));
-    // the lowest krem - eq_before of this thread's keys equal to T are kept
-    uint32_t take = eq_before < krem ? krem - eq_before : 0u;
-    uint32_t sel = gt32;
-    while (take > 0u && eq32 != 0u) {
-        sel |= eq32 & (0u - eq32);
-        eq32 &= eq32 - 1u;
-        --take;
-    }
-    while (sel != 0u) {  // ascending slot order
-        emit(place++, KPT * tid + __builtin_ctz(sel));
-        sel &= sel - 1u;
+    uint32_t before, after_;
+    wsum_around(before, after_);
+    uint32_t gtb = before >> 16, eqb = before & 0xffffu;  // keys > T and == T in earlier columns
+    uint32_t Tq = T;
+    asm volatile("" : "+s"(Tq));
+    const int wslot = KPT * kWave * wave + lane;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+        const bool gt = key[q] > Tq, eq = key[q] == Tq;
+        const uint64_t mg = ballot(gt), me = ballot(eq);
+        const uint32_t eq_before = eqb + (uint32_t)lanes_below(me);
+        if (gt || (eq && eq_before < krem))
+            emit((int)(gtb + (uint32_t)lanes_below(mg) + min(eq_before, krem)), q, wslot + kWave * q);
+        gtb += (uint32_t)__popcll(mg);
+        eqb += (uint32_t)__popcll(me);
+        asm volatile("" : "+s"(gtb), "+s"(eqb));  // one column's masks live at a time
     }
 }
 
@@ -314,7 +311,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_reg_kernel(const float* __re
         }
         uint32_t key[KPT];
         load_keys<KPT>(scores + (int64_t)r * ld, wb, L, lane, key);
-        block_select<KPT>(sh, key, top_k, [&](int place, int slot) { out[place] = slot; });
+        block_select<KPT>(sh, key, top_k, [&](int place, int, int slot) { out[place] = slot; });
         __syncthreads();  // the scan words and column masks are reused by the next row
     }
 }
@@ -335,7 +332,6 @@ __global__ __launch_bounds__(kSelThreads) void topk_segment_kernel(const float* 
                                                                    int32_t* __restrict__ cand,
                                                                    uint32_t* __restrict__ ckey) {
     __shared__ SelectShared<kSegKpt> sh;
-    __shared__ uint32_t skey[kSegLen];  // the segment's keys by slot, for the emit
     const int seg = blockIdx.x, r = rows - 1 - (int)blockIdx.y;
     const int b = r / n_q, i0 = r % n_q;
     const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, i0);
@@ -357,12 +353,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_segment_kernel(const float* 
     const int wb = kSegKpt * kWave * __builtin_amdgcn_readfirstlane(tid >> 6);
     uint32_t key[kSegKpt];
     load_keys<kSegKpt>(row, wb, Ls, lane, key);
-#pragma unroll
-    for (int q = 0; q < kSegKpt; ++q) skey[wb + kWave * q + lane] = key[q];
     clear_hist(sh);
-    block_select<kSegKpt>(sh, key, top_k, [&](int place, int slot) {
+    block_select<kSegKpt>(sh, key, top_k, [&](int place, int q, int slot) {
         outp[place] = s0 + slot;
-        outk[place] = skey[slot];
+        outk[place] = key[q];
     });
 }
 
@@ -373,7 +367,6 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(const int32_t* 
                                                                  const uint32_t* __restrict__ ckey,
                                                                  int32_t* __restrict__ indices) {
     __shared__ SelectShared<KPT> sh;
-    __shared__ int32_t spos[KPT * kSelThreads];  // candidate positions by slot, for the emit
     const int r = rows - 1 - (int)blockIdx.x;
     const int b = r / n_q, i0 = r % n_q;
     const int L = history_len(clamp_len(seq_lens, b, max_seq_len), n_q, i0);
@@ -396,16 +389,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(const int32_t* 
         pos[q] = cr[sl];
         key[q] = ck[sl];
     }
-    // slots past the list (n <= KPT * 1024) and -1 padding are empty; an empty
-    // slot's position is never read
+    // slots past the list (n <= KPT * 1024) and -1 padding are empty
 #pragma unroll
-    for (int q = 0; q < KPT; ++q) {
-        const int sl = wb + kWave * q + lane;
-        if (sl >= n || pos[q] < 0) key[q] = 0u;
-        spos[sl] = pos[q];
-    }
+    for (int q = 0; q < KPT; ++q)
+        if (wb + kWave * q + lane >= n || pos[q] < 0) key[q] = 0u;
     clear_hist(sh);
-    block_select<KPT>(sh, key, top_k, [&](int place, int slot) { out[place] = spos[slot]; });
+    block_select<KPT>(sh, key, top_k, [&](int place, int q, int) { out[place] = pos[q]; });
 }
 
 int topk_segments(int max_seq_len) { return (max_seq_len + kSegLen - 1) / kSegLen; }
