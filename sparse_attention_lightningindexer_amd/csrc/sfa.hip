@@ -48,23 +48,16 @@ constexpr float kSlack = 32.0f;        // probabilities may exceed 1 by up to 2^
 __device__ __forceinline__ int row_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int lds_unit(int row, int u) { return row * kRowB + ((u ^ row_swz(row)) << 4); }
 
-// E8M0 byte -> fp32 2^(b-127) (b = 0 gives the subnormal 2^-127; 255 is NaN).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
-    if (b == 0u) return __uint_as_float(0x00400000u);
-    if (b == 255u) return __uint_as_float(0x7fc00000u);
-    return __uint_as_float(b << 23);
-}
-
-// 16 e4m3 codes (one 16-byte unit) times a power-of-two scale -> 16 bf16 (exact).
-__device__ __forceinline__ void dequant_unit(i32x4 codes, float scale, i32x4& lo, i32x4& hi) {
+// 16 e4m3 codes (one 16-byte unit) times the power of two 2^(e8m0 - 127) ->
+// 16 bf16 (exact): the scaled conversion takes the scale's exponent field as
+// the E8M0 byte, two codes per instruction.
+__device__ __forceinline__ void dequant_unit_mx(i32x4 codes, uint32_t e8m0, i32x4& lo, i32x4& hi) {
+    const float scale = __uint_as_float(e8m0 << 23);  // only the exponent field is read
     uint32_t packed[8];
+#pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(codes[w], false);
-        const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(codes[w], true);
-        const uint32_t b0 = __float_as_uint(a[0] * scale) >> 16, b1 = __float_as_uint(a[1] * scale) >> 16;
-        const uint32_t b2 = __float_as_uint(c[0] * scale) >> 16, b3 = __float_as_uint(c[1] * scale) >> 16;
-        packed[2 * w] = b0 | (b1 << 16);
-        packed[2 * w + 1] = b2 | (b3 << 16);
+        packed[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[w], scale, false));
+        packed[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[w], scale, true));
     }
     lo = i32x4{(int)packed[0], (int)packed[1], (int)packed[2], (int)packed[3]};
     hi = i32x4{(int)packed[4], (int)packed[5], (int)packed[6], (int)packed[7]};
@@ -306,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                 const int U = min(kWave * i + lane, kStRows * kMxUnitsRow - 1);
                 const int r = U / kMxUnitsRow, u = U - r * kMxUnitsRow;
                 i32x4 lo, hi;
-                if constexpr (KV == 2) dequant_unit(st.v[i], e8m0_to_f32(st.sc[i]), lo, hi);
+                if constexpr (KV == 2) dequant_unit_mx(st.v[i], st.sc[i], lo, hi);
                 else dequant_unit_rne(st.v[i], __uint_as_float(st.sc[i]), lo, hi);
                 *reinterpret_cast<i32x4*>(T + lds_unit(srow0 + r, 2 * u)) = lo;
                 *reinterpret_cast<i32x4*>(T + lds_unit(srow0 + r, 2 * u + 1)) = hi;
