@@ -163,13 +163,14 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     // 0. ordered compaction of the valid index slots into pool-row numbers.
     //    All of the split's indices are loaded first, then all of their table
     //    entries (two memory round trips in total), then compacted.
-    //    Run by both roles (the QK waves first issue their query loads, which
-    //    then arrive during the compaction); it ends with a barrier, after
+    //    Run by both roles; the QK waves issue their query loads once the
+    //    indices and table entries have arrived, so the queries arrive during
+    //    the compaction without delaying it.  It ends with a barrier, after
     //    which every wave loads the pool rows of its chunk rows (vid).
     const int srow0 = kStRows * wave;  // the wave's first chunk row (staging, below)
     int n_valid = 0, nchunks = 0;
     int vid[kStRows];  // pool row of chunk row srow0 + r of chunk c, in lane c
-    auto compact = [&]() __attribute__((always_inline)) {
+    auto compact = [&](auto&& after_reads) __attribute__((always_inline)) {
         constexpr int kSlotIters = kAttnMaxSplitSlots / kThreads;
         // The sequence's block-table row goes to LDS beside the slot list
         // (when it fits), loaded together with the indices: then the
@@ -189,11 +190,13 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                 const int v = indices[(int64_t)row * top_k + min(t, top_k - 1)];
                 sv[k] = t < slot1 && v >= 0 && v < L ? v : -1;
             }
-            if (tab_lds) {
+            if (tab_lds)
                 for (int jb = tid; jb < nb; jb += kThreads)
                     tab_s[jb] = (int)phys_block(table, max_blocks, b, jb, num_blocks);
-                __syncthreads();
-            }
+            if (tab_lds) __syncthreads();
+            // the indices and table entries have arrived; later loads (the QK
+            // waves' query) now overlap the compaction instead of delaying it
+            after_reads();
 #pragma unroll
             for (int k = 0; k < kSlotIters; ++k) {
                 const int sk = sv[k];
@@ -355,12 +358,11 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         // q[hb + hl0 + j][32ks + 8g .. +8] (the B operand of S^T = K . Q^T).
         const int hl0 = kQkHeads * wave;
         bf16x8 qf[kDqk / 32];
-        {
+        compact([&]() __attribute__((always_inline)) {
             const uint16_t* qrow = q + ((int64_t)row * kH + hb + hl0 + j) * kDqk + 8 * g;
 #pragma unroll
             for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-        }
-        compact();
+        });
         // per head hl0 + j (identical in the four lane groups): the reference,
         // the largest scaled logit seen, and the denominator
         float m_ref = -INFINITY, m_obs = -INFINITY, l_run = 0.f;
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
         // value channels 128pw + 16dt + 4g + i for the half's 64 heads:
         // o[dt][ht] holds O^T[128pw + 16dt + 4g + i][head hb + 16ht + j].
         const int pw = wave - kRoleWaves;
-        compact();
+        compact([]() __attribute__((always_inline)) {});
         f32x4 o[kDvPerPv / 16][kHalf / 16];
 #pragma unroll
         for (int dt = 0; dt < kDvPerPv / 16; ++dt)
@@ -488,8 +490,13 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
 #pragma unroll
             for (int ht = 0; ht < kHalf / 16; ++ht)
                 pf[ht] = *reinterpret_cast<const bf16x8*>(pbuf[c & 1] + (16 * ht + j) * kPRow + 16 * g);
-            const int e_ = j >> 2, q4 = j & 3;
-            const int r0 = 8 * g + e_, r1 = 8 * g + 4 + e_;
+            // the V^T read places are rebuilt per chunk from a fresh lane index
+            // rather than held in registers through the pipeline
+            int lv = lane;
+            asm volatile("" : "+v"(lv));
+            const int jv = lv & 15, gv = lv >> 4;
+            const int e_ = jv >> 2, q4 = jv & 3;
+            const int r0 = 8 * gv + e_, r1 = 8 * gv + 4 + e_;
             auto vaddr = [&](int r_, int dd) __attribute__((always_inline)) -> const uint8_t* {
                 const int unit = 16 * pw + 2 * dd + (q4 >> 1);
                 return T + r_ * kRowB + ((unit ^ row_swz(r_)) << 4) + 8 * (q4 & 1);
@@ -560,19 +567,24 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     const uint8_t* obuf = &tile[0][0];
     const int64_t part = (int64_t)row * splits + split;
     uint16_t* dst = splits == 1 ? out + ((int64_t)row * kH + hb) * kDv : ws_o + (part * kH + hb) * kDv;
+    // the thread index, taken afresh: the addresses below are rebuilt here
+    // rather than held in registers through the whole pipeline
+    int t4 = (int)threadIdx.x;
+    asm volatile("" : "+v"(t4));
+    const int l4 = t4 & 63;
 #pragma unroll
     for (int k = 0; k < kHalf / kWaves; ++k) {
         const int h = wave + kWaves * k;
-        *reinterpret_cast<uint4*>(dst + (int64_t)h * kDv + 8 * lane) =
-            *reinterpret_cast<const uint4*>(obuf + h * kORow + 16 * lane);
+        *reinterpret_cast<uint4*>(dst + (int64_t)h * kDv + 8 * l4) =
+            *reinterpret_cast<const uint4*>(obuf + h * kORow + 16 * l4);
     }
-    if (tid < kHalf) {
-        const float lsum = l_s[tid];
-        const float hl_lse = lsum > 0.f ? (m_s[tid] + __log2f(lsum)) * kLn2 : -INFINITY;
+    if (t4 < kHalf) {
+        const float lsum = l_s[t4];
+        const float hl_lse = lsum > 0.f ? (m_s[t4] + __log2f(lsum)) * kLn2 : -INFINITY;
         if (splits == 1) {
-            if (lse != nullptr) lse[(int64_t)row * kH + hb + tid] = hl_lse;
+            if (lse != nullptr) lse[(int64_t)row * kH + hb + t4] = hl_lse;
         } else {
-            ws_lse[part * kH + hb + tid] = hl_lse;
+            ws_lse[part * kH + hb + t4] = hl_lse;
         }
     }
 }
