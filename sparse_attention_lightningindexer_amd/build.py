@@ -4,15 +4,18 @@ Every HIP source is compiled by hipcc for gfx950 with packed-fp32 instructions
 disabled, then linked into one shared library.  Objects go to _build/ next to
 this file.
 
-Resource guard.  Several kernels wait on hand-counted `s_waitcnt vmcnt(n)`
-over loads issued outside the compiler's bookkeeping (global_load_lds into an
-LDS ring).  Those counts are exact only while the compiler adds no vector
-memory operation of its own to the loops, and register spills to scratch are
-such operations.  Every source is therefore compiled with the compiler's
-per-kernel resource remarks, and the build fails if a kernel of a source that
-issues such loads (one that calls wait_vmcnt) uses scratch memory or spills
-vector registers.  In the other sources a spill costs only time; it is
-reported.  The per-kernel figures are written to _build/resource_usage.json.
+Resource guard.  Every source is compiled with the compiler's per-kernel
+resource remarks, and the build fails if a kernel uses scratch memory or
+spills vector registers, for two reasons:
+  * correctness: several kernels wait on hand-counted `s_waitcnt vmcnt(n)`
+    over loads issued outside the compiler's bookkeeping (global_load_lds
+    into an LDS ring).  Those counts are exact only while the compiler adds
+    no vector memory operation of its own to the loops, and spills are such
+    operations.  In a source that calls wait_vmcnt this is always an error;
+  * time: on this stack a kernel with scratch memory pays about 3 us of
+    dispatch set-up per launch, as much as a whole decode Top-K.  In the
+    other sources DSA_ALLOW_SCRATCH=1 turns this failure into a report.
+The per-kernel figures are written to _build/resource_usage.json.
 """
 import json
 import os
@@ -82,8 +85,12 @@ def compile_source(path: str, obj: str, verbose: bool = False) -> dict:
     if bad and uses_counted_waits(path):
         raise RuntimeError(f"{name}: kernels using scratch memory or spilling vector registers "
                            "(hand-counted vmcnt waits would be wrong):\n  " + "\n  ".join(bad))
+    if bad and os.environ.get("DSA_ALLOW_SCRATCH") != "1":
+        raise RuntimeError(f"{name}: kernels using scratch memory or spilling vector registers "
+                           "(about 3 us of dispatch set-up per launch; DSA_ALLOW_SCRATCH=1 only "
+                           "reports them):\n  " + "\n  ".join(bad))
     if bad and verbose:
-        print(f"{name}: spills (no hand-counted waits in this source):\n  " + "\n  ".join(bad))
+        print(f"{name}: spills (allowed by DSA_ALLOW_SCRATCH=1):\n  " + "\n  ".join(bad))
     return usage
 
 

@@ -1,7 +1,9 @@
 """The build's resource guard (CPU only): hipcc's per-kernel resource remarks are
 parsed, and a kernel that uses scratch memory or spills vector registers fails
-the build, since the hand-counted vmcnt waits of the LDS-ring kernels are exact
-only without compiler-issued memory operations in their loops."""
+the build: always where waits are hand-counted (the vmcnt waits of the
+LDS-ring kernels are exact only without compiler-issued memory operations in
+their loops), and elsewhere unless DSA_ALLOW_SCRATCH=1 (a kernel with scratch
+memory pays a per-launch dispatch set-up)."""
 import json
 import os
 
@@ -40,23 +42,31 @@ def test_parser_reads_every_kernel_and_flags_scratch_and_vgpr_spills():
     assert len(bad) == 1 and bad[0].startswith("_Z6kernelPf")   # SGPR spills go to VGPR lanes: allowed
 
 
-def test_a_kernel_using_scratch_fails_the_build_where_waits_are_counted(tmp_path):
+def test_a_kernel_using_scratch_fails_the_build(tmp_path, monkeypatch):
     if not os.path.exists(Bld.HIPCC):
         pytest.skip("hipcc not installed")
+    monkeypatch.delenv("DSA_ALLOW_SCRATCH", raising=False)
     src = tmp_path / "spills.hip"
     src.write_text(SPILLING_KERNEL)
-    with pytest.raises(RuntimeError, match="scratch"):
+    with pytest.raises(RuntimeError, match="hand-counted"):
         Bld.compile_source(str(src), str(tmp_path / "spills.o"))
-    # the same kernel in a source without counted waits builds (the spill is reported)
+    # without counted waits it fails too, for the dispatch cost ...
     src2 = tmp_path / "spills_plain.hip"
     src2.write_text(SPILLING_KERNEL.replace("wait_vmcnt", "no counted waits"))
+    with pytest.raises(RuntimeError, match="dispatch"):
+        Bld.compile_source(str(src2), str(tmp_path / "spills_plain.o"))
+    # ... unless allowed, and then it is only reported
+    monkeypatch.setenv("DSA_ALLOW_SCRATCH", "1")
     usage = Bld.compile_source(str(src2), str(tmp_path / "spills_plain.o"))
     assert Bld.resource_violations(usage)
+    # the allowance never covers a source with counted waits
+    with pytest.raises(RuntimeError, match="hand-counted"):
+        Bld.compile_source(str(src), str(tmp_path / "spills.o"))
 
 
-def test_the_library_kernels_with_counted_waits_use_no_scratch():
+def test_the_library_kernels_use_no_scratch():
     """The last build's report lists the LDS-ring kernels (hand-counted waits), and
-    every kernel of their sources is free of scratch use and VGPR spills."""
+    every kernel of every source is free of scratch use and VGPR spills."""
     path = os.path.join(Bld.OUT, "resource_usage.json")
     if not os.path.exists(path):
         pytest.skip("library not built")
@@ -67,3 +77,6 @@ def test_the_library_kernels_with_counted_waits_use_no_scratch():
     assert any("indexer_prefill_kernel" in k for k in kernels)
     assert any("indexer_prolog_kernel" in k for k in kernels)
     assert not Bld.resource_violations(kernels)
+    everything = {k: v for s in report for k, v in report[s].items()}
+    assert any("sfa_mla_kernel" in k for k in everything) and any("topk_" in k for k in everything)
+    assert not Bld.resource_violations(everything)
