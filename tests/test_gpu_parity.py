@@ -187,6 +187,45 @@ def test_topk_register_resident_lengths_with_ties(long_len, top_k):
     check_indices_exact(idx, O.topk(s.astype(np.float64), wl.row_lens(), top_k))
 
 
+@pytest.mark.parametrize("long_len", [8192, 32768, 100000, 140000])
+def test_topk_nan_scores_still_give_valid_index_rows(long_len):
+    """NaN scores have no specified order (dsa.h), but every row must still come
+    out as k_r distinct ascending positions of its history, and the finite scores
+    kept must be the largest finite ones: positive NaNs sort above +inf and
+    negative NaNs below -inf, the all-ones NaN included (it shares the lowest
+    real key)."""
+    # 100000 x 4096: segments and merge; 140000 x 4096: no workspace
+    top_k = 2048 if long_len < 100000 else 4096
+    wl = make_workload(4, batch=2, lens=[long_len, long_len // 3 + 5], top_k=top_k)
+    dev = B.DeviceInputs(wl)
+    say(f"[parity] topk NaN rows {long_len}")
+    rng = np.random.default_rng(long_len + 11)
+    s = rng.standard_normal((wl.rows, long_len)).astype(np.float32)
+    bits = s.view(np.uint32)
+    bits[:, ::37] = 0x7FC00000                            # quiet NaN
+    bits[:, 5::211] = 0xFFFFFFFF                          # the all-ones NaN (key 1)
+    bits[:, 9::401] = 0xFF800001                          # negative signalling NaN
+    bits[:, 11::503] = 0x7F800001                         # positive signalling NaN
+    idx = B.dsa_topk(dev, torch.from_numpy(s).cuda()).cpu().numpy()
+    for r, L in enumerate(wl.row_lens()):
+        k = min(top_k, int(L))
+        row, sel = s[r, :L], idx[r]
+        assert (sel[k:] == -1).all(), r
+        kept = sel[:k]
+        assert (np.diff(kept) > 0).all() and kept[0] >= 0 and kept[-1] < L, r
+        nan = np.isnan(row)
+        pos_nan = nan & ((row.view(np.uint32) >> 31) == 0)
+        # every positive NaN ranks above every finite score, every negative NaN below
+        n_pos = int(pos_nan.sum())
+        assert n_pos <= k  # by construction of the row
+        assert np.isin(np.nonzero(pos_nan)[0], kept).all(), r
+        fin_kept = kept[~nan[kept]]
+        if n_pos < k and len(fin_kept):
+            lo = row[fin_kept].min()
+            fin = ~nan
+            assert np.isin(np.nonzero(fin & (row > lo))[0], kept).all(), r
+
+
 # ------------------------------------------------------- full workload sizes
 
 @pytest.mark.parametrize("cfg", [1, 2, 4, 5, 6])
