@@ -132,6 +132,39 @@ def test_empty_histories_and_absent_blocks():
     assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
 
 
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_attention_history_too_long_for_the_table_in_lds(cfg):
+    # A 470000-position history: 7344 table blocks, more than the 7168 whose
+    # block-table row the attention's compaction stages in LDS, so the
+    # compaction reads the table from memory per slot.  Logical blocks map
+    # onto the 15 full physical blocks of a 1000-position sequence (two absent),
+    # which is legal paging and keeps the pool small; the indices reach past
+    # position 458752.
+    wl = make_workload(cfg, batch=2, lens=[1000, 700], top_k=512, poison=True)
+    own = wl.block_table[0, :15]             # the 15 full blocks of sequence 0's 1000 positions
+    long_len, nbl = 470000, 7344
+    table = np.full((2, nbl), -1, np.int32)
+    table[0] = own[np.arange(nbl) % own.size]
+    table[0, 7200] = -1                      # an absent block past the LDS window
+    table[0, 100] = wl.num_blocks + 3        # an out-of-range entry: absent too
+    table[1, :wl.block_table.shape[1]] = wl.block_table[1]
+    wl.block_table = table
+    wl.seq_lens = np.array([long_len, 700], np.int32)
+    rng = np.random.default_rng(11)
+    idx = np.full((wl.rows, 512), -1, np.int32)
+    far = rng.choice(np.arange(458752, long_len), 200, replace=False)
+    near = rng.choice(long_len, 300, replace=False)
+    row0 = np.unique(np.concatenate([far, near, [7200 * 64 + 5, 100 * 64 + 1, long_len - 1]]))[:512]
+    idx[0, :row0.size] = row0
+    idx[1, :300] = np.sort(rng.choice(700, 300, replace=False))
+    dev = B.DeviceInputs(wl)
+    say(f"[parity] attention over a {long_len}-position history, cfg {cfg}")
+    out, lse = B.dsa_sparse_attn(dev, torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    ref_o, ref_l = O.sparse_attn(wl, idx)
+    check_attention(wl, f64(out), f64(lse), ref_o, ref_l, f"long table cfg {cfg}")
+
+
 def test_topk_ties_all_equal_scores_and_duplicate_keys():
     wl = make_workload(2, batch=2, lens=[1000, 333], top_k=100)
     dev = B.DeviceInputs(wl)
