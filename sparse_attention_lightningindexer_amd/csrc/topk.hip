@@ -15,7 +15,7 @@
 // longest) down.
 // Three forms:
 //   * rows up to 32768 positions: the keys stay in registers (8, 16 or 32
-//     per thread of a 1024-thread workgroup), three digit passes;
+//     per thread of a 1024-thread workgroup), up to three digit passes;
 //   * longer rows: a top_k per 16384-position segment into a candidate
 //     workspace, then the same register-resident selection over the
 //     candidates;
@@ -161,7 +161,7 @@ template <int KPT>
 struct SelectShared {
     uint32_t hist[4096];
     uint32_t wsum[kSelWaves] __attribute__((aligned(16)));
-    uint32_t cut_digit, cut_above;
+    uint32_t cut_digit, cut_above, cut_count;
 };
 
 template <int KPT>
@@ -219,6 +219,7 @@ __device__ __forceinline__ void block_select(SelectShared<KPT>& sh, const uint32
                 if (sfx + cnt[k] >= krem) {
                     sh.cut_digit = (uint32_t)(per * tid + k);
                     sh.cut_above = sfx;
+                    sh.cut_count = cnt[k];
                     break;
                 }
                 sfx += cnt[k];
@@ -229,12 +230,26 @@ __device__ __forceinline__ void block_select(SelectShared<KPT>& sh, const uint32
         mask |= dm << shift;
         krem -= __builtin_amdgcn_readfirstlane(sh.cut_above);
     };
+    // When the cut bin holds exactly the krem keys still needed, every key from
+    // that bin's lowest value up is kept and the remaining passes are skipped:
+    // the cut becomes the value just below the bin (T = prefix - 1, no keys
+    // equal to T taken).  A bin starting at 0 goes on to the next pass.
+    bool whole_bin = false;
+    auto take_whole_bin = [&]() {
+        whole_bin = __builtin_amdgcn_readfirstlane(sh.cut_count) == krem && prefix != 0u;
+    };
     pass(20, 12, true);
-    pass(10, 10, false);
-    pass(0, 10, false);
+    take_whole_bin();
+    if (!whole_bin) {
+        pass(10, 10, false);
+        take_whole_bin();
+        if (!whole_bin) pass(0, 10, false);
+    }
+    if (whole_bin) krem = 0u;
 
-    // prefix is the k-th largest key T; krem keys equal to it are taken, lowest first.
-    const uint32_t T = prefix;
+    // T is the k-th largest key, or the value just below its whole cut bin;
+    // krem keys equal to it are taken, lowest first.
+    const uint32_t T = whole_bin ? prefix - 1u : prefix;
     // Ordered emit, column by column.  A kept slot's place is the number of
     // kept slots before it: the keys > T before it plus min(keys == T before
     // it, krem).  The waves' totals go through one block scan; within a wave
