@@ -173,7 +173,7 @@ dsa::AttnLaunch attn_launch(const dsa_batch* b, const dsa_attn_args* a, const in
     L.Dv = a->d_v;
     L.top_k = top_k;
     L.sm_scale = a->sm_scale;
-    L.indices = indices;
+    L.indices = const_cast<int32_t*>(indices);  // read only unless L.scores is set
     L.out = a->out;
     L.lse = a->lse;
     L.ws = ws;
@@ -314,10 +314,18 @@ dsa_status forward_impl(const dsa_batch* batch, const dsa_indexer_args* idx, con
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = dsa::launch_indexer(indexer_launch(batch, idx, scores, ld), st);
     if (e != hipSuccess) return DSA_ERR_HIP;
+    dsa::AttnLaunch A = attn_launch(batch, attn, indices, top_k, attn_ws_p);
+    if (dsa::attn_fuses_topk(A)) {
+        // each attention workgroup selects its row's Top-K from the scores and
+        // writes the indices itself: one launch fewer, the same indices
+        A.scores = scores;
+        A.ld = ld;
+        return hip_status(dsa::launch_sparse_attn(A, st));
+    }
     dsa::TopkLaunch T{scores, ld, batch->seq_lens, batch->batch, batch->n_q, batch->max_seq_len, top_k, indices,
                       topk_ws};
     if ((e = dsa::launch_topk(T, st)) != hipSuccess) return DSA_ERR_HIP;
-    return hip_status(dsa::launch_sparse_attn(attn_launch(batch, attn, indices, top_k, attn_ws_p), st));
+    return hip_status(dsa::launch_sparse_attn(A, st));
 }
 
 }  // namespace

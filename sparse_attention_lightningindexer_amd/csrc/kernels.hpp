@@ -56,11 +56,13 @@ struct AttnLaunch {
     int64_t num_blocks;
     int batch, n_q, max_seq_len, H, Dqk, Dv, top_k;
     float sm_scale;
-    const int32_t* indices;
+    int32_t* indices;          // the index lists; written instead when scores is set
     void* out;
     float* lse;
     void* ws;                  // split partials, attn_ws_bytes
     int splits;
+    const float* scores = nullptr;  // set: select each row's Top-K from these (attn_fuses_topk)
+    int64_t ld = 0;
 };
 
 struct AppendLaunch {
@@ -110,6 +112,7 @@ hipError_t launch_indexer_prolog(const PrologLaunch& a, hipStream_t st);
 hipError_t launch_cache_append(const AppendLaunch& a, hipStream_t st);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t st);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st);
+bool attn_fuses_topk(const AttnLaunch& a);
 
 int attn_splits(int rows, int top_k, int Dqk);
 size_t topk_ws_bytes(int rows, int max_seq_len, int top_k);

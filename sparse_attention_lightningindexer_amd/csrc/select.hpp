@@ -44,13 +44,21 @@ struct SelectShared {
     uint32_t cut_digit, cut_above, cut_count;
 };
 
-template <int NT>
-__device__ __forceinline__ void clear_hist(SelectShared<NT>& sh) {
-    for (int t = threadIdx.x; t < 4096; t += NT) sh.hist[t] = 0u;
-    __syncthreads();
+// Workgroup barrier of the select.  LDSB: wait for LDS operations only, so
+// that unrelated global loads (a caller's prefetch) stay in flight.
+template <bool LDSB>
+__device__ __forceinline__ void select_barrier() {
+    if constexpr (LDSB) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else __syncthreads();
 }
 
-template <int NT, int KPT, class Emit>
+template <int NT, bool LDSB = false>
+__device__ __forceinline__ void clear_hist(SelectShared<NT>& sh) {
+    for (int t = threadIdx.x; t < 4096; t += NT) sh.hist[t] = 0u;
+    select_barrier<LDSB>();
+}
+
+template <int NT, int KPT, bool LDSB = false, class Emit>
 __device__ __forceinline__ void block_select(SelectShared<NT>& sh, const uint32_t (&key)[KPT], int top_k,
                                              Emit&& emit) {
     static_assert(KPT <= 32, "registers per thread");
@@ -75,7 +83,7 @@ __device__ __forceinline__ void block_select(SelectShared<NT>& sh, const uint32_
 #pragma unroll
         for (int q = 0; q < KPT; ++q)
             if (first ? key[q] != 0u : (key[q] & mask) == prefix) atomicAdd(&sh.hist[(key[q] >> shift) & dm], 1u);
-        __syncthreads();
+        select_barrier<LDSB>();
         // thread t owns bins [per*t, per*t + per); its counts are read, cleared
         // for the next pass, and scanned from the top digit down.
         const int per = (int)nb / NT;  // bins per thread
@@ -88,7 +96,7 @@ __device__ __forceinline__ void block_select(SelectShared<NT>& sh, const uint32_
         const uint32_t P = wave_scan_incl(own);                    // lanes <= this one
         const uint32_t wtot = __builtin_amdgcn_readlane(P, kWave - 1);
         if (lane == 0) sh.wsum[wave] = wtot;
-        __syncthreads();
+        select_barrier<LDSB>();
         // keys in higher bins: later lanes of this wave, then later waves
         uint32_t wb_, wa_;
         wsum_around(wb_, wa_);
@@ -106,7 +114,7 @@ __device__ __forceinline__ void block_select(SelectShared<NT>& sh, const uint32_
                 sfx += cnt[k];
             }
         }
-        __syncthreads();
+        select_barrier<LDSB>();
         prefix |= __builtin_amdgcn_readfirstlane(sh.cut_digit) << shift;
         mask |= dm << shift;
         krem -= __builtin_amdgcn_readfirstlane(sh.cut_above);
@@ -145,7 +153,7 @@ __device__ __forceinline__ void block_select(SelectShared<NT>& sh, const uint32_
         asm volatile("" : "+s"(wgt), "+s"(weq));  // summed column by column, one column's masks live
     }
     if (lane == 0) sh.wsum[wave] = (wgt << 16) | weq;  // both totals stay below 2^16
-    __syncthreads();
+    select_barrier<LDSB>();
     uint32_t before, after_;
     wsum_around(before, after_);
     uint32_t gtb = before >> 16, eqb = before & 0xffffu;  // keys > T and == T in earlier columns

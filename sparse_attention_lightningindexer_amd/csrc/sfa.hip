@@ -30,6 +30,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace dsa {
 
@@ -102,6 +103,7 @@ constexpr int kRing = 4;                        // bf16 tiles resident in LDS
 constexpr int kPRow = kCh * 2 + 16;             // bytes per head row of P (64 + 16 pad)
 constexpr int kMxUnitsRow = kDqk / 16;          // 36 16-code units per MXFP8 row
 constexpr int kStRows = kCh / kWaves;           // chunk rows gathered per wave
+constexpr int kFusedTopkKpt = 16;               // keys per thread of the fused Top-K (rows up to 8192)
 
 // two floats -> two bfloat16 (round to nearest even) packed in 32 bits
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -126,13 +128,21 @@ __device__ __forceinline__ void dequant_unit_rne(i32x4 codes, float scale, i32x4
 // KV: 1 bf16, 2 MXFP8 (e4m3 + E8M0 per 32), 3 e4m3 + fp32 scale per 128.
 // DENSE: the pool has the dense layout, so a row's place is a constant
 // multiple of its number (no per-row stride arithmetic).
-template <int KV, bool DENSE>
+// TK: 0, the index lists are given (`indices`); else the fused form, in which
+// every workgroup selects its row's top_k positions itself from the indexer's
+// scores (TK keys per thread, rows up to 512 * TK positions), keeps its
+// split's slots, and writes them to `indices` (head half 0).  The selection
+// is the Top-K kernels' own (select.hpp), so the indices are the same
+// ("Day0 Inference Adaptation and Performance Optimization for
+// New-Architecture LLMs", §4.1: the top-k step feeds the sparse core).
+template <int KV, bool DENSE, int TK>
 __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, const void* __restrict__ kvscale,
     PoolLayout kvl, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
-    int64_t num_blocks, int n_q, int max_seq_len, int rows, const int32_t* __restrict__ indices,
+    int64_t num_blocks, int n_q, int max_seq_len, int rows, int32_t* __restrict__ indices,
     int top_k, int per_split, int splits, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, uint16_t* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    float* __restrict__ lse, uint16_t* __restrict__ ws_o, float* __restrict__ ws_lse,
+    const float* __restrict__ scores, int64_t ld) {
     constexpr bool MX = KV != 1;  // e4m3 codes, dequantized to bf16 while staged
     __shared__ __attribute__((aligned(16))) uint8_t tile[kRing][kTileB];
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][kHalf * kPRow];  // P[head][pos] bf16, by chunk parity
@@ -184,19 +194,60 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
             // reads are unconditional (clamped to in-range slots and blocks) so
             // that each round trip is one batch of loads
             int sv[kSlotIters];
+            if constexpr (TK == 0) {
 #pragma unroll
-            for (int k = 0; k < kSlotIters; ++k) {
-                const int t = slot0 + kThreads * k + tid;
-                const int v = indices[(int64_t)row * top_k + min(t, top_k - 1)];
-                sv[k] = t < slot1 && v >= 0 && v < L ? v : -1;
+                for (int k = 0; k < kSlotIters; ++k) {
+                    const int t = slot0 + kThreads * k + tid;
+                    const int v = indices[(int64_t)row * top_k + min(t, top_k - 1)];
+                    sv[k] = t < slot1 && v >= 0 && v < L ? v : -1;
+                }
+                if (tab_lds)
+                    for (int jb = tid; jb < nb; jb += kThreads)
+                        tab_s[jb] = (int)phys_block(table, max_blocks, b, jb, num_blocks);
+                if (tab_lds) __syncthreads();
+                // the indices and table entries have arrived; later loads (the QK
+                // waves' query) now overlap the compaction instead of delaying it
+                after_reads();
+            } else {
+                // The row's Top-K, selected here: the table entries, the row's
+                // score keys and (QK waves) the queries are all issued first, so
+                // the queries arrive during the selection, whose barriers wait
+                // for LDS only.  The split's positions go to spos (tile 0),
+                // the selection's histogram to tile 1.
+                int32_t* const spos = reinterpret_cast<int32_t*>(&tile[0][0]);
+                auto& ssh = *reinterpret_cast<SelectShared<kThreads>*>(&tile[1][0]);
+                static_assert(sizeof(SelectShared<kThreads>) <= kTileB, "select state fits in one tile");
+                static_assert(kAttnMaxSplitSlots * 4 <= kTileB, "split positions fit in one tile");
+                int32_t* const iout = indices + (int64_t)row * top_k;
+                const bool whole = L <= top_k;  // the whole history is kept (workgroup-uniform)
+                uint32_t key[TK];
+                if (!whole) load_keys<TK>(scores + (int64_t)row * ld, TK * kWave * wave, L, lane, key);
+                if (tab_lds)
+                    for (int jb = tid; jb < nb; jb += kThreads)
+                        tab_s[jb] = (int)phys_block(table, max_blocks, b, jb, num_blocks);
+                after_reads();
+                if (whole) {
+                    for (int t = slot0 + tid; t < slot1; t += kThreads) {
+                        spos[t - slot0] = t < L ? t : -1;
+                        if (half == 0) iout[t] = t < L ? t : -1;
+                    }
+                } else {
+                    clear_hist<kThreads, true>(ssh);
+                    block_select<kThreads, TK, true>(ssh, key, top_k, [&](int place, int, int slot) {
+                        if (place >= slot0 && place < slot1) {
+                            spos[place - slot0] = slot;
+                            if (half == 0) iout[place] = slot;
+                        }
+                    });
+                }
+                sync_lds();  // spos and the table row are in LDS
+#pragma unroll
+                for (int k = 0; k < kSlotIters; ++k) {
+                    const int t = slot0 + kThreads * k + tid;
+                    const int v = t < slot1 ? spos[t - slot0] : -1;
+                    sv[k] = v >= 0 && v < L ? v : -1;
+                }
             }
-            if (tab_lds)
-                for (int jb = tid; jb < nb; jb += kThreads)
-                    tab_s[jb] = (int)phys_block(table, max_blocks, b, jb, num_blocks);
-            if (tab_lds) __syncthreads();
-            // the indices and table entries have arrived; later loads (the QK
-            // waves' query) now overlap the compaction instead of delaying it
-            after_reads();
 #pragma unroll
             for (int k = 0; k < kSlotIters; ++k) {
                 const int sk = sv[k];
@@ -721,6 +772,22 @@ int attn_per_split(int top_k, int splits) {
     return ((nchunks + splits - 1) / splits) * kCh;
 }
 
+// Whether the attention selects its rows' Top-K itself (a.scores set): the
+// MLA kernel with a dense pool, rows up to 8192 positions (16 keys per
+// thread), and few enough rows that the Top-K kernel, one workgroup per row,
+// would leave most compute units idle.  Measured on the decode workloads:
+// 8192-position rows save 0.8-2.9 us of a 65-67 us step; 16384-position rows
+// (32 keys per thread) save nothing, the longer selection outweighing the
+// launch it replaces.
+bool attn_fuses_topk(const AttnLaunch& a) {
+    if (a.q_dtype == 0 || a.Dqk != kDqk || a.H != kH || a.Dv != kDv) return false;
+    if (a.max_seq_len > kThreads * kFusedTopkKpt || (int64_t)a.batch * a.n_q > 256) return false;
+    const int64_t drow = a.kv_kind == 1 ? kRowB : kDqk;
+    const int64_t dsrow = a.kv_kind == 2 ? kDqk / 32 : a.kv_kind == 3 ? 5 * 4 : 0;
+    return a.kvl.rs == drow && a.kvl.bs == 64 * drow &&
+           (a.kv_kind == 1 || (a.kvl.srs == dsrow && a.kvl.sbs == 64 * dsrow));
+}
+
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st) {
     const int rows = a.batch * a.n_q;
     if (rows == 0) return hipSuccess;
@@ -743,17 +810,21 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st) {
     const int64_t dsrow = a.kv_kind == 2 ? kDqk / 32 : a.kv_kind == 3 ? 5 * 4 : 0;
     const bool dense = a.kvl.rs == drow && a.kvl.bs == 64 * drow &&
                        (a.kv_kind == 1 || (a.kvl.srs == dsrow && a.kvl.sbs == 64 * dsrow));
-#define DSA_SFA(KV, D)                                                                                         \
-    hipLaunchKernelGGL((sfa_mla_kernel<KV, D>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,     \
+#define DSA_SFA(KV, D, TK)                                                                                      \
+    hipLaunchKernelGGL((sfa_mla_kernel<KV, D, TK>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,    \
                        (const uint8_t*)a.kv, a.kvscale, a.kvl, a.seq_lens, a.table, a.max_blocks, a.num_blocks, \
                        a.n_q, a.max_seq_len, rows, a.indices, a.top_k, per, splits, scale_log2,              \
-                       (uint16_t*)a.out, a.lse, ws_o, ws_lse)
-    if (a.kv_kind == 3) {
-        if (dense) DSA_SFA(3, true); else DSA_SFA(3, false);
+                       (uint16_t*)a.out, a.lse, ws_o, ws_lse, a.scores, a.ld)
+    if (a.scores != nullptr) {  // fused Top-K (attn_fuses_topk holds)
+        if (a.kv_kind == 3) DSA_SFA(3, true, kFusedTopkKpt);
+        else if (a.kv_kind == 2) DSA_SFA(2, true, kFusedTopkKpt);
+        else DSA_SFA(1, true, kFusedTopkKpt);
+    } else if (a.kv_kind == 3) {
+        if (dense) DSA_SFA(3, true, 0); else DSA_SFA(3, false, 0);
     } else if (a.kv_kind == 2) {
-        if (dense) DSA_SFA(2, true); else DSA_SFA(2, false);
+        if (dense) DSA_SFA(2, true, 0); else DSA_SFA(2, false, 0);
     } else {
-        if (dense) DSA_SFA(1, true); else DSA_SFA(1, false);
+        if (dense) DSA_SFA(1, true, 0); else DSA_SFA(1, false, 0);
     }
 #undef DSA_SFA
     hipError_t e = hipGetLastError();

@@ -132,6 +132,28 @@ def test_empty_histories_and_absent_blocks():
     assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
 
 
+@pytest.mark.parametrize("cfg", [2, 6])
+def test_forward_with_the_topk_in_the_attention_matches_the_separate_calls(cfg):
+    # dsa_forward selects each row's Top-K inside the attention kernel when the
+    # rows are at most 8192 positions long and few: histories just below, at
+    # and above top_k (the whole history, then a selection), the 8192 limit
+    # and none; 22 splits of 96 slots, so every workgroup keeps
+    # a narrow range of the row's places.  Indices, outputs and LSEs must equal
+    # the three separate calls bit for bit.
+    wl = make_workload(cfg, batch=6, lens=[2047, 2048, 2049, 8192, 1, 5000], top_k=2048, poison=True)
+    wl.seq_lens = wl.seq_lens.copy()
+    wl.seq_lens[4] = 0
+    _, sc, idx, out, lse = gpu_all(wl)
+    dev = B.DeviceInputs(wl)
+    say(f"[parity] fused Top-K forward, cfg {cfg}")
+    out2, lse2, idx2 = B.dsa_forward(dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx2.cpu().numpy(), idx)
+    assert np.array_equal(f64(out2), out) and np.array_equal(f64(lse2), lse)
+    check_indices_exact(idx, O.topk(sc, wl.row_lens(), wl.top_k))
+    assert (idx[4] == -1).all() and (idx[0][:2047] == np.arange(2047)).all() and idx[0][2047] == -1
+
+
 @pytest.mark.parametrize("cfg", [2, 5])
 def test_attention_history_too_long_for_the_table_in_lds(cfg):
     # A 470000-position history: 7344 table blocks, more than the 7168 whose
