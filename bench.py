@@ -70,17 +70,26 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-# kernels of each stage, by name, as rocprofv3 reports them
+# kernels of each stage, by name, as rocprofv3 reports them; the attention
+# kernel's fused form (it selects the Top-K too, template argument TK != 0,
+# run by dsa_forward) is not the attention stage's
 STAGE_KERNELS = {"indexer": ("indexer_f32_kernel", "indexer_decode_kernel", "indexer_prefill_kernel"),
                  "topk": ("topk_",), "attention": ("sfa_",), "prolog": ("indexer_prolog_kernel",)}
+STAGE_EXCLUDE = {"attention": (", 16>",)}
+
+
+def stage_kernel(stage: str, name: str) -> bool:
+    return any(t in name for t in STAGE_KERNELS[stage]) and not any(x in name for x in STAGE_EXCLUDE.get(stage, ()))
 COPY_KERNEL = "neg_kernel"  # the plain copy used to calibrate the byte counters
 
 KERNEL_SOURCES = {
     "indexer": ["sparse_attention_lightningindexer_amd/csrc/indexer.hip",
                 "sparse_attention_lightningindexer_amd/csrc/common.hpp"],
     "topk": ["sparse_attention_lightningindexer_amd/csrc/topk.hip",
+             "sparse_attention_lightningindexer_amd/csrc/select.hpp",
              "sparse_attention_lightningindexer_amd/csrc/common.hpp"],
     "attention": ["sparse_attention_lightningindexer_amd/csrc/sfa.hip",
+                  "sparse_attention_lightningindexer_amd/csrc/select.hpp",
                   "sparse_attention_lightningindexer_amd/csrc/common.hpp"],
     "prolog": ["sparse_attention_lightningindexer_amd/csrc/prolog.hip",
                "sparse_attention_lightningindexer_amd/csrc/common.hpp"],
@@ -132,7 +141,7 @@ def traffic_summary(stage: str, workload: str, fetch_dir: str, write_dir: str, c
         if not cal:
             raise SystemExit(f"the calibration copy ({COPY_KERNEL}) is missing from the {what} run")
         factor = copy_bytes / (cal[0][0] * 1024.0)
-        ks = {k: v for k, v in table.items() if any(t in k for t in STAGE_KERNELS[stage])}
+        ks = {k: v for k, v in table.items() if stage_kernel(stage, k)}
         if not ks:
             raise SystemExit(f"no {stage} kernels in the {what} run")
         raw = sum(v[0] for v in ks.values()) * 1024.0

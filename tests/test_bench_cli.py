@@ -36,3 +36,14 @@ def test_prolog_bytes_count_every_operand_once():
     nb = bench.prolog_bytes(32, 7168, 64, 128, mx=False)
     assert nb == 2 * (8192 + 64) * 7168 + 2 * 32 * 7168 + 2 * 32 * 128 + 4 * 128 + 32 * 8192 * 2 + 4 * 32 * 64 + 2 * 32 * 128
     assert bench.prolog_bytes(32, 7168, 64, 128, mx=True) == nb - 32 * 8192 + 32 * 256
+
+
+def test_the_attention_stage_leaves_out_the_fused_topk_form():
+    """The attention stage's counters take the unfused attention kernels and the
+    split merge; dsa_forward's fused form (which selects the Top-K too) is not
+    the attention stage."""
+    import bench
+    assert bench.stage_kernel("attention", "void dsa::sfa_mla_kernel<1, true, 0>(unsigned short const*)")
+    assert bench.stage_kernel("attention", "dsa::sfa_combine_kernel(unsigned short const*, float const*)")
+    assert not bench.stage_kernel("attention", "void dsa::sfa_mla_kernel<1, true, 16>(unsigned short const*)")
+    assert bench.stage_kernel("topk", "void dsa::topk_reg_kernel<8>(float const*, long)")
