@@ -227,9 +227,12 @@ size_t dsa_forward_workspace_bytes(const dsa_batch* batch, const dsa_indexer_arg
  * dsa_forward -- the whole stage: scoring -> weighting -> Top-K -> sparse
  * attention ([A] §4 "Indexer fusion" and its illustrative pipeline
  * fused_indexer then sfa; [D] §4.1).  The result equals dsa_indexer_scores,
- * then dsa_topk, then dsa_sparse_attn on the same inputs, bit for bit.
- * indices_out: device int32 [rows][top_k] receiving the selected positions,
- * or NULL.  Errors: as the three calls, plus WORKSPACE.
+ * then dsa_topk, then dsa_sparse_attn on the same inputs, bit for bit.  For
+ * a few rows of at most 8192 positions (decode batches) the attention
+ * launch selects the Top-K itself, so the stage is two launches plus the
+ * split merge; otherwise the three run in turn.  indices_out: device int32
+ * [rows][top_k] receiving the selected positions, or NULL.  Errors: as the
+ * three calls, plus WORKSPACE.
  */
 dsa_status dsa_forward(const dsa_batch* batch, const dsa_indexer_args* idx,
                        const dsa_attn_args* attn, int32_t top_k, int32_t* indices_out,
