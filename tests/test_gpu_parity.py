@@ -132,6 +132,21 @@ def test_empty_histories_and_absent_blocks():
     assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
 
 
+def test_forward_with_the_topk_in_the_attention_at_256_rows():
+    # 256 rows (64 sequences x 4 query tokens), the most the fused form takes:
+    # one split per row, so each workgroup keeps all top_k places and its
+    # head-half-0 workgroup writes the whole index row.
+    wl = make_workload(2, batch=64, n_q=4, lens=[3000 + 37 * b for b in range(64)], top_k=2048)
+    _, sc, idx, out, lse = gpu_all(wl)
+    dev = B.DeviceInputs(wl)
+    say("[parity] fused Top-K forward, 256 rows")
+    out2, lse2, idx2 = B.dsa_forward(dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx2.cpu().numpy(), idx)
+    assert np.array_equal(f64(out2), out) and np.array_equal(f64(lse2), lse)
+    check_indices_exact(idx, O.topk(sc, wl.row_lens(), wl.top_k))
+
+
 @pytest.mark.parametrize("cfg", [2, 6])
 def test_forward_with_the_topk_in_the_attention_matches_the_separate_calls(cfg):
     # dsa_forward selects each row's Top-K inside the attention kernel when the
