@@ -767,6 +767,15 @@ int attn_splits(int rows, int top_k, int Dqk) {
     return s < 1 ? 1 : s;
 }
 
+// The latent pool (and its scales) in the dense layout of its format, in
+// bytes: rows, blocks, scale rows, scale blocks.
+static bool dense_pool(const AttnLaunch& a) {
+    const int64_t drow = a.kv_kind == 1 ? kRowB : kDqk;
+    const int64_t dsrow = a.kv_kind == 2 ? kDqk / 32 : a.kv_kind == 3 ? 5 * 4 : 0;
+    return a.kvl.rs == drow && a.kvl.bs == 64 * drow &&
+           (a.kv_kind == 1 || (a.kvl.srs == dsrow && a.kvl.sbs == 64 * dsrow));
+}
+
 int attn_per_split(int top_k, int splits) {
     const int nchunks = (top_k + kCh - 1) / kCh;
     return ((nchunks + splits - 1) / splits) * kCh;
@@ -782,10 +791,7 @@ int attn_per_split(int top_k, int splits) {
 bool attn_fuses_topk(const AttnLaunch& a) {
     if (a.q_dtype == 0 || a.Dqk != kDqk || a.H != kH || a.Dv != kDv) return false;
     if (a.max_seq_len > kThreads * kFusedTopkKpt || (int64_t)a.batch * a.n_q > 256) return false;
-    const int64_t drow = a.kv_kind == 1 ? kRowB : kDqk;
-    const int64_t dsrow = a.kv_kind == 2 ? kDqk / 32 : a.kv_kind == 3 ? 5 * 4 : 0;
-    return a.kvl.rs == drow && a.kvl.bs == 64 * drow &&
-           (a.kv_kind == 1 || (a.kvl.srs == dsrow && a.kvl.sbs == 64 * dsrow));
+    return dense_pool(a);
 }
 
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st) {
@@ -805,11 +811,7 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t st) {
     const float scale_log2 = a.sm_scale * kLog2e;
     uint16_t* ws_o = (uint16_t*)a.ws;
     float* ws_lse = splits == 1 ? nullptr : (float*)(ws_o + (size_t)rows * splits * kH * kDv);
-    // the dense layout of each format, in bytes: rows, blocks, scale rows, scale blocks
-    const int64_t drow = a.kv_kind == 1 ? kRowB : kDqk;
-    const int64_t dsrow = a.kv_kind == 2 ? kDqk / 32 : a.kv_kind == 3 ? 5 * 4 : 0;
-    const bool dense = a.kvl.rs == drow && a.kvl.bs == 64 * drow &&
-                       (a.kv_kind == 1 || (a.kvl.srs == dsrow && a.kvl.sbs == 64 * dsrow));
+    const bool dense = dense_pool(a);
 #define DSA_SFA(KV, D, TK)                                                                                      \
     hipLaunchKernelGGL((sfa_mla_kernel<KV, D, TK>), dim3(grid), dim3(kThreads), 0, st, (const uint16_t*)a.q,    \
                        (const uint8_t*)a.kv, a.kvscale, a.kvl, a.seq_lens, a.table, a.max_blocks, a.num_blocks, \
