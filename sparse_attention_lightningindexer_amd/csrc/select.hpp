@@ -27,16 +27,18 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // slots -- one coalesced load, and one ballot is the column's bit mask.  Key 0
 // marks an empty slot.  The MSB-first radix select uses digits of 12, 10 and
 // 10 bits (one LDS histogram per pass, bins owned by threads for the suffix
-// scan) and finds the k-th largest key T and the number of keys equal to T to
+// scan; the later passes are skipped once a cut bin holds exactly the keys
+// still needed) and finds the cut key T and the number of keys equal to T to
 // keep.  The histogram is all zero on entry (clear_hist, once per workgroup)
-// and is left so.  The column masks of the keys > T and == T go to LDS as 64-bit words
-// in slot order; thread t then takes slots KPT*t .. KPT*t + KPT - 1, and one
-// block scan of its counts gives every kept slot its output place, the lowest
-// slots first among equal keys.  emit(place, slot) writes a kept slot.  Exactly top_k slots
-// are kept (callers guarantee that at least top_k slots are not empty).  Empty
-// slots are left out of the first histogram only to spare one bin the atomic
-// traffic; the later passes and the final comparisons need no test, since
-// key 0 lies below the cut.
+// and is left so.  The emit goes column by column: a kept slot's place is the
+// number of kept slots before it, the keys > T before it plus min(keys == T
+// before it, the number to keep), so the lowest slots come first among equal
+// keys; the waves' totals go through one block scan and a column's lanes
+// count with mbcnt.  emit(place, q, slot) writes a kept slot.  Exactly top_k
+// slots are kept (callers guarantee that at least top_k slots are not empty).
+// Empty slots are left out of the first histogram only to spare one bin the
+// atomic traffic; the later passes and the final comparisons need no test,
+// since key 0 lies below the cut.
 template <int NT>
 struct SelectShared {
     uint32_t hist[4096];
