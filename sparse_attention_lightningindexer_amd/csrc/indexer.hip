@@ -304,13 +304,13 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
 }
 
 // Prefill (many query rows per sequence): 8 waves x 2 rows = 16 rows per row
-// block; the block's K tiles are gathered straight into a 4-deep LDS ring and
-// shared by all 16 rows.  Causal load skew is balanced by pairing row block x
+// block; the block's K tiles are gathered straight into a 6-tile LDS ring and
+// shared by all 16 rows, scored two tiles per barrier.  Causal load skew is balanced by pairing row block x
 // with row block NB-1-x in one workgroup, the head-tail pairing the pages use
 // across devices ("Day0 Inference Adaptation and Performance Optimization for
 // New-Architecture LLMs", §6.2 Zigzag Layout), applied here across the GPU's
 // compute units.  grid (ceil(NB/2), batch), block 512.
-constexpr int kIdxRing = 4;
+constexpr int kIdxRing = 6;
 
 template <class T>
 __global__ __launch_bounds__(512) void indexer_prefill_kernel(
@@ -324,7 +324,6 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t ktile[kIdxRing][TILE_BYTES];
     // fp8: the scale of each position of the tile; MXFP8: its four E8M0 bytes (k-blocks 0..3)
     __shared__ __attribute__((aligned(16))) float kst[kIdxRing][kBlock];
-    __shared__ int tile_ok[kIdxRing];
 
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
@@ -344,7 +343,9 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
     // Raw block-table entries of tiles 64m .. 64m+63, gathered by each wave
     // into its own LDS window (clamped columns; validated when used).  Window
     // m+1 is gathered when tile 64m is staged, 64 tiles before it is needed;
-    // the tile waits cover it, since operations complete in order.
+    // the tile waits cover it, since operations complete in order.  When tile
+    // 64m is staged the wave also reads window m into a register (lane l holds
+    // tile 64m + l), so each later tile's entry is one lane read.
     __shared__ int tabw[8][2][kWave];
     auto tab_fetch = [&](int m) __attribute__((always_inline)) {
         const int j_ = min(kWave * m + lane, max_blocks - 1);
@@ -354,20 +355,35 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
 
     // Gather tile t into ring slot `buf`: unit U of the tile (row U/UNITS, column
     // U%UNITS) receives global column (U%UNITS) ^ (row % UNITS), an XOR swizzle
-    // that keeps the column reads below bank-conflict free.  Absent blocks read
-    // block 0 and are flagged; their scores are -inf.
+    // that keeps the column reads below bank-conflict free.  The wave gathers
+    // units U = 64k + lane for k = wave, wave + 8, at the same offsets in every
+    // tile.  Absent blocks read block 0 and are flagged in a bit mask that
+    // every wave keeps alike (each stages every tile); their scores are -inf.
+    constexpr int KPW = (TILE_K + 7) / 8;
+    int64_t goff[KPW];
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+        const int U = (wave + 8 * i) * kWave + lane;
+        const int row = U / UNITS, col = (U % UNITS) ^ (row % UNITS);
+        goff[i] = row * kl.rs + col * 16;
+    }
+    int win = 0;        // the table window of the tiles being staged
+    uint32_t okm = 0u;  // bit s: ring slot s holds a present block
     auto stage = [&](int t, int buf) __attribute__((always_inline)) {
-        if ((t & 63) == 0) tab_fetch((t >> 6) + 1);
-        int64_t p = tabw[wave][(t >> 6) & 1][t & 63];
+        if ((t & 63) == 0) {
+            tab_fetch((t >> 6) + 1);
+            win = tabw[wave][(t >> 6) & 1][lane];
+        }
+        int64_t p = __builtin_amdgcn_readlane(win, t & 63);
         if (t >= max_blocks || p < 0 || p >= num_blocks) p = -1;  // absent block
-        if (threadIdx.x == 0) tile_ok[buf] = p >= 0;
+        okm = (okm & ~(1u << buf)) | ((p >= 0 ? 1u : 0u) << buf);
         if (p < 0) p = 0;
         const uint8_t* base = kpool + p * kl.bs;
         const uint32_t dst = lds_addr(&ktile[buf][0]);
-        for (int k = wave; k < TILE_K; k += 8) {
-            const int U = k * kWave + lane;
-            const int row = U / UNITS, col = (U % UNITS) ^ (row % UNITS);
-            lds_gather16(base + row * kl.rs + col * 16, dst + k * kWave * 16);
+#pragma unroll
+        for (int i = 0; i < KPW; ++i) {
+            const int k = wave + 8 * i;
+            if (k < TILE_K) lds_gather16(base + goff[i], dst + k * kWave * 16);
         }
         if constexpr (kScaleLine) {  // one dword per position: the fp32 scale or the four E8M0 bytes
             if (wave == 0)
@@ -400,32 +416,38 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
             tab_fetch(0);
             wait_vmcnt<0>();
         }
-        // mark0..2: `issued` right after the gathers of tiles t, t+1, t+2
-        int mark0 = issued, mark1 = issued, mark2 = issued;
-        static_assert(kIdxRing == 4, "three tiles are in flight ahead of the one scored");
-        if (ntiles > 0) { stage(0, 0); mark0 = issued; }
-        if (ntiles > 1) { stage(1, 1); mark1 = issued; }
-        if (ntiles > 2) { stage(2, 2); mark2 = issued; }
-        for (int t = 0; t < ntiles; ++t) {
-            const int buf = t % kIdxRing;
-            wait_vmcnt(issued - mark0);  // tile t has landed (operations complete in order)
-            sync_lds();  // ... for every wave; slot (t-1) % 4 is free
-            if (t + kIdxRing - 1 < ntiles) stage(t + kIdxRing - 1, (t + kIdxRing - 1) % kIdxRing);
-            mark0 = mark1;
-            mark1 = mark2;
-            mark2 = issued;
-            const int s0 = t * kBlock;
-            const bool ok = tile_ok[buf] != 0;
-            if (s0 < Lr[0] || s0 < Lr[1]) {
-                // eight steps k = (N-tile k/2, row k%2): 16 MFMAs, then the
+        // Tiles are scored in pairs (t, t+1), t even, with one wait and one
+        // barrier per pair; the two pairs after it are in flight meanwhile.
+        // markA: `issued` right after the gathers of the pair scored next;
+        // markB: of the pair after it.
+        static_assert(kIdxRing == 6, "two pairs of tiles are in flight ahead of the pair scored");
+        if (ntiles > 0) stage(0, 0);
+        if (ntiles > 1) stage(1, 1);
+        int markA = issued;
+        if (ntiles > 2) stage(2, 2);
+        if (ntiles > 3) stage(3, 3);
+        int markB = issued;
+        for (int t = 0; t < ntiles; t += 2) {
+            wait_vmcnt(issued - markA);  // tiles t and t+1 have landed (operations complete in order)
+            sync_lds();  // ... for every wave; the slots of tiles t-2 and t-1 are free
+            if (t + 4 < ntiles) stage(t + 4, (t + 4) % kIdxRing);
+            if (t + 5 < ntiles) stage(t + 5, (t + 5) % kIdxRing);
+            markA = markB;
+            markB = issued;
+            // tiles of the pair that this wave scores: none, t, or t and t+1
+            const int Lw = max(Lr[0], Lr[1]);
+            const int ntw = t * kBlock >= Lw ? 0 : (t + 1 < ntiles && (t + 1) * kBlock < Lw ? 2 : 1);
+            if (ntw > 0) {
+                // per tile eight steps k = (N-tile k/2, row k%2): 16 MFMAs, then the
                 // ReLU-weighted head sum (VALU).  A wave's own MFMAs and VALU
                 // work do not overlap; waves w and w+4 share a SIMD, and waves
-                // 4..7 run each step's sum one step late, so that one wave's
-                // sum runs under the other's MFMAs.  MFMA steps run at raised
-                // wave priority, so the matrix core is fed first.
+                // 4..7 run each step's sum one step late (across the two tiles
+                // of the pair), so that one wave's sum runs under the other's
+                // MFMAs.  MFMA steps run at raised wave priority, so the matrix
+                // core is fed first.
                 typename T::frag kf[2][T::KSTEPS];
                 int ksx[2];  // MXFP8: E8M0 scale of position 16nt + j, k-block g
-                auto read_k = [&](int nt, typename T::frag (&f)[T::KSTEPS], int& kx) __attribute__((always_inline)) {
+                auto read_k = [&](int buf, int nt, typename T::frag (&f)[T::KSTEPS], int& kx) __attribute__((always_inline)) {
                     const int prow = 16 * nt + j;
                     const uint8_t* rowp = &ktile[buf][prow * T::ROW];
                     kx = T::MX ? (int)reinterpret_cast<const uint8_t*>(&kst[buf][0])[prow * 4 + g] : 127;
@@ -442,12 +464,12 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
                         }
                     }
                 };
-                auto mfma_step = [&](int k, f32x4 (&acc)[4]) __attribute__((always_inline)) {
+                auto mfma_step = [&](int u, int k, f32x4 (&acc)[4]) __attribute__((always_inline)) {
                     __builtin_amdgcn_sched_barrier(0);
                     __builtin_amdgcn_s_setprio(2);
                     __builtin_amdgcn_sched_barrier(0);
                     const int nt = k >> 1, qi = k & 1;
-                    if (qi == 0) read_k(nt, kf[nt & 1], ksx[nt & 1]);
+                    if (qi == 0) read_k((t + u) % kIdxRing, nt, kf[nt & 1], ksx[nt & 1]);
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) {
                         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -469,31 +491,59 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
                     else
                         sel0 = g == (k >> 1) ? v : sel0;
                 };
+                // one 256-byte store per row: lane l scores position s0 + l
+                auto store = [&](int u) __attribute__((always_inline)) {
+                    const int tt = t + u, buf = tt % kIdxRing, s0 = tt * kBlock;
+                    const bool ok = (okm >> buf) & 1u;
+#pragma unroll
+                    for (int qi = 0; qi < 2; ++qi) {
+                        float v = qi ? sel1 : sel0;
+                        if constexpr (T::SCALED) v *= kst[buf][lane];
+                        if (!ok) v = -INFINITY;
+                        const int64_t row = (int64_t)b * n_q + rb * 16 + wave * 2 + qi;
+                        if (s0 + lane < Lr[qi]) scores[row * ld + s0 + lane] = v;
+                        issued += s0 < Lr[qi];  // the store issues when lane 0 is active
+                    }
+                };
                 f32x4 acc[2][4];
                 if (wave < 4) {
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        mfma_step(k, acc[0]);
-                        sum_step(k, acc[0]);
+                    for (int u = 0; u < 2; ++u) {
+                        if (u < ntw) {
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) {
+                                mfma_step(u, k, acc[0]);
+                                sum_step(k, acc[0]);
+                            }
+                            store(u);
+                        }
                     }
                 } else {
-                    mfma_step(0, acc[0]);
+                    // the first tile's stores wait for the second tile's
+                    // second MFMA step, where no K fragments are held
+                    mfma_step(0, 0, acc[0]);
 #pragma unroll
                     for (int k = 1; k < 8; ++k) {
-                        mfma_step(k, acc[k & 1]);
+                        mfma_step(0, k, acc[k & 1]);
                         sum_step(k - 1, acc[(k - 1) & 1]);
                     }
-                    sum_step(7, acc[1]);
-                }
-                // one 256-byte store per row: lane l scores position s0 + l
+                    if (ntw == 2) {
+                        mfma_step(1, 0, acc[0]);
+                        sum_step(7, acc[1]);
+                        mfma_step(1, 1, acc[1]);
+                        store(0);
+                        sum_step(0, acc[0]);
 #pragma unroll
-                for (int qi = 0; qi < 2; ++qi) {
-                    float v = qi ? sel1 : sel0;
-                    if constexpr (T::SCALED) v *= kst[buf][lane];
-                    if (!ok) v = -INFINITY;
-                    const int64_t row = (int64_t)b * n_q + rb * 16 + wave * 2 + qi;
-                    if (s0 + lane < Lr[qi]) scores[row * ld + s0 + lane] = v;
-                    issued += s0 < Lr[qi];  // the store issues when lane 0 is active
+                        for (int k = 2; k < 8; ++k) {
+                            mfma_step(1, k, acc[k & 1]);
+                            sum_step(k - 1, acc[(k - 1) & 1]);
+                        }
+                        sum_step(7, acc[1]);
+                        store(1);
+                    } else {
+                        sum_step(7, acc[1]);
+                        store(0);
+                    }
                 }
             }
         }
