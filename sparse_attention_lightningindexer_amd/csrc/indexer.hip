@@ -565,22 +565,34 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
         return hipGetLastError();
     }
     if (a.n_q <= 2) {
-        // one row: 8 waves x 2 tiles (both in flight, two waves per SIMD); two
-        // rows need more registers: 4 waves x 4 tiles, two in flight
+        // 4 waves per workgroup, each streaming TPW consecutive tiles with two
+        // in flight.  One row: the longest run that still gives 256
+        // workgroups, up to 8 tiles of fp8 keys (8 KB each) or 4 of bf16 (16
+        // KB).  Two rows (more registers): 4 tiles.
         const int tiles = (a.max_seq_len + kBlock - 1) / kBlock;
+        int tpw = 4;
+        if (a.n_q == 1) {
+            tpw = a.dtype == 1 ? 4 : 8;
+            while (tpw > 2 && (int64_t)((tiles + 4 * tpw - 1) / (4 * tpw)) * a.batch < 256) tpw /= 2;
+        }
 #define DSA_DEC(T, NQ, TPW, NW)                                                                  \
     hipLaunchKernelGGL((indexer_decode_kernel<T, NQ, TPW, NW>),                                  \
                        dim3((tiles + NW * TPW - 1) / (NW * TPW), a.batch), dim3(64 * NW), 0, st, \
                        (const uint8_t*)a.q, a.q_scale, a.w, (const uint8_t*)a.kpool, a.kscale,   \
                        a.kl, a.seq_lens, a.table, a.max_blocks, a.num_blocks, a.n_q, a.max_seq_len, \
                        a.scores, a.ld)
+#define DSA_DEC1(T)                               \
+    if (tpw == 8) DSA_DEC(T, 1, 8, 4);            \
+    else if (tpw == 4) DSA_DEC(T, 1, 4, 4);       \
+    else DSA_DEC(T, 1, 2, 4);
         if (a.dtype == 2) {
-            if (a.n_q == 1) DSA_DEC(IdxFp8, 1, 2, 8); else DSA_DEC(IdxFp8, 2, 4, 4);
+            if (a.n_q == 1) { DSA_DEC1(IdxFp8) } else DSA_DEC(IdxFp8, 2, 4, 4);
         } else if (a.dtype == 3) {
-            if (a.n_q == 1) DSA_DEC(IdxMx, 1, 2, 8); else DSA_DEC(IdxMx, 2, 4, 4);
+            if (a.n_q == 1) { DSA_DEC1(IdxMx) } else DSA_DEC(IdxMx, 2, 4, 4);
         } else {
-            if (a.n_q == 1) DSA_DEC(IdxBf16, 1, 2, 8); else DSA_DEC(IdxBf16, 2, 4, 4);
+            if (a.n_q == 1) { DSA_DEC1(IdxBf16) } else DSA_DEC(IdxBf16, 2, 4, 4);
         }
+#undef DSA_DEC1
 #undef DSA_DEC
         return hipGetLastError();
     }

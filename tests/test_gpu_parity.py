@@ -326,6 +326,24 @@ def test_full_size_every_row(cfg):
     check_attention(wl, f64(out), f64(lse), ref_o, ref_l, f"full cfg {cfg}")
 
 
+@pytest.mark.parametrize("cfg,batch,L", [(2, 32, 8192), (5, 64, 16384), (6, 64, 16384)])
+def test_decode_indexer_long_wave_runs_with_ragged_lengths(cfg, batch, L):
+    # One query row per sequence at the decode workloads' sizes, where each
+    # indexer wave streams a run of 4 (bf16) or 8 (fp8, MXFP8) tiles.  Lengths
+    # step down by 37 per sequence, so histories end inside tiles and inside
+    # runs, and with permuted paging every table entry of a run matters.
+    lens = [L - 37 * b for b in range(batch)]
+    wl = make_workload(cfg, batch=batch, n_q=1, lens=lens, top_k=256, paging="permuted", poison=True)
+    dev = B.DeviceInputs(wl)
+    say(f"[parity] decode indexer runs, cfg {cfg}, batch {batch}: scores on GPU")
+    sc = B.dsa_indexer_scores(dev)
+    torch.cuda.synchronize()
+    rows = sorted(set(range(0, batch, 5)) | {batch - 1})
+    sc_h = sc[rows].cpu().numpy().astype(np.float64)
+    ref_sc = O.indexer_scores(wl, rows, ld=sc.shape[1])
+    check_scores(wl, sc_h, ref_sc, rows)
+
+
 @pytest.mark.parametrize("cfg", [3, 5, 6])
 def test_prefill_permuted_paging_across_table_windows(cfg):
     # 4500 causal rows: the prefill indexer kernel reads the block table in
