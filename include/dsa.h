@@ -133,10 +133,12 @@ typedef struct {
 /* Indexer inputs ([D] §4.1 "Indexer Fusion": q_idx, paged K cache, head
  * weights; [D] §4.2: the head weights come from the head-weight projection). */
 typedef struct {
-    const void* q;              /* device [rows][n_heads][head_dim] in dtype       */
+    const void* q;              /* device [rows][n_heads][head_dim] in dtype;      */
+                                /*   BF16 and E4M3: 16-byte aligned                */
     dsa_dtype dtype;            /* F32, BF16 or E4M3; k.dtype must match           */
     const void* q_scale;        /* device, E4M3 only, same kind and group as k:    */
-                                /*   [rows][n_heads][head_dim/group] fp32 or E8M0  */
+                                /*   [rows][n_heads][head_dim/group] fp32 or E8M0, */
+                                /*   4-byte aligned                                */
     int32_t n_heads;            /* H_I                                             */
     int32_t head_dim;           /* d_I                                             */
     const float* head_w;        /* device [rows][n_heads] fp32                     */

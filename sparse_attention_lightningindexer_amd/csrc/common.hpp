@@ -116,16 +116,20 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-// wave-uniform n in [0, 31]
+// wave-uniform n in [0, 63] (the counter's range; a larger n waits for 63)
 __device__ __forceinline__ void wait_vmcnt(int n) {
     switch (n) {
 #define DSA_W(N) case N: wait_vmcnt<N>(); break;
     DSA_W(0) DSA_W(1) DSA_W(2) DSA_W(3) DSA_W(4) DSA_W(5) DSA_W(6) DSA_W(7)
     DSA_W(8) DSA_W(9) DSA_W(10) DSA_W(11) DSA_W(12) DSA_W(13) DSA_W(14) DSA_W(15)
     DSA_W(16) DSA_W(17) DSA_W(18) DSA_W(19) DSA_W(20) DSA_W(21) DSA_W(22) DSA_W(23)
-    DSA_W(24) DSA_W(25) DSA_W(26) DSA_W(27) DSA_W(28) DSA_W(29) DSA_W(30)
+    DSA_W(24) DSA_W(25) DSA_W(26) DSA_W(27) DSA_W(28) DSA_W(29) DSA_W(30) DSA_W(31)
+    DSA_W(32) DSA_W(33) DSA_W(34) DSA_W(35) DSA_W(36) DSA_W(37) DSA_W(38) DSA_W(39)
+    DSA_W(40) DSA_W(41) DSA_W(42) DSA_W(43) DSA_W(44) DSA_W(45) DSA_W(46) DSA_W(47)
+    DSA_W(48) DSA_W(49) DSA_W(50) DSA_W(51) DSA_W(52) DSA_W(53) DSA_W(54) DSA_W(55)
+    DSA_W(56) DSA_W(57) DSA_W(58) DSA_W(59) DSA_W(60) DSA_W(61) DSA_W(62)
 #undef DSA_W
-    default: wait_vmcnt<31>(); break;
+    default: wait_vmcnt<63>(); break;
     }
 }
 // Workgroup barrier for LDS data only (no wait on outstanding global loads).

@@ -88,6 +88,8 @@ dsa_status check_indexer(const dsa_batch* b, const dsa_indexer_args* a) {
     case DSA_BF16:
         if (a->n_heads != 64 || a->head_dim != 128) return DSA_ERR_UNSUPPORTED;
         if (a->k.scale_kind != DSA_SCALE_NONE) return DSA_ERR_UNSUPPORTED;
+        // queries arrive in 16-byte pieces, head weights in 4-byte ones
+        if ((uintptr_t)a->q % 16 != 0 || (uintptr_t)a->head_w % 4 != 0) return DSA_ERR_SHAPE;
         return DSA_OK;
     case DSA_E4M3:  // fp32 per 128 (one per head vector) or MXFP8 (E8M0 per 32)
         if (a->n_heads != 64 || a->head_dim != 128) return DSA_ERR_UNSUPPORTED;
@@ -95,6 +97,9 @@ dsa_status check_indexer(const dsa_batch* b, const dsa_indexer_args* a) {
               (a->k.scale_kind == DSA_SCALE_E8M0 && a->k.group == 32)))
             return DSA_ERR_UNSUPPORTED;
         if (a->k.scales == nullptr || (b->batch > 0 && a->q_scale == nullptr)) return DSA_ERR_NULL;
+        // queries in 16-byte pieces; head weights and a head's scale (fp32, or its four E8M0 bytes) in 4
+        if ((uintptr_t)a->q % 16 != 0 || ((uintptr_t)a->head_w | (uintptr_t)a->q_scale) % 4 != 0)
+            return DSA_ERR_SHAPE;
         if (a->k.scale_kind == DSA_SCALE_E8M0) {  // a position's four E8M0 bytes are read as one dword
             const dsa::PoolLayout L = layout_of(&a->k);
             if ((uintptr_t)a->k.scales % 4 != 0 || L.srs % 4 != 0 || L.sbs % 4 != 0) return DSA_ERR_SHAPE;

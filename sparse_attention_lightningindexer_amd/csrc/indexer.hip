@@ -154,18 +154,40 @@ __device__ __forceinline__ float head_weighted_relu_sum(const f32x4 (&acc)[4], c
 }
 
 // Decode: a sequence's n_q <= NQ rows share every K tile.  Each wave owns TPW
-// consecutive 64-position tiles of one sequence; their K fragments come
-// straight from HBM into registers (no reuse across waves), two tiles in
-// flight while the previous one is scored; the workgroup's NW waves share the
-// sequence's queries through LDS.  grid (ceil(tiles / (NW*TPW)), batch),
-// block 64*NW.
+// consecutive 64-position tiles of one sequence and streams them through two
+// LDS slots of its own, two tiles in flight while the previous one is scored.
+// Everything the kernel reads from global memory beyond the block table
+// arrives by DMA (global_load_lds), each instruction one contiguous 1 KB of
+// K (or of the queries): fragment loads straight from HBM touch half of 16
+// cache lines per instruction, and a plain read in that pattern stays near
+// 4 TB/s where contiguous 1 KB reads reach 5.5.  Being invisible to the
+// compiler's wait bookkeeping, the DMAs are waited for with hand-counted
+// waits; there are no compiler-visible vector loads, whose waits would also
+// drain the tiles in flight.  grid (ceil(tiles / (NW*TPW)), batch), block
+// 64*NW.
 template <class T, int NQ, int TPW, int NW>
 __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kpool, const void* __restrict__ kscale, PoolLayout kl,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks,
     int64_t num_blocks, int n_q, int max_seq_len, float* __restrict__ scores, int64_t ld) {
-    static_assert(NQ <= 2, "decode rows per sequence");
+    static_assert(NQ <= 2 && NQ <= NW, "decode rows per sequence");
+    constexpr int UNITS = T::ROW / 16;                  // 16-byte units per 128-element vector
+    constexpr int TILE_BYTES = kBlock * T::ROW;
+    constexpr int TILE_K = TILE_BYTES / (16 * kWave);   // 1 KB gathers per K tile (16 or 8)
+    constexpr int Q_K = NQ * kIdxHeads * T::ROW / (16 * kWave);  // 1 KB gathers of the queries
+    constexpr bool kScaleLine = T::SCALED || T::MX;
+    // Unit c of vector v (a query head row or a K position) sits at column
+    // c ^ (v % UNITS), an XOR swizzle that keeps the fragment reads free of
+    // bank conflicts.
+    __shared__ __attribute__((aligned(16))) uint8_t q_s[NQ * kIdxHeads * T::ROW];
+    __shared__ __attribute__((aligned(16))) float w_s[NQ][kIdxHeads];
+    // fp8: the query scale of each head; MXFP8: its four E8M0 bytes
+    __shared__ __attribute__((aligned(16))) float qsc_s[NQ][kIdxHeads];
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[NW][2][TILE_BYTES];
+    // fp8: the scale of each position of the tile; MXFP8: its four E8M0 bytes
+    __shared__ __attribute__((aligned(16))) float kst[NW][2][kBlock];
+
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: the table reads are scalar
@@ -174,57 +196,36 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
     if ((int)blockIdx.x * NW * TPW * kBlock >= Lb) return;  // block-uniform
     const int tile0 = (blockIdx.x * NW + wave) * TPW;
 
-    // Memory round trips before the first K tile: the block-table entries
-    // (the K addresses depend on them) are read first, then the query units
-    // are loaded into registers; the K loads issue as soon as the table
-    // entries arrive, and the query goes to LDS (padded rows keep the 16-row
-    // fragment reads conflict free) while the K tiles are in flight.
-    int32_t traw[TPW];  // raw table entries; checked once the later loads are issued
+    // Round trips before the first K tile: the block-table entries (scalar
+    // loads; the K addresses depend on them) and, at the same time, the
+    // queries, head weights and query scales (DMA, shared by the waves).
+    int32_t traw[TPW];  // raw table entries; checked once they have arrived
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int t = tile0 + u;
         traw[u] = table[(int64_t)b * max_blocks + (t < max_blocks ? t : 0)];  // unconditional read
     }
     __builtin_amdgcn_sched_barrier(0);  // the table reads issue first
-    constexpr int QROW = T::ROW + 16;
-    constexpr int QUNITS = NQ * kIdxHeads * T::ROW / 16;
-    constexpr int QPER = (QUNITS + 64 * NW - 1) / (64 * NW);  // query units per thread
-    __shared__ __attribute__((aligned(16))) uint8_t q_s[NQ * kIdxHeads * QROW];
-    i32x4 qunit[QPER];
-    auto q_unit = [&](int k, int& hr, int& c) {
-        const int u = min((int)threadIdx.x + 64 * NW * k, QUNITS - 1);  // unconditional: one batch of loads
-        hr = u / (T::ROW / 16);                                          // head row qi*64 + h
-        c = u % (T::ROW / 16);                                           // 16-byte unit of the row
-    };
-#pragma unroll
-    for (int k = 0; k < QPER; ++k) {
-        int hr, c;
-        q_unit(k, hr, c);
-        const int qi = hr / kIdxHeads;
+    int issued = 0;  // vector-memory operations this wave has issued (uniform)
+    for (int k = wave; k < Q_K; k += NW) {
+        const int U = k * kWave + lane;
+        const int v = U / UNITS, col = (U % UNITS) ^ (v % UNITS);
+        const int qi = v / kIdxHeads;
         const int64_t rr = (int64_t)b * n_q + (qi < n_q ? qi : 0);
-        qunit[k] = *reinterpret_cast<const i32x4*>(q + (rr * kIdxHeads + hr % kIdxHeads) * (int64_t)T::ROW + 16 * c);
+        lds_gather16(q + (rr * kIdxHeads + v % kIdxHeads) * (int64_t)T::ROW + col * 16, lds_addr(q_s) + k * kWave * 16);
+        ++issued;
     }
-    // head weights (and query scales), also before the K tiles
-    float wr[NQ][4][4];
-    int qsx[NQ][4];  // MXFP8: E8M0 scale of head 16mt + j, k-block g
-#pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
-        const bool valid = qi < n_q;
-        const int64_t rr = (int64_t)b * n_q + (valid ? qi : 0);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            qsx[qi][mt] = T::MX ? (int)static_cast<const uint8_t*>(q_scale)[(rr * kIdxHeads + 16 * mt + j) * 4 + g]
-                                : 127;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int h = 16 * mt + 4 * g + i;
-                float x = w[rr * kIdxHeads + h];
-                if constexpr (T::SCALED) x *= static_cast<const float*>(q_scale)[rr * kIdxHeads + h];
-                wr[qi][mt][i] = valid ? x : 0.f;
-            }
+    if (wave < NQ) {  // wave qi brings row qi's head weights and query scales
+        const int64_t rr = (int64_t)b * n_q + (wave < n_q ? wave : 0);
+        lds_gather4(w + rr * kIdxHeads + lane, lds_addr(&w_s[wave][0]));
+        ++issued;
+        if constexpr (kScaleLine) {
+            lds_gather4(static_cast<const uint8_t*>(q_scale) + (rr * kIdxHeads + lane) * 4, lds_addr(&qsc_s[wave][0]));
+            ++issued;
         }
     }
-    __builtin_amdgcn_sched_barrier(0);  // the loads above issue before the table entries are used
+    const int markQ = issued;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) asm volatile("" ::"s"(traw[u]));  // all entries arrive in one round trip
     int64_t pt[TPW];
@@ -234,72 +235,123 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
         const int64_t p = traw[u];
         pt[u] = (t * kBlock < Lb && t < max_blocks && p >= 0 && p < num_blocks) ? p : -1;
     }
-    typename T::frag kf[2][4][T::KSTEPS];
-    float ksc[2][4];  // fp8: the position's scale; MXFP8: its E8M0 byte of k-block g (as bits)
-    auto load_tile = [&](int u, typename T::frag (&f)[4][T::KSTEPS], float (&sc)[4]) {
-        const int64_t p = pt[u] < 0 ? 0 : pt[u];
+
+    auto gather = [&](int u, int slot) __attribute__((always_inline)) {
+        const int64_t p = pt[u] < 0 ? 0 : pt[u];  // an absent block reads block 0 (its scores are -inf)
+        const uint8_t* base = kpool + p * kl.bs;
+        const uint32_t dst = lds_addr(&ktile[wave][slot][0]);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {  // an absent block reads block 0 (its scores are -inf)
-            const uint8_t* v = kpool + p * kl.bs + (16 * nt + j) * kl.rs;
-#pragma unroll
-            for (int ks = 0; ks < T::KSTEPS; ++ks) f[nt][ks] = load_frag<T>(v, ks, g);
-            const uint8_t* sp = static_cast<const uint8_t*>(kscale) + p * kl.sbs + (16 * nt + j) * kl.srs;
-            if constexpr (T::SCALED) sc[nt] = *reinterpret_cast<const float*>(sp);
-            if constexpr (T::MX) sc[nt] = __int_as_float(sp[g]);
+        for (int k = 0; k < TILE_K; ++k) {
+            const int U = k * kWave + lane;
+            const int row = U / UNITS, col = (U % UNITS) ^ (row % UNITS);
+            lds_gather16(base + row * kl.rs + col * 16, dst + k * kWave * 16);
         }
+        if constexpr (kScaleLine)  // one dword per position: the fp32 scale or the four E8M0 bytes
+            lds_gather4(static_cast<const uint8_t*>(kscale) + p * kl.sbs + lane * kl.srs,
+                        lds_addr(&kst[wave][slot][0]));
+        issued += TILE_K + (kScaleLine ? 1 : 0);
     };
-    load_tile(0, kf[0], ksc[0]);
-    if (TPW > 1) load_tile(1, kf[1], ksc[1]);
-#pragma unroll
-    for (int k = 0; k < QPER; ++k) {
-        int hr, c;
-        q_unit(k, hr, c);
-        *reinterpret_cast<i32x4*>(q_s + hr * QROW + 16 * c) = qunit[k];
+    // markA, markB: `issued` right after the gathers of tiles u and u+1
+    gather(0, 0);
+    int markA = issued, markB = issued;
+    if (TPW > 1) {
+        gather(1, 1);
+        markB = issued;
     }
 
+    wait_vmcnt(issued - markQ);  // this wave's query parts have landed (operations complete in order)
+    sync_lds();                  // ... and every wave's
     typename T::frag qa[NQ][4][T::KSTEPS];
-    __syncthreads();
+    float wr[NQ][4][4];
+    int qsx[NQ][4];  // MXFP8: E8M0 scale of head 16mt + j, k-block g
 #pragma unroll
-    for (int qi = 0; qi < NQ; ++qi)
+    for (int qi = 0; qi < NQ; ++qi) {
+        const bool valid = qi < n_q;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const uint8_t* v = q_s + (qi * kIdxHeads + 16 * mt + j) * QROW;
+            const int v = qi * kIdxHeads + 16 * mt + j;
+            const uint8_t* rowp = q_s + v * T::ROW;
 #pragma unroll
-            for (int ks = 0; ks < T::KSTEPS; ++ks) qa[qi][mt][ks] = load_frag<T>(v, ks, g);
+            for (int ks = 0; ks < T::KSTEPS; ++ks) {
+                if constexpr (T::FB == 16) {
+                    qa[qi][mt][ks] = *reinterpret_cast<const bf16x8*>(rowp + ((4 * ks + g) ^ (v % UNITS)) * 16);
+                } else {  // elements [16g, +16) and [64 + 16g, +16) (the MFMA's operand order)
+                    const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + (g ^ (v % UNITS)) * 16);
+                    const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + ((4 + g) ^ (v % UNITS)) * 16);
+                    qa[qi][mt][ks] = typename T::frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+            }
+            qsx[qi][mt] = T::MX ? (int)reinterpret_cast<const uint8_t*>(&qsc_s[qi][0])[(16 * mt + j) * 4 + g] : 127;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = 16 * mt + 4 * g + i;
+                float x = w_s[qi][h];
+                if constexpr (T::SCALED) x *= qsc_s[qi][h];
+                wr[qi][mt][i] = valid ? x : 0.f;
+            }
         }
+    }
 
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
+        const int slot = u & 1;
         const int s0 = (tile0 + u) * kBlock;
-        const auto& f = kf[u & 1];
+        wait_vmcnt(issued - markA);  // tile u is in this wave's slot (operations complete in order)
+        if (s0 < Lb) {
+            // the sum of N-tile nt reaches all four lane groups; lane 16g + j
+            // keeps N-tile g's, which is position 16g + j
+            float sel[NQ];
 #pragma unroll
-        for (int qi = 0; qi < NQ; ++qi) {
-            if (qi >= n_q) continue;
-            const int64_t row = (int64_t)b * n_q + qi;
-            const int Lr = history_len(Lb, n_q, qi);
-            if (s0 >= Lr) continue;
-            if (pt[u] < 0) {  // absent block: every position scores -inf
-                if (s0 + lane < Lr) scores[row * ld + s0 + lane] = -INFINITY;
-                continue;
-            }
+            for (int qi = 0; qi < NQ; ++qi) sel[qi] = 0.f;
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                f32x4 acc[4];
+                const int prow = 16 * nt + j;
+                const uint8_t* rowp = &ktile[wave][slot][prow * T::ROW];
+                const int kx = T::MX ? (int)reinterpret_cast<const uint8_t*>(&kst[wave][slot][0])[prow * 4 + g] : 127;
+                typename T::frag kf[T::KSTEPS];
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < T::KSTEPS; ++ks)
-                        acc[mt] = mma<T>(qa[qi][mt][ks], f[nt][ks], acc[mt], qsx[qi][mt],
-                                         __float_as_int(ksc[u & 1][nt]));
+                for (int ks = 0; ks < T::KSTEPS; ++ks) {
+                    if constexpr (T::FB == 16) {
+                        kf[ks] = *reinterpret_cast<const bf16x8*>(rowp + ((4 * ks + g) ^ (prow % UNITS)) * 16);
+                    } else {
+                        const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + (g ^ (prow % UNITS)) * 16);
+                        const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + ((4 + g) ^ (prow % UNITS)) * 16);
+                        kf[ks] = typename T::frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    }
                 }
-                float v = head_weighted_relu_sum(acc, wr[qi]);
-                if constexpr (T::SCALED) v *= ksc[u & 1][nt];
-                const int s = s0 + 16 * nt + j;
-                if (g == 0 && s < Lr) scores[row * ld + s] = v;
+#pragma unroll
+                for (int qi = 0; qi < NQ; ++qi) {
+                    f32x4 acc[4];
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < T::KSTEPS; ++ks)
+                            acc[mt] = mma<T>(qa[qi][mt][ks], kf[ks], acc[mt], qsx[qi][mt], kx);
+                    }
+                    const float v = head_weighted_relu_sum(acc, wr[qi]);
+                    sel[qi] = g == nt ? v : sel[qi];
+                }
+            }
+            // one 256-byte store per row: lane l scores position s0 + l
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) {
+                if (qi >= n_q) continue;  // uniform
+                const int Lr = history_len(Lb, n_q, qi);
+                float v = sel[qi];
+                if constexpr (T::SCALED) v *= kst[wave][slot][lane];
+                if (pt[u] < 0) v = -INFINITY;  // absent block: every position scores -inf
+                if (s0 + lane < Lr) scores[((int64_t)b * n_q + qi) * ld + s0 + lane] = v;
+                issued += s0 < Lr;  // the store issues when lane 0 is active
             }
         }
-        if (u + 2 < TPW) load_tile(u + 2, kf[u & 1], ksc[u & 1]);
+        if (u + 2 < TPW) {
+            // the slot's fragment reads have returned before it is refilled
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            gather(u + 2, slot);
+        }
+        markA = markB;
+        markB = issued;
     }
 }
 
@@ -565,10 +617,11 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
         return hipGetLastError();
     }
     if (a.n_q <= 2) {
-        // 4 waves per workgroup, each streaming TPW consecutive tiles with two
-        // in flight.  One row: the longest run that still gives 256
+        // Each wave streams TPW consecutive tiles with two in flight.  One
+        // row: 4 waves per workgroup and the longest run that still gives 256
         // workgroups, up to 8 tiles of fp8 keys (8 KB each) or 4 of bf16 (16
-        // KB).  Two rows (more registers): 4 tiles.
+        // KB).  Two rows: 3 waves of 4 tiles (the second row's queries take
+        // LDS that a fourth wave's slots would need).
         const int tiles = (a.max_seq_len + kBlock - 1) / kBlock;
         int tpw = 4;
         if (a.n_q == 1) {
@@ -586,11 +639,11 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
     else if (tpw == 4) DSA_DEC(T, 1, 4, 4);       \
     else DSA_DEC(T, 1, 2, 4);
         if (a.dtype == 2) {
-            if (a.n_q == 1) { DSA_DEC1(IdxFp8) } else DSA_DEC(IdxFp8, 2, 4, 4);
+            if (a.n_q == 1) { DSA_DEC1(IdxFp8) } else DSA_DEC(IdxFp8, 2, 4, 3);
         } else if (a.dtype == 3) {
-            if (a.n_q == 1) { DSA_DEC1(IdxMx) } else DSA_DEC(IdxMx, 2, 4, 4);
+            if (a.n_q == 1) { DSA_DEC1(IdxMx) } else DSA_DEC(IdxMx, 2, 4, 3);
         } else {
-            if (a.n_q == 1) { DSA_DEC1(IdxBf16) } else DSA_DEC(IdxBf16, 2, 4, 4);
+            if (a.n_q == 1) { DSA_DEC1(IdxBf16) } else DSA_DEC(IdxBf16, 2, 4, 3);
         }
 #undef DSA_DEC1
 #undef DSA_DEC

@@ -131,6 +131,31 @@ def test_pool_strides_are_validated_before_any_launch():
     assert idx_status(scale_row_stride=8, scale_block_stride=520) == B.DSA_ERR_NULL  # valid; scores NULL
 
 
+def test_indexer_query_alignment_is_validated_before_any_launch():
+    """BF16 and E4M3 indexer queries arrive in 16-byte pieces, head weights and
+    query scales in 4-byte ones: misaligned pointers are refused with DSA_ERR_SHAPE."""
+    lib = B.lib()
+    ref = C.byref
+    for cfg in (2, 5, 6):
+        wl = make_workload(cfg, batch=2, lens=[100, 50])
+        batch, idx, _ = _fake_structs(wl)
+
+        def status(**kv):
+            i2 = B.dsa_indexer_args.from_buffer_copy(idx)
+            if cfg != 2:
+                i2.q_scale, i2.k.scales = 0x30000, 0x20000
+                i2.k.scale_kind, i2.k.group = ((B.DSA_SCALE_F32, 128) if cfg == 5 else (B.DSA_SCALE_E8M0, 32))
+            for k, v in kv.items():
+                setattr(i2, k, v)
+            return lib.dsa_indexer_scores(ref(batch), ref(i2), None, 128, None)
+
+        assert status() == B.DSA_ERR_NULL, cfg  # valid: the NULL scores are what remains
+        assert status(q=0x10008) == B.DSA_ERR_SHAPE, cfg
+        assert status(head_w=0x10002) == B.DSA_ERR_SHAPE, cfg
+        if cfg != 2:
+            assert status(q_scale=0x30002) == B.DSA_ERR_SHAPE, cfg
+
+
 def test_noalloc_forward_refuses_batches_beyond_its_scratch_before_any_launch():
     """dsa_forward_noalloc checks the batch's workspace against its fixed per-GPU
     array on the host: a 4096-row prefill needs more and is refused without any
