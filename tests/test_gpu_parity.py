@@ -342,6 +342,23 @@ def test_decode_indexer_long_wave_runs_with_ragged_lengths(cfg, batch, L):
     sc_h = sc[rows].cpu().numpy().astype(np.float64)
     ref_sc = O.indexer_scores(wl, rows, ld=sc.shape[1])
     check_scores(wl, sc_h, ref_sc, rows)
+    # absent blocks inside a run: those positions score -inf, every other score
+    # is unchanged to the bit
+    wl2 = copy.copy(wl)
+    wl2.block_table = wl.block_table.copy()
+    wl2.block_table[0, 37] = -1
+    wl2.block_table[5, 100] = wl.num_blocks + 5
+    sc2 = B.dsa_indexer_scores(B.DeviceInputs(wl2))
+    torch.cuda.synchronize()
+    L = wl.row_lens()
+    for r, blk in ((0, 37), (5, 100)):
+        a, b_ = sc[r, :L[r]].cpu(), sc2[r, :L[r]].cpu()
+        gone = torch.zeros(int(L[r]), dtype=torch.bool)
+        gone[64 * blk:64 * blk + 64] = True
+        assert torch.isneginf(b_[gone]).all(), r
+        assert torch.equal(a[~gone].view(torch.int32), b_[~gone].view(torch.int32)), r
+    others = [r for r in range(batch) if r not in (0, 5)]
+    assert torch.equal(sc[others].view(torch.int32), sc2[others].view(torch.int32))
 
 
 @pytest.mark.parametrize("cfg", [3, 5, 6])
