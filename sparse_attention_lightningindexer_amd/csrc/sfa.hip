@@ -227,24 +227,21 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                         tab_s[jb] = (int)phys_block(table, max_blocks, b, jb, num_blocks);
                 after_reads();
                 if (whole) {
-                    for (int t = slot0 + tid; t < slot1; t += kThreads) {
-                        spos[t - slot0] = t < L ? t : -1;
-                        if (half == 0) iout[t] = t < L ? t : -1;
-                    }
+                    for (int t = slot0 + tid; t < slot1; t += kThreads) spos[t - slot0] = t < L ? t : -1;
                 } else {
                     clear_hist<kThreads, true>(ssh);
                     block_select<kThreads, TK, true>(ssh, key, top_k, [&](int place, int, int slot) {
-                        if (place >= slot0 && place < slot1) {
-                            spos[place - slot0] = slot;
-                            if (half == 0) iout[place] = slot;
-                        }
+                        if (place >= slot0 && place < slot1) spos[place - slot0] = slot;
                     });
                 }
                 sync_lds();  // spos and the table row are in LDS
+                // the head-half-0 workgroups write their split's indices, one
+                // coalesced store per thread (not scattered through the emit)
 #pragma unroll
                 for (int k = 0; k < kSlotIters; ++k) {
                     const int t = slot0 + kThreads * k + tid;
                     const int v = t < slot1 ? spos[t - slot0] : -1;
+                    if (half == 0 && t < slot1) iout[t] = v;
                     sv[k] = v >= 0 && v < L ? v : -1;
                 }
             }
