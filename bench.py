@@ -11,7 +11,8 @@ launch stream), and the CPU oracle timed on the host's cores over a bounded
 sample of the same workload.  The metric is quoted on decode B32 x 8k and
 prefill 32k: with the default decode workload, the line also carries a
 "prefill" record of the same form, whose roofline is the indexer and
-attention contractions against the bf16 MFMA peak.
+attention contractions against the bf16 MFMA peak (its traffic: one indexer
+launch plus one attention launch).
 """
 from __future__ import annotations
 
@@ -342,8 +343,10 @@ def measure(cfg, args, steps, warmup, nsets, extras):
         nflops = algo["indexer"][1] + algo["attention"][1]
         dur_us = stage_us["indexer"] + stage_us["attention"]
         ach = nflops / (dur_us * 1e-6) / 1e12
+        # HBM bytes of one indexer launch plus one attention launch (counters)
+        parts = [measured_traffic(k, WORKLOAD_NAMES[cfg]) for k in ("indexer", "attention")]
         roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
+                "frac": ach / BF16_PEAK_TFLOPS, "traffic": None if None in parts else sum(parts),
                 "kernel": "indexer scoring + sparse attention (indexer_prefill_kernel, sfa_mla_kernel)",
                 "algorithmic_flops": nflops, "avg_us": dur_us,
                 "stage_frac": {k: algo[k][1] / (stage_us[k] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS
