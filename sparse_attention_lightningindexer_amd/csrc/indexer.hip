@@ -142,15 +142,34 @@ __device__ __forceinline__ void load_row_query(const uint8_t* q, const void* q_s
 // instructions); here a NaN with the sign bit clear passes through.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-__device__ __forceinline__ float head_weighted_relu_sum(const f32x4 (&acc)[4], const float (&wr)[4][4]) {
-    float v[4];  // four independent partial sums (one per M-tile), then a tree
+// This lane's share: its 16 heads, as four independent partial sums (one per
+// M-tile) and a tree.
+__device__ __forceinline__ float head_weighted_relu_part(const f32x4 (&acc)[4], const float (&wr)[4][4]) {
+    float v[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         v[mt] = wr[mt][0] * relu(acc[mt][0]);
 #pragma unroll
         for (int i = 1; i < 4; ++i) v[mt] = fmaf(wr[mt][i], relu(acc[mt][i]), v[mt]);
     }
-    return sum_over_groups((v[0] + v[1]) + (v[2] + v[3]));
+    return (v[0] + v[1]) + (v[2] + v[3]);
+}
+__device__ __forceinline__ float head_weighted_relu_sum(const f32x4 (&acc)[4], const float (&wr)[4][4]) {
+    return sum_over_groups(head_weighted_relu_part(acc, wr));
+}
+
+// The sums over the four lane groups of four N-tiles' shares at once, each
+// group keeping its own N-tile's: lane 16g + j returns N-tile g's sum for
+// position j.  Pairs of N-tiles meet in one permlane16 swap (row r keeps
+// N-tile r&1 of the pair, the sum of its row pair), then the pairs in one
+// permlane32 swap; the additions are those of sum_over_groups, in its order.
+__device__ __forceinline__ float pair_sum16(float p0, float p1) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+__device__ __forceinline__ float pair_sum32(float u01, float u23) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(u01), __float_as_uint(u23), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
 // Decode: a sequence's n_q <= NQ rows share every K tile.  Each wave owns TPW
@@ -530,18 +549,23 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
                             acc[mt] = mma<T>(qa[qi][mt][ks], kf[nt & 1][ks], acc[mt], qsx[qi][mt], ksx[nt & 1]);
                     }
                 };
-                // the sum of step k reaches all four lane groups; lane 16g + j
-                // keeps N-tile g's, which is position 16g + j
+                // step k leaves this lane's share of row k%2, N-tile k/2; after
+                // N-tiles 1 and 3 the shares of two N-tiles are reduced across
+                // the lane groups, and lane 16g + j keeps N-tile g's sum, which
+                // is position 16g + j
                 float sel0 = 0.f, sel1 = 0.f;
+                float sh[2][2], u01[2];  // shares of the pending N-tile pair; pair sums of N-tiles 0, 1
                 auto sum_step = [&](int k, const f32x4 (&acc)[4]) __attribute__((always_inline)) {
                     __builtin_amdgcn_sched_barrier(0);
                     __builtin_amdgcn_s_setprio(0);
                     __builtin_amdgcn_sched_barrier(0);
-                    const float v = head_weighted_relu_sum(acc, wr[k & 1]);
-                    if (k & 1)
-                        sel1 = g == (k >> 1) ? v : sel1;
-                    else
-                        sel0 = g == (k >> 1) ? v : sel0;
+                    const int nt = k >> 1, qi = k & 1;
+                    sh[qi][nt & 1] = head_weighted_relu_part(acc, wr[qi]);
+                    if (nt == 1) u01[qi] = pair_sum16(sh[qi][0], sh[qi][1]);
+                    if (nt == 3) {
+                        const float v = pair_sum32(u01[qi], pair_sum16(sh[qi][0], sh[qi][1]));
+                        if (qi) sel1 = v; else sel0 = v;
+                    }
                 };
                 // one 256-byte store per row: lane l scores position s0 + l
                 auto store = [&](int u) __attribute__((always_inline)) {
