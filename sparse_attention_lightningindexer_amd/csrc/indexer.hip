@@ -135,15 +135,15 @@ __device__ __forceinline__ void load_row_query(const uint8_t* q, const void* q_s
     }
 }
 
-// ReLU-weighted sum over the 64 heads of one 16-position N-tile: lane holds
-// D[head 16*mt + 4g + i][pos j]; returns the full sum for position j.
+// ReLU-weighted sum over the 64 heads of a 16-position N-tile, where lane
+// 16g + j holds D[head 16*mt + 4g + i][pos j].
 // max(x, 0) as one signed-integer max on the bits: negative floats (and -0)
 // are negative integers.  A float max would also quiet NaNs first (two
 // instructions); here a NaN with the sign bit clear passes through.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// This lane's share: its 16 heads, as four independent partial sums (one per
-// M-tile) and a tree.
+// This lane's share of the sum: its 16 heads, as four independent partial
+// sums (one per M-tile) and a tree.
 __device__ __forceinline__ float head_weighted_relu_part(const f32x4 (&acc)[4], const float (&wr)[4][4]) {
     float v[4];
 #pragma unroll
@@ -153,9 +153,6 @@ __device__ __forceinline__ float head_weighted_relu_part(const f32x4 (&acc)[4], 
         for (int i = 1; i < 4; ++i) v[mt] = fmaf(wr[mt][i], relu(acc[mt][i]), v[mt]);
     }
     return (v[0] + v[1]) + (v[2] + v[3]);
-}
-__device__ __forceinline__ float head_weighted_relu_sum(const f32x4 (&acc)[4], const float (&wr)[4][4]) {
-    return sum_over_groups(head_weighted_relu_part(acc, wr));
 }
 
 // The sums over the four lane groups of four N-tiles' shares at once, each
@@ -317,11 +314,11 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
         const int s0 = (tile0 + u) * kBlock;
         wait_vmcnt(issued - markA);  // tile u is in this wave's slot (operations complete in order)
         if (s0 < Lb) {
-            // the sum of N-tile nt reaches all four lane groups; lane 16g + j
-            // keeps N-tile g's, which is position 16g + j
-            float sel[NQ];
-#pragma unroll
-            for (int qi = 0; qi < NQ; ++qi) sel[qi] = 0.f;
+            // each N-tile leaves this lane's share per row; after N-tiles 1
+            // and 3 the shares of two N-tiles are reduced across the lane
+            // groups, and lane 16g + j keeps N-tile g's sum, which is
+            // position 16g + j
+            float sel[NQ], shr[NQ][2], u01[NQ];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const int prow = 16 * nt + j;
@@ -348,8 +345,9 @@ __global__ __launch_bounds__(64 * NW) void indexer_decode_kernel(
                         for (int ks = 0; ks < T::KSTEPS; ++ks)
                             acc[mt] = mma<T>(qa[qi][mt][ks], kf[ks], acc[mt], qsx[qi][mt], kx);
                     }
-                    const float v = head_weighted_relu_sum(acc, wr[qi]);
-                    sel[qi] = g == nt ? v : sel[qi];
+                    shr[qi][nt & 1] = head_weighted_relu_part(acc, wr[qi]);
+                    if (nt == 1) u01[qi] = pair_sum16(shr[qi][0], shr[qi][1]);
+                    if (nt == 3) sel[qi] = pair_sum32(u01[qi], pair_sum16(shr[qi][0], shr[qi][1]));
                 }
             }
             // one 256-byte store per row: lane l scores position s0 + l
