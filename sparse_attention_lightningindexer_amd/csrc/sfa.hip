@@ -411,8 +411,9 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
 #pragma unroll
             for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
         });
-        // per head hl0 + j (identical in the four lane groups): the reference,
-        // the largest scaled logit seen, and the denominator
+        // per head hl0 + j: the reference (identical in the four lane groups),
+        // and this lane's largest scaled logit seen and share of the
+        // denominator (both reduced over the lane groups only at the end)
         float m_ref = -INFINITY, m_obs = -INFINITY, l_run = 0.f;
         bool exact = false;  // the reference is the exact maximum (second pass)
 
@@ -465,10 +466,10 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                     sm[pt][i] = 16 * pt + i < lim ? s.v[pt][i] : -INFINITY;
                     cmax = fmaxf(cmax, sm[pt][i]);
                 }
-            cmax = max_over_groups(cmax) * scale_log2;  // scale_log2 > 0
-            if (!exact && c == 0) m_ref = cmax;
+            cmax *= scale_log2;  // scale_log2 > 0; this lane's positions only
+            if (!exact && c == 0) m_ref = max_over_groups(cmax);
             m_obs = fmaxf(m_obs, cmax);
-            const bool over = cmax > m_ref + kSlack;     // also a reference of -inf
+            const bool over = cmax > m_ref + kSlack;     // also a reference of -inf; any lane counts
             const float mneg = m_ref == -INFINITY ? 0.f : -m_ref;
             float psum = 0.f;
             const int hl = hl0 + j;
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
                 *reinterpret_cast<uint2*>(pbuf[c & 1] + hl * kPRow + 2 * (16 * pt + 4 * g)) =
                     make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
             }
-            l_run += sum_over_groups(psum);
+            l_run += psum;
             if (ballot(over) != 0ull && lane == 0) overflow = 1;
         };
 
@@ -506,9 +507,10 @@ __global__ __launch_bounds__(kThreads, 1) void sfa_mla_kernel(
             __syncthreads();           // every wave has read the flag
             if (tid == 0) overflow = 0;
             exact = true;
-            m_ref = m_obs;
+            m_ref = max_over_groups(m_obs);
             l_run = 0.f;
         }
+        l_run = sum_over_groups(l_run);
         if (g == 0) {
             l_s[hl0 + j] = l_run;
             m_s[hl0 + j] = m_ref;
